@@ -1,0 +1,212 @@
+/*
+ * sparse_mla.h - C ABI of the MI355X (gfx950) top-k sparse MLA decode library.
+ *
+ * What the library computes
+ * -------------------------
+ * Decode attention for DeepSeek-V4-style multi-head latent attention in which every
+ * query row attends only to its own list of top-k cache positions.  One latent KV
+ * "head" (576 wide = 512 latent + 64 rope) is shared by all query heads; the value
+ * vector is the 512-wide latent part.  The serving engines on the source pages call
+ * such a kernel from the sparse-MLA attention backend's forward_mqa, after
+ * translating request-local top-k positions to global cache slots through the block
+ * table, and allocate the output as [tokens, heads, kv_lora_rank=512] in the dtype
+ * of q (prhub vllm#43477 "DSv4 and GLM-5.1 on Blackwell SM120", key code excerpts:
+ * FlashInferMLASparseSM120Impl.forward_mqa).  Gathering and dequantizing the paged
+ * entries, a tiled online softmax, the merge of split partial results and the
+ * attention sink are the pieces of the Triton decode path described on prhub
+ * sglang#24692 "SM120 support for DeepSeek-V4", implementation breakdown items 2-3.
+ *
+ * For query row r (request b = row_req[r]) and head h, with J the multiset of list
+ * positions j whose index idx[r][j] != -1:
+ *     s_j    = softmax_scale * sum_{d<576} q[r][h][d] * k_j[d]
+ *     sigma  = sinks[h]   (or -inf when sinks == NULL)
+ *     m      = max(max_j s_j, sigma)
+ *     Z      = exp(sigma - m) + sum_j exp(s_j - m)
+ *     out[r][h][:] = sum_j exp(s_j - m) * k_j[0:512] / Z        (bf16, round to nearest even)
+ *     lse[r][h]    = m + ln Z                                    (fp32, natural log)
+ * A row with no valid entry gives out = 0 and lse = sigma (-inf without a sink).
+ * The sink adds exp(sigma) to the denominator and carries no value; it is applied once.
+ *
+ * Split-KV: with S splits, list positions [c*C, (c+1)*C), C = ceil(K/S), form chunk c.
+ * A chunk's partial result is sink-free:
+ *     o_c   = sum_{j in c} exp(s_j - m_c) k_j[0:512] / sum_{j in c} exp(s_j - m_c)
+ *     lse_c = ln sum_{j in c} exp(s_j)          (o_c = 0, lse_c = -inf for an empty chunk)
+ * and the merge is
+ *     M = max(max_c lse_c, sigma), w_c = exp(lse_c - M), w_s = exp(sigma - M),
+ *     out = sum_c w_c o_c / (sum_c w_c + w_s),  lse = M + ln(sum_c w_c + w_s).
+ *
+ * Cache byte layout (the library's own; the source pages describe one paged buffer
+ * read through fp8 / uint8 / bf16 views with in-page addressing, prhub sglang#24692,
+ * implementation breakdown items 2-3, and a bf16 cache of shape
+ * (num_blocks, block_size, 576), prhub vllm#43477, key code excerpts: get_kv_cache_shape):
+ *   SMLA_KV_BF16       page = bf16[page_size][576]; bytes per page 1152*page_size.
+ *                      Dims 0..511 are the latent (= V), 512..575 the rope part.
+ *   SMLA_KV_FP8_UE8M0  page = 648*page_size bytes, three regions:
+ *                        latent  e4m3fn[page_size][512]  at byte 0
+ *                        rope    bf16  [page_size][64]   at byte 512*page_size
+ *                        scales  uint8 [page_size][8]    at byte 640*page_size
+ *                      k[d] = e4m3fn(latent[d]) * 2^(scale[d/64] - 127) for d < 512,
+ *                      k[512+i] = rope[i].  e4m3fn is OCP FP8 E4M3 (bias 7, max 448,
+ *                      S.1111.111 = NaN); a scale byte is UE8M0 (power of two, 255 = NaN).
+ *                      The dequantized value is exact in bf16 for scale bytes 10..246;
+ *                      outside that range the kernel's bf16 rounding applies.
+ * A cache slot s lives in page s / page_size at in-page row s % page_size.
+ *
+ * Conventions
+ *   - All device pointers are caller-owned device memory; the library never allocates,
+ *     frees or synchronises, and launches only on the stream passed in (a hipStream_t
+ *     passed as void*; NULL = the null stream).
+ *   - Shapes are row-major and contiguous unless a stride is named.
+ *   - Every entry point checks its arguments on the host first and returns a status
+ *     without launching anything when they are invalid.  A failed launch returns
+ *     SMLA_ERR_HIP.
+ *   - Index values outside the valid range (< -1, beyond the request's page table,
+ *     or page ids outside [0, num_pages)) are never dereferenced: the kernel treats
+ *     them as -1.  With SMLA_F_CHECK_INDICES the first such (row, position) is also
+ *     recorded in the workspace and can be read with sparse_mla_read_index_error.
+ *   - The plan is plain host memory, independent of any data, and may be reused across
+ *     calls and graph replays.  The library keeps no mutable global state beyond a
+ *     per-device attribute cache filled once.
+ */
+#ifndef SPARSE_MLA_H_
+#define SPARSE_MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SMLA_QK_DIM 576
+#define SMLA_V_DIM 512
+#define SMLA_ROPE_DIM 64
+#define SMLA_SCALE_GROUP 64
+#define SMLA_NUM_SCALE_GROUPS 8
+#define SMLA_FP8_ENTRY_BYTES 648
+#define SMLA_BF16_ENTRY_BYTES 1152
+#define SMLA_MAX_HEADS 128
+#define SMLA_MAX_SPLITS 256
+
+typedef enum {
+  SMLA_OK = 0,
+  SMLA_ERR_NULL_ARG = 1,             /* a required pointer is NULL */
+  SMLA_ERR_BAD_SHAPE = 2,            /* a size is negative, zero where it must not be, or inconsistent */
+  SMLA_ERR_UNSUPPORTED = 3,          /* valid but unsupported: head count, format, mode, flag */
+  SMLA_ERR_MISALIGNED = 4,           /* a pointer or a row stride breaks the alignment rule */
+  SMLA_ERR_WORKSPACE_TOO_SMALL = 5,  /* workspace_bytes below what the plan asks for */
+  SMLA_ERR_HIP = 6,                  /* the HIP runtime reported an error (no device, launch failure) */
+  SMLA_ERR_BAD_PLAN = 7              /* the plan was not produced by sparse_mla_decode_plan */
+} smla_status;
+
+typedef enum { SMLA_KV_BF16 = 0, SMLA_KV_FP8_UE8M0 = 1 } smla_kv_format;
+
+/* LOGICAL: idx is a request-local position t; slot = page_table[row_req[r]][t / page_size]
+ * * page_size + t % page_size (the block-table translation that the vLLM SM120 backend
+ * performs before its kernel, prhub vllm#43477, key code excerpts: forward_mqa).
+ * GLOBAL: idx already is the cache slot. */
+typedef enum { SMLA_IDX_LOGICAL = 0, SMLA_IDX_GLOBAL = 1 } smla_index_mode;
+
+enum {
+  /* Write the per-chunk sink-free partials (partial_o, partial_lse) instead of the merged
+   * output; out/lse are not written.  For callers that merge elsewhere. */
+  SMLA_F_PARTIALS_ONLY = 1,
+  /* Record the first out-of-range index in the workspace (see sparse_mla_read_index_error). */
+  SMLA_F_CHECK_INDICES = 2
+};
+
+typedef struct {
+  int32_t num_rows;          /* R query rows (decode tokens); >= 0 */
+  int32_t num_requests;      /* B requests; rows map to requests through row_req; >= 1 in LOGICAL mode */
+  int32_t num_heads;         /* H query heads: a multiple of 16 in [16, 128] */
+  int32_t topk;              /* K = index row stride in int32 elements; >= 4 and a multiple of 4
+                                (16-byte aligned rows, as the page prhub vllm#43827 notes for
+                                the FlashInfer sparse kernels, review highlights item 2) */
+  int32_t page_size;         /* tokens per page; a power of two in [1, 1024] */
+  int32_t num_pages;         /* pages in kv_cache; >= 1 */
+  int32_t max_pages_per_req; /* page_table row stride; >= 1 in LOGICAL mode */
+  int32_t kv_format;         /* smla_kv_format */
+  int32_t index_mode;        /* smla_index_mode */
+  int32_t num_splits;        /* 0: the planner chooses; > 0: forced S (chunks of ceil(K/S) positions) */
+  int32_t flags;             /* SMLA_F_* */
+  float softmax_scale;       /* multiplies q.k; the sink lives in the same (scaled) logit domain */
+} smla_problem;
+
+/* Host-side plan.  Copyable plain bytes; contents are private to the library. */
+typedef struct {
+  uint8_t opaque[256];
+} smla_plan;
+
+/* Choose the split count and launch shape for a problem and report the workspace size.
+ *   p               problem description (host memory, read only)
+ *   num_cus         compute units to plan for; <= 0 queries the current HIP device
+ *                   (the only HIP call this function makes)
+ *   plan            output (host memory)
+ *   workspace_bytes output: device bytes that sparse_mla_decode_run needs (0 when none)
+ * Depends only on shapes and num_cus, never on data; no device memory is touched.
+ * Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED, HIP (device query failed). */
+smla_status sparse_mla_decode_plan(const smla_problem* p, int32_t num_cus, smla_plan* plan,
+                                   size_t* workspace_bytes);
+
+/* Number of splits S chosen by a plan (>= 1), or -1 for an invalid plan. */
+int32_t sparse_mla_plan_num_splits(const smla_plan* plan);
+
+/* Run the decode on `stream`.  All pointers are device pointers.
+ *   q           bf16 [R][H][576]; 16-byte aligned
+ *   kv_cache    num_pages pages in the layout above; 16-byte aligned
+ *   indices     int32 [R][K]; -1 = empty; 16-byte aligned (K is a multiple of 4)
+ *   row_req     int32 [R] request of each row (LOGICAL mode; may be NULL in GLOBAL mode)
+ *   page_table  int32 [B][max_pages_per_req] page ids (LOGICAL mode; may be NULL in GLOBAL mode)
+ *   sinks       fp32 [H] per-head sink logits, or NULL for no sink (-inf sinks are allowed)
+ *   out         bf16 [R][H][512]                  (not written with SMLA_F_PARTIALS_ONLY)
+ *   lse         fp32 [R][H] or NULL               (not written with SMLA_F_PARTIALS_ONLY)
+ *   partial_o   fp32 [R][S][H][512]  only with SMLA_F_PARTIALS_ONLY, else NULL
+ *   partial_lse fp32 [R][S][H]       only with SMLA_F_PARTIALS_ONLY, else NULL
+ *   workspace   device scratch of at least the planned size (may be NULL when it is 0);
+ *               256-byte aligned; its contents need not be initialised
+ * R == 0 returns SMLA_OK without launching.  No device-to-host traffic and no
+ * allocation: the call can be captured in a HIP graph.
+ * Errors: BAD_PLAN, NULL_ARG, MISALIGNED, WORKSPACE_TOO_SMALL, HIP. */
+smla_status sparse_mla_decode_run(const smla_plan* plan, const void* q, const void* kv_cache,
+                                  const int32_t* indices, const int32_t* row_req,
+                                  const int32_t* page_table, const float* sinks, void* out,
+                                  float* lse, float* partial_o, float* partial_lse,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* LSE-merge S sink-free partials and apply the sink once (the merge and sink steps that
+ * follow the split decode on prhub sglang#24692, key files: flash_mla_sm120_triton.py).
+ *   partial_o   fp32 [R][S][H][512], partial_lse fp32 [R][S][H] (natural log, -inf = empty)
+ *   sinks       fp32 [H] or NULL;  out bf16 [R][H][512];  lse fp32 [R][H] or NULL
+ * num_rows == 0 returns SMLA_OK without launching.  H need not be a multiple of 16 here
+ * (1..1024); S in [1, SMLA_MAX_SPLITS].
+ * Errors: NULL_ARG, BAD_SHAPE, MISALIGNED, HIP. */
+smla_status sparse_mla_merge_partials(const float* partial_o, const float* partial_lse,
+                                      int32_t num_rows, int32_t num_splits, int32_t num_heads,
+                                      const float* sinks, void* out, float* lse, void* stream);
+
+/* Test helper: decode n cache slots (global slot numbers, device int32 [n]) into bf16
+ * rows out[n][576] with the same device code the decode kernel uses for its gather and
+ * dequantisation.  Slots outside [0, num_pages*page_size) give a zero row.
+ * Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED, MISALIGNED, HIP. */
+smla_status sparse_mla_gather_debug(const void* kv_cache, int32_t kv_format, int32_t page_size,
+                                    int32_t num_pages, const int32_t* slots, int32_t n, void* out,
+                                    void* stream);
+
+/* With SMLA_F_CHECK_INDICES: copy the two int32 words (row, position) of the first
+ * out-of-range index recorded in `workspace` by the last run into host memory
+ * `row_pos` (-1, -1 when none).  Synchronises `stream`; for tests and debugging only.
+ * Errors: BAD_PLAN, NULL_ARG, HIP. */
+smla_status sparse_mla_read_index_error(const smla_plan* plan, const void* workspace,
+                                        int32_t* row_pos, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* sparse_mla_status_string(smla_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t sparse_mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_MLA_H_ */

@@ -1,0 +1,28 @@
+"""Float64 CPU oracle for the sparse MLA decode path.
+
+TEST INFRASTRUCTURE: only tests/, the smoke check in __graft_entry__ and the
+cpu_baseline leg of bench.py may import it.  The library never does; it shares no
+code, constants or helpers with the HIP implementation.
+"""
+
+from .sparse_mla_oracle import (  # noqa: F401
+    BF16_ENTRY_BYTES,
+    FP8_ENTRY_BYTES,
+    IDX_GLOBAL,
+    IDX_LOGICAL,
+    KV_BF16,
+    KV_FP8_UE8M0,
+    QK_DIM,
+    V_DIM,
+    attend,
+    bf16_bits_to_f64,
+    chunk_bounds,
+    decode_entries,
+    e4m3fn_to_f64,
+    merge_partials,
+    page_bytes,
+    sparse_mla_decode,
+    sparse_mla_decode_partials,
+    translate,
+    ue8m0_to_f64,
+)

@@ -1,0 +1,262 @@
+"""Seeded synthetic inputs for sparse MLA decode.
+
+This module only draws random numbers and lays bytes out in the paged cache format; it
+holds none of the decode arithmetic (no dequantisation, no dot products, no softmax).
+Both the HIP path and the float64 oracle consume what it produces.
+
+Five workloads, following the shapes used for the DeepSeek-V4 sparse decode on the
+source pages (576-wide latent KV shared by all heads, top-k lists of 2048, page size 64,
+MTP rows with their own index lists):
+  tiny_bf16     1 request x 1 row, 16 heads, BF16 cache of 4 pages (identity table),
+                64 distinct indices out of 256 tokens with the last 8 set to -1, no sink.
+  b32_h64_fp8   32 requests x 1 row, 64 heads, context ~ U[4096, 32768], FP8+UE8M0,
+                2048 distinct indices per row, sinks ~ N(0,1).
+  b128_mtp4_h128_fp8
+                128 requests x 4 rows (independent lists), 128 heads,
+                context ~ U[8192, 131072], FP8+UE8M0, sinks ~ N(0,1).
+  b2_h128_bf16_split16
+                2 requests x 1 row, 128 heads, context 131072, BF16, 16 forced splits.
+  ragged_b256_h64_fp8
+                256 requests with next_n in {1,2,4}, 64 heads, context 4096 each over a
+                shuffled pool of 16384 pages, valid count ~ U[1, 2048] padded with -1,
+                about 10% of requests share their first 32 pages with another request,
+                sinks -inf on heads 0..31 and ~ N(0,1) on 32..63.
+
+Draw order (numpy.random.default_rng(seed)): context lengths, rows per request, page
+permutation, shared-page copies, then per row (valid count, indices), then q, then
+sinks.  The cache is drawn by torch.Generator(device).manual_seed(seed) in chunks of
+pages, so it can be produced directly on the GPU for the large workloads.
+
+FP8 encoding of the latent (the cache producer, not the decode path): per token and
+per group of 64 dims, k = the smallest integer with amax <= 448 * 2^k (k = 0 for an
+all-zero group); scale byte = k + 127; code = round-to-nearest-even e4m3fn of x / 2^k
+(torch's float8_e4m3fn cast; |x / 2^k| <= 448 so nothing saturates).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+KV_BF16 = "bf16"
+KV_FP8 = "fp8"
+
+LATENT = 512
+ROPE = 64
+WIDTH = 576
+GROUPS = 8
+
+
+@dataclass(frozen=True)
+class WorkloadSpec:
+    name: str
+    num_requests: int
+    rows_per_request: tuple          # choices drawn uniformly per request
+    num_heads: int
+    topk: int
+    ctx_lo: int
+    ctx_hi: int
+    kv_format: str
+    page_size: int = 64
+    valid: str = "all"               # "all" | "tail8_masked" | "uniform"
+    sinks: str = "normal"            # "none" | "normal" | "half_neg_inf"
+    shared_frac: float = 0.0         # fraction of requests whose first pages are shared
+    shared_pages: int = 32
+    permute_pages: bool = True
+    num_splits: int = 0              # 0 = planner decides
+    softmax_scale: float = 1.0 / math.sqrt(576.0)
+
+    def scaled(self, **kw) -> "WorkloadSpec":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS = {
+    "tiny_bf16": WorkloadSpec("tiny_bf16", 1, (1,), 16, 64, 256, 256, KV_BF16,
+                              valid="tail8_masked", sinks="none", permute_pages=False),
+    "b32_h64_fp8": WorkloadSpec("b32_h64_fp8", 32, (1,), 64, 2048, 4096, 32768, KV_FP8),
+    "b128_mtp4_h128_fp8": WorkloadSpec("b128_mtp4_h128_fp8", 128, (4,), 128, 2048, 8192,
+                                       131072, KV_FP8),
+    "b2_h128_bf16_split16": WorkloadSpec("b2_h128_bf16_split16", 2, (1,), 128, 2048, 131072,
+                                         131072, KV_BF16, num_splits=16),
+    "ragged_b256_h64_fp8": WorkloadSpec("ragged_b256_h64_fp8", 256, (1, 2, 4), 64, 2048, 4096,
+                                        4096, KV_FP8, valid="uniform", sinks="half_neg_inf",
+                                        shared_frac=0.1),
+}
+# Order of the workloads as they are numbered in the documentation (1..5).
+WORKLOAD_ORDER = ["tiny_bf16", "b32_h64_fp8", "b128_mtp4_h128_fp8", "b2_h128_bf16_split16",
+                  "ragged_b256_h64_fp8"]
+
+
+@dataclass
+class Inputs:
+    spec: WorkloadSpec
+    q: torch.Tensor                  # bf16 [R, H, 576]
+    kv_cache: torch.Tensor           # uint8 [num_pages, page_bytes]
+    indices: torch.Tensor            # int32 [R, K]
+    row_req: torch.Tensor            # int32 [R]
+    page_table: torch.Tensor         # int32 [B, max_pages]
+    sinks: Optional[torch.Tensor]    # fp32 [H] or None
+    context_lens: torch.Tensor       # int32 [B]
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def num_rows(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def num_heads(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.kv_cache.shape[0])
+
+    def num_valid(self) -> int:
+        return int((self.indices != -1).sum().item())
+
+    def to(self, device) -> "Inputs":
+        mv = lambda t: None if t is None else t.to(device)  # noqa: E731
+        return Inputs(self.spec, mv(self.q), mv(self.kv_cache), mv(self.indices),
+                      mv(self.row_req), mv(self.page_table), mv(self.sinks),
+                      mv(self.context_lens), dict(self.meta))
+
+
+def page_bytes(kv_format: str, page_size: int) -> int:
+    return (648 if kv_format == KV_FP8 else 1152) * page_size
+
+
+def encode_fp8_groups(x: torch.Tensor):
+    """Encode float32 latents [n, 512] as e4m3fn codes [n, 512] and UE8M0 bytes [n, 8]."""
+    n = x.shape[0]
+    g = x.reshape(n, GROUPS, LATENT // GROUPS)
+    amax = g.abs().amax(dim=-1)
+    lim = torch.full_like(amax, 448.0)
+    pos = amax > 0
+    k = torch.where(pos, torch.ceil(torch.log2(torch.where(pos, amax, lim) / 448.0)),
+                    torch.zeros_like(amax))
+    # log2 and the division round; settle k exactly with power-of-two products.
+    k = torch.where(pos & (amax > torch.ldexp(lim, k)), k + 1, k)
+    k = torch.where(pos & (amax <= torch.ldexp(lim, k - 1)), k - 1, k)
+    y = g * torch.ldexp(torch.ones_like(amax), -k)[..., None]
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8).reshape(n, LATENT)
+    sbytes = (k + 127).clamp(0, 254).to(torch.uint8)
+    return codes, sbytes
+
+
+def pack_fp8_pages(codes: torch.Tensor, rope_bf16: torch.Tensor, scale_bytes: torch.Tensor,
+                   page_size: int) -> torch.Tensor:
+    """Region-split FP8 pages: latent [ps][512] | rope bf16 [ps][64] | scales [ps][8]."""
+    n = codes.shape[0]
+    assert n % page_size == 0
+    npg = n // page_size
+    out = torch.empty((npg, 648 * page_size), dtype=torch.uint8, device=codes.device)
+    out[:, : 512 * page_size] = codes.reshape(npg, 512 * page_size)
+    out[:, 512 * page_size: 640 * page_size] = (
+        rope_bf16.contiguous().view(torch.uint8).reshape(npg, 128 * page_size))
+    out[:, 640 * page_size:] = scale_bytes.reshape(npg, 8 * page_size)
+    return out
+
+
+def make_cache(num_pages: int, page_size: int, kv_format: str, seed: int,
+               device="cpu", chunk_pages: int = 2048) -> torch.Tensor:
+    """Random paged cache: N(0,1) values, FP8+UE8M0 latent with bf16 rope, or plain bf16."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    pb = page_bytes(kv_format, page_size)
+    cache = torch.empty((num_pages, pb), dtype=torch.uint8, device=device)
+    for p0 in range(0, num_pages, chunk_pages):
+        p1 = min(num_pages, p0 + chunk_pages)
+        ntok = (p1 - p0) * page_size
+        if kv_format == KV_BF16:
+            vals = torch.randn((ntok, WIDTH), generator=gen, device=device, dtype=torch.float32)
+            cache[p0:p1] = vals.to(torch.bfloat16).view(torch.uint8).reshape(p1 - p0, pb)
+        else:
+            lat = torch.randn((ntok, LATENT), generator=gen, device=device, dtype=torch.float32)
+            rope = torch.randn((ntok, ROPE), generator=gen, device=device, dtype=torch.float32)
+            codes, sb = encode_fp8_groups(lat)
+            cache[p0:p1] = pack_fp8_pages(codes, rope.to(torch.bfloat16), sb, page_size)
+    return cache
+
+
+def _bf16_from_normal(rng: np.random.Generator, shape) -> torch.Tensor:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    return torch.from_numpy(x).to(torch.bfloat16)
+
+
+def make_inputs(spec: WorkloadSpec, seed: int, device="cpu", cache_device=None) -> Inputs:
+    """Draw one workload.  Small tensors are drawn on the host with numpy and moved to
+    `device`; the cache is drawn on `cache_device` (default: `device`)."""
+    cache_device = device if cache_device is None else cache_device
+    rng = np.random.default_rng(seed)
+    B, ps, K = spec.num_requests, spec.page_size, spec.topk
+    ctx = rng.integers(spec.ctx_lo, spec.ctx_hi + 1, size=B)
+    nrows = rng.choice(np.asarray(spec.rows_per_request), size=B)
+    pages_per_req = -(-ctx // ps)
+    num_pages = int(pages_per_req.sum())
+    max_pages = int(pages_per_req.max())
+    perm = rng.permutation(num_pages) if spec.permute_pages else np.arange(num_pages)
+    page_table = np.full((B, max_pages), -1, dtype=np.int32)
+    start = 0
+    for b in range(B):
+        page_table[b, : pages_per_req[b]] = perm[start: start + pages_per_req[b]]
+        start += pages_per_req[b]
+    shared = []
+    n_shared = int(round(spec.shared_frac * B))
+    if n_shared > 0:
+        takers = rng.choice(B, size=n_shared, replace=False)
+        for b in takers:
+            donor = int(rng.integers(0, B - 1))
+            donor = donor + 1 if donor >= b else donor
+            npg = min(spec.shared_pages, pages_per_req[b], pages_per_req[donor])
+            page_table[b, :npg] = page_table[donor, :npg]
+            shared.append((int(b), donor, int(npg)))
+    R = int(nrows.sum())
+    row_req = np.repeat(np.arange(B, dtype=np.int32), nrows)
+    indices = np.full((R, K), -1, dtype=np.int32)
+    for r in range(R):
+        c = int(ctx[row_req[r]])
+        if spec.valid == "uniform":
+            count = int(rng.integers(1, K + 1))
+        else:
+            count = K
+        count = min(count, c)
+        indices[r, :count] = rng.choice(c, size=count, replace=False)
+        if spec.valid == "tail8_masked":
+            indices[r, K - 8:] = -1
+    q = _bf16_from_normal(rng, (R, spec.num_heads, WIDTH))
+    if spec.sinks == "none":
+        sinks = None
+    else:
+        sinks = rng.standard_normal(size=spec.num_heads).astype(np.float32)
+        if spec.sinks == "half_neg_inf":
+            sinks[: spec.num_heads // 2] = -np.inf
+        sinks = torch.from_numpy(sinks)
+    cache = make_cache(num_pages, ps, spec.kv_format, seed, device=cache_device)
+    inp = Inputs(spec, q, cache, torch.from_numpy(indices), torch.from_numpy(row_req),
+                 torch.from_numpy(page_table), sinks, torch.from_numpy(ctx.astype(np.int32)),
+                 {"seed": seed, "shared": shared})
+    small = inp.to(device)
+    small.kv_cache = cache
+    return small
+
+
+def compulsory_bytes(inp: Inputs) -> int:
+    """Bytes the method must move once: q, gathered entries, indices, page-table rows
+    of the requests, out (bf16) and lse (fp32), sinks."""
+    R, H, K = inp.num_rows, inp.num_heads, inp.spec.topk
+    entry = 648 if inp.spec.kv_format == KV_FP8 else 1152
+    n = inp.num_valid()
+    ctx = inp.context_lens.cpu().numpy().astype(np.int64)
+    pt = int((-(-ctx // inp.spec.page_size)).sum()) * 4
+    sinks = 0 if inp.sinks is None else 4 * H
+    return R * H * 1152 + n * entry + R * K * 4 + pt + R * H * (1024 + 4) + sinks
+
+
+def algorithmic_flops(inp: Inputs) -> int:
+    """2*H*(576+512) per attended entry: the QK and PV contractions."""
+    return 2 * inp.num_heads * (WIDTH + LATENT) * inp.num_valid()
