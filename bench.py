@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Throughput of top-k sparse MLA decode on one MI355X.
+
+A step is one sparse_mla_decode_run call over the whole workload (index translation,
+gather + dequant, QK, online softmax with sinks, PV, and the split merge when the plan
+splits).  Inputs are seeded synthetic data resident in HBM before timing starts.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Prints one JSON line.  The default workload is b128_mtp4_h128_fp8: 128 requests x 4
+MTP rows, 128 heads, top-k 2048 over contexts of 8K..128K tokens, FP8+UE8M0 cache.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PMC_FILE = os.path.join(ROOT, "profiles", "decode_b128_mtp4_h128_fp8_pmc.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "sparse_mla_decode_03_amd", "csrc", f)
+                  for f in ("smla_decode.hip", "smla_device.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic(launch_units: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source; else None."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    kv = {}
+    with open(PMC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        fetch = float(kv["fetch_kib_per_dispatch"]) * 1024 / float(kv["fetch_copy_factor"])
+        write = float(kv["write_kib_per_dispatch"]) * 1024 / float(kv["write_copy_factor"])
+    except (KeyError, ValueError):
+        return None
+    return fetch + write
+
+
+def cpu_baseline(inp, budget_s: float):
+    """Time the float64 oracle on whole rows of the same workload until about budget_s
+    of CPU work has been done."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import sparse_mla_oracle as orc
+
+    R = inp.num_rows
+    rows_done, entries, elapsed = 0, 0, 0.0
+    kvf = orc.KV_FP8_UE8M0 if inp.spec.kv_format == "fp8" else orc.KV_BF16
+    qb = inp.q.cpu().view(torch.int16).numpy().view(np.uint16)
+    idx = inp.indices.cpu()
+    rr = inp.row_req.cpu()
+    pt = inp.page_table.cpu()
+    step = 4
+    while rows_done < R and elapsed < budget_s:
+        rows = list(range(rows_done, min(R, rows_done + step)))
+        reqs = torch.unique(rr[rows])
+        used = pt[reqs]
+        used = torch.unique(used[used >= 0])
+        remap = torch.full((inp.num_pages,), -1, dtype=torch.int32)
+        remap[used.long()] = torch.arange(used.numel(), dtype=torch.int32)
+        sub = inp.kv_cache.index_select(0, used.to(inp.kv_cache.device).long()).cpu().numpy()
+        npt = torch.where(pt >= 0, remap[pt.clamp(min=0).long()], torch.full_like(pt, -1)).numpy()
+        sinks = None if inp.sinks is None else inp.sinks.cpu().numpy()
+        t0 = time.perf_counter()
+        orc.sparse_mla_decode(qb, sub, kvf, inp.spec.page_size, idx.numpy(), rr.numpy(), npt,
+                              sinks, inp.spec.softmax_scale, rows=rows)
+        elapsed += time.perf_counter() - t0
+        entries += int((idx[rows] != -1).sum())
+        rows_done += len(rows)
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    return {"value": entries / elapsed, "unit": "entries/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {rows_done} of {R} rows ({entries} attended entries), "
+                      f"float64 numpy oracle, {elapsed:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="b128_mtp4_h128_fp8")
+    ap.add_argument("--seed", type=int, default=3)
+    ap.add_argument("--num-splits", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run only a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by rows with no exchange; see the design notes)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from sparse_mla_decode_03_amd import binding as B
+    from sparse_mla_decode_03_amd import workloads as W
+
+    dev = torch.device("cuda")
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).random_(0, 255)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "dispatches": 5}))
+        return 0
+
+    spec = W.WORKLOADS[args.workload]
+    if args.num_splits is not None:
+        spec = spec.scaled(num_splits=args.num_splits)
+    t_gen = time.perf_counter()
+    inp = W.make_inputs(spec, args.seed, device=dev, cache_device=dev)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    R, H, K = inp.num_rows, inp.num_heads, spec.topk
+    kvf = B.KV_FP8_UE8M0 if spec.kv_format == "fp8" else B.KV_BF16
+    prob = B.make_problem(R, spec.num_requests, H, K, spec.page_size, inp.num_pages,
+                          inp.page_table.shape[1], kvf, B.IDX_LOGICAL, spec.num_splits, 0,
+                          spec.softmax_scale)
+    info = B.plan(prob)
+    out = torch.empty((R, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((R, H), dtype=torch.float32, device=dev)
+    ws = (torch.empty(info.workspace_bytes, dtype=torch.uint8, device=dev)
+          if info.workspace_bytes else None)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.run(info, inp.q, inp.kv_cache, inp.indices, inp.row_req, inp.page_table, inp.sinks,
+              out, lse, None, None, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    mean_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+
+    n_valid = inp.num_valid()
+    flops = W.algorithmic_flops(inp)
+    cbytes = W.compulsory_bytes(inp)
+    K_steps = args.steps
+    value = n_valid * K_steps / wall
+    mfma_tflops = flops / mean_launch_s / 1e12
+    hbm_gbs = cbytes / mean_launch_s / 1e9
+    traffic = pmc_traffic(1)
+    res = {
+        "metric": "sparse-MLA decode attended KV entries/s",
+        "value": value,
+        "unit": "entries/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / K_steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": spec.name, "requests": spec.num_requests, "rows": R, "heads": H,
+            "topk": K, "kv_format": "fp8_e4m3+ue8m0" if spec.kv_format == "fp8" else "bf16",
+            "page_size": spec.page_size, "pages": inp.num_pages, "num_splits": info.num_splits,
+            "attended_entries_per_step": n_valid,
+            "tokens_per_s": R * K_steps / wall,
+            "compulsory_bytes_per_step": cbytes,
+            "hbm_tb_s": hbm_gbs / 1e3,
+            "hbm_frac": hbm_gbs / PEAK_HBM_GBS,
+            "mfma_tflop_s": mfma_tflops,
+            "launch_ms_mean": mean_launch_s * 1e3,
+            "launch_ms_min": min(launch_ms),
+            "input_generation_s": round(t_gen, 2),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": mfma_tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": mfma_tflops / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+            "kernel": "decode_kernel (+merge when split)",
+            "flops_per_launch": flops,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,278 @@
+"""ctypes binding of libsparse_mla.so (C ABI in include/sparse_mla.h).
+
+Argument marshalling only: torch tensors supply device pointers and the current HIP
+stream; every step of the decode runs in the library's kernels.  The library must be
+built (python -m sparse_mla_decode_03_amd.build); loading fails loudly otherwise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsparse_mla.so")
+
+# status codes
+OK = 0
+ERR_NULL_ARG = 1
+ERR_BAD_SHAPE = 2
+ERR_UNSUPPORTED = 3
+ERR_MISALIGNED = 4
+ERR_WORKSPACE_TOO_SMALL = 5
+ERR_HIP = 6
+ERR_BAD_PLAN = 7
+
+KV_BF16 = 0
+KV_FP8_UE8M0 = 1
+IDX_LOGICAL = 0
+IDX_GLOBAL = 1
+F_PARTIALS_ONLY = 1
+F_CHECK_INDICES = 2
+
+EXPORTED = [
+    "sparse_mla_decode_plan", "sparse_mla_plan_num_splits", "sparse_mla_decode_run",
+    "sparse_mla_merge_partials", "sparse_mla_gather_debug", "sparse_mla_read_index_error",
+    "sparse_mla_status_string", "sparse_mla_version",
+]
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("num_rows", ctypes.c_int32), ("num_requests", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32), ("topk", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+        ("max_pages_per_req", ctypes.c_int32), ("kv_format", ctypes.c_int32),
+        ("index_mode", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+        ("flags", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+    ]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("opaque", ctypes.c_uint8 * 256)]
+
+
+class SparseMLAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m sparse_mla_decode_03_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32p, i32p = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p
+    lib.sparse_mla_decode_plan.argtypes = [ctypes.POINTER(Problem), i32, ctypes.POINTER(Plan),
+                                           ctypes.POINTER(ctypes.c_size_t)]
+    lib.sparse_mla_decode_plan.restype = ctypes.c_int
+    lib.sparse_mla_plan_num_splits.argtypes = [ctypes.POINTER(Plan)]
+    lib.sparse_mla_plan_num_splits.restype = i32
+    lib.sparse_mla_decode_run.argtypes = [ctypes.POINTER(Plan), vp, vp, i32p, i32p, i32p, f32p, vp,
+                                          f32p, f32p, f32p, vp, ctypes.c_size_t, vp]
+    lib.sparse_mla_decode_run.restype = ctypes.c_int
+    lib.sparse_mla_merge_partials.argtypes = [f32p, f32p, i32, i32, i32, f32p, vp, f32p, vp]
+    lib.sparse_mla_merge_partials.restype = ctypes.c_int
+    lib.sparse_mla_gather_debug.argtypes = [vp, i32, i32, i32, i32p, i32, vp, vp]
+    lib.sparse_mla_gather_debug.restype = ctypes.c_int
+    lib.sparse_mla_read_index_error.argtypes = [ctypes.POINTER(Plan), vp, ctypes.POINTER(i32 * 2), vp]
+    lib.sparse_mla_read_index_error.restype = ctypes.c_int
+    lib.sparse_mla_status_string.argtypes = [ctypes.c_int]
+    lib.sparse_mla_status_string.restype = ctypes.c_char_p
+    lib.sparse_mla_version.argtypes = []
+    lib.sparse_mla_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().sparse_mla_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != OK:
+        raise SparseMLAError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+@dataclass
+class PlanInfo:
+    plan: Plan
+    workspace_bytes: int
+    num_splits: int
+    problem: Problem
+
+
+def make_problem(num_rows, num_requests, num_heads, topk, page_size, num_pages,
+                 max_pages_per_req, kv_format, index_mode=IDX_LOGICAL, num_splits=0, flags=0,
+                 softmax_scale=1.0 / math.sqrt(576.0)) -> Problem:
+    return Problem(int(num_rows), int(num_requests), int(num_heads), int(topk), int(page_size),
+                   int(num_pages), int(max_pages_per_req), int(kv_format), int(index_mode),
+                   int(num_splits), int(flags), float(softmax_scale))
+
+
+def plan(problem: Problem, num_cus: int = 0) -> PlanInfo:
+    lib = load_library()
+    p = Plan()
+    ws = ctypes.c_size_t(0)
+    _check("sparse_mla_decode_plan",
+           lib.sparse_mla_decode_plan(ctypes.byref(problem), int(num_cus), ctypes.byref(p),
+                                      ctypes.byref(ws)))
+    return PlanInfo(p, int(ws.value), int(lib.sparse_mla_plan_num_splits(ctypes.byref(p))), problem)
+
+
+def run(info: PlanInfo, q, kv_cache, indices, row_req, page_table, sinks, out, lse=None,
+        partial_o=None, partial_lse=None, workspace=None, stream=None) -> None:
+    """Raw run: every tensor is caller-allocated on the GPU."""
+    lib = load_library()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("sparse_mla_decode_run",
+           lib.sparse_mla_decode_run(ctypes.byref(info.plan), _ptr(q), _ptr(kv_cache), _ptr(indices),
+                                     _ptr(row_req), _ptr(page_table), _ptr(sinks), _ptr(out),
+                                     _ptr(lse), _ptr(partial_o), _ptr(partial_lse), _ptr(workspace),
+                                     ctypes.c_size_t(ws_bytes), _stream(stream)))
+
+
+def _kv_format_of(kv_format) -> int:
+    if isinstance(kv_format, str):
+        return KV_FP8_UE8M0 if kv_format == "fp8" else KV_BF16
+    return int(kv_format)
+
+
+def _require(t: torch.Tensor, name: str, dtype, dev):
+    if t.device != dev:
+        raise ValueError(f"{name} must be on {dev}, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def sparse_mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, indices: torch.Tensor,
+                      row_req: Optional[torch.Tensor], page_table: Optional[torch.Tensor],
+                      sinks: Optional[torch.Tensor], kv_format, page_size: int,
+                      softmax_scale: float, index_mode: int = IDX_LOGICAL, num_splits: int = 0,
+                      flags: int = 0, num_cus: int = 0, stream=None, return_info: bool = False):
+    """Convenience wrapper: plan, allocate out/lse/workspace with torch, run.
+
+    q bf16 [R,H,576]; kv_cache uint8 [num_pages, page_bytes]; indices int32 [R,K];
+    row_req int32 [R] and page_table int32 [B,P] (LOGICAL mode); sinks fp32 [H] or None.
+    Returns (out bf16 [R,H,512], lse fp32 [R,H]) - or, with F_PARTIALS_ONLY,
+    (partial_o fp32 [R,S,H,512], partial_lse fp32 [R,S,H]).
+    """
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("sparse_mla_decode runs on the GPU only")
+    _require(q, "q", torch.bfloat16, dev)
+    _require(kv_cache, "kv_cache", torch.uint8, dev)
+    _require(indices, "indices", torch.int32, dev)
+    R, H, D = q.shape
+    if D != 576:
+        raise ValueError("q must be [R, H, 576]")
+    K = indices.shape[1]
+    if indices.shape[0] != R:
+        raise ValueError("indices must be [R, K]")
+    if index_mode == IDX_LOGICAL:
+        _require(row_req, "row_req", torch.int32, dev)
+        _require(page_table, "page_table", torch.int32, dev)
+        B, P = page_table.shape
+    else:
+        B, P = 0, 0
+    if index_mode == IDX_LOGICAL and row_req.numel() != R:
+        raise ValueError("row_req must hold one request id per row")
+    if sinks is not None:
+        _require(sinks, "sinks", torch.float32, dev)
+        if sinks.numel() != H:
+            raise ValueError("sinks must hold one value per head")
+    kvf = _kv_format_of(kv_format)
+    if kv_cache.dim() != 2 or kv_cache.shape[1] != (648 if kvf == KV_FP8_UE8M0 else 1152) * page_size:
+        raise ValueError("kv_cache must be [num_pages, page_bytes] for this format and page size")
+    prob = make_problem(R, B, H, K, page_size, kv_cache.shape[0], P, _kv_format_of(kv_format),
+                        index_mode, num_splits, flags, softmax_scale)
+    with torch.cuda.device(dev):
+        info = plan(prob, num_cus)
+        ws = (torch.empty(info.workspace_bytes, dtype=torch.uint8, device=dev)
+              if info.workspace_bytes > 0 else None)
+        if flags & F_PARTIALS_ONLY:
+            po = torch.empty((R, info.num_splits, H, 512), dtype=torch.float32, device=dev)
+            pl = torch.empty((R, info.num_splits, H), dtype=torch.float32, device=dev)
+            run(info, q, kv_cache, indices, row_req, page_table, sinks, None, None, po, pl, ws, stream)
+            res = (po, pl)
+        else:
+            out = torch.empty((R, H, 512), dtype=torch.bfloat16, device=dev)
+            lse = torch.empty((R, H), dtype=torch.float32, device=dev)
+            run(info, q, kv_cache, indices, row_req, page_table, sinks, out, lse, None, None, ws, stream)
+            res = (out, lse)
+    if return_info:
+        return res + (info, ws)
+    return res
+
+
+def merge_partials(partial_o: torch.Tensor, partial_lse: torch.Tensor,
+                   sinks: Optional[torch.Tensor], stream=None):
+    """LSE-merge partials [R,S,H,512] / [R,S,H] with the sink; returns (out, lse)."""
+    lib = load_library()
+    dev = partial_o.device
+    _require(partial_o, "partial_o", torch.float32, dev)
+    _require(partial_lse, "partial_lse", torch.float32, dev)
+    R, S, H, D = partial_o.shape
+    if D != 512 or tuple(partial_lse.shape) != (R, S, H):
+        raise ValueError("partials must be [R,S,H,512] and [R,S,H]")
+    if sinks is not None:
+        _require(sinks, "sinks", torch.float32, dev)
+    out = torch.empty((R, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((R, H), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check("sparse_mla_merge_partials",
+               lib.sparse_mla_merge_partials(_ptr(partial_o), _ptr(partial_lse), R, S, H,
+                                             _ptr(sinks), _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def gather_debug(kv_cache: torch.Tensor, kv_format, page_size: int, slots: torch.Tensor,
+                 stream=None) -> torch.Tensor:
+    """Dequantize cache slots to bf16 [n, 576] with the decode kernel's gather code."""
+    lib = load_library()
+    dev = kv_cache.device
+    _require(kv_cache, "kv_cache", torch.uint8, dev)
+    _require(slots, "slots", torch.int32, dev)
+    if kv_cache.dim() != 2 or kv_cache.shape[1] != (648 if _kv_format_of(kv_format) == KV_FP8_UE8M0
+                                                    else 1152) * page_size:
+        raise ValueError("kv_cache must be [num_pages, page_bytes] for this format and page size")
+    n = slots.numel()
+    out = torch.empty((n, 576), dtype=torch.bfloat16, device=dev)
+    with torch.cuda.device(dev):
+        _check("sparse_mla_gather_debug",
+               lib.sparse_mla_gather_debug(_ptr(kv_cache), _kv_format_of(kv_format), int(page_size),
+                                           int(kv_cache.shape[0]), _ptr(slots), int(n), _ptr(out),
+                                           _stream(stream)))
+    return out
+
+
+def read_index_error(info: PlanInfo, workspace: torch.Tensor, stream=None):
+    lib = load_library()
+    rp = (ctypes.c_int32 * 2)()
+    _check("sparse_mla_read_index_error",
+           lib.sparse_mla_read_index_error(ctypes.byref(info.plan), _ptr(workspace), ctypes.byref(rp),
+                                           _stream(stream)))
+    return int(rp[0]), int(rp[1])

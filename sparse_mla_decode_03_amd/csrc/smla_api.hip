@@ -1,0 +1,297 @@
+// Host side of the C ABI declared in include/sparse_mla.h: argument checks, the
+// data-independent split planner, and kernel launches on the caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "sparse_mla.h"
+#include "smla_kernels.h"
+
+namespace {
+
+constexpr uint32_t kPlanMagic = 0x534d4c41u;  // "SMLA"
+constexpr int kMaxDevices = 64;
+
+struct PlanImpl {
+  uint32_t magic;
+  int32_t num_splits;
+  int32_t chunk;
+  int32_t ps_log2;
+  smla_problem p;
+  uint64_t off_part_o;
+  uint64_t off_part_lse;
+  uint64_t off_err;
+  uint64_t ws_bytes;
+};
+static_assert(sizeof(PlanImpl) <= sizeof(smla_plan), "plan does not fit its opaque storage");
+
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int cu_count(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < kMaxDevices) {
+    const int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *out = c;
+      return 0;
+    }
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return -1;
+  if (dev < kMaxDevices) g_cu_count[dev].store(n, std::memory_order_relaxed);
+  *out = n;
+  return 0;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+int log2_exact(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return (1 << l) == v ? l : -1;
+}
+
+const PlanImpl* as_impl(const smla_plan* plan) {
+  if (plan == nullptr) return nullptr;
+  const PlanImpl* pi = reinterpret_cast<const PlanImpl*>(plan->opaque);
+  return pi->magic == kPlanMagic ? pi : nullptr;
+}
+
+smla_status check_problem(const smla_problem* p) {
+  if (p->num_rows < 0 || p->topk < 4 || p->num_pages < 1) return SMLA_ERR_BAD_SHAPE;
+  if (p->topk % 4 != 0) return SMLA_ERR_MISALIGNED;
+  if (p->num_heads % 16 != 0 || p->num_heads < 16 || p->num_heads > SMLA_MAX_HEADS)
+    return SMLA_ERR_UNSUPPORTED;
+  if (p->kv_format != SMLA_KV_BF16 && p->kv_format != SMLA_KV_FP8_UE8M0) return SMLA_ERR_UNSUPPORTED;
+  if (p->index_mode != SMLA_IDX_LOGICAL && p->index_mode != SMLA_IDX_GLOBAL) return SMLA_ERR_UNSUPPORTED;
+  if (p->flags & ~(SMLA_F_PARTIALS_ONLY | SMLA_F_CHECK_INDICES)) return SMLA_ERR_UNSUPPORTED;
+  const int l = log2_exact(p->page_size);
+  if (p->page_size < 1 || p->page_size > 1024 || l < 0) return SMLA_ERR_BAD_SHAPE;
+  if ((int64_t)p->num_pages * p->page_size > INT32_MAX) return SMLA_ERR_BAD_SHAPE;
+  if (p->index_mode == SMLA_IDX_LOGICAL) {
+    if (p->num_requests < 1 || p->max_pages_per_req < 1) return SMLA_ERR_BAD_SHAPE;
+    if ((int64_t)p->max_pages_per_req * p->page_size > INT32_MAX) return SMLA_ERR_BAD_SHAPE;
+  }
+  if (p->num_splits < 0 || p->num_splits > SMLA_MAX_SPLITS || p->num_splits > p->topk)
+    return SMLA_ERR_BAD_SHAPE;
+  if (!isfinite(p->softmax_scale)) return SMLA_ERR_BAD_SHAPE;
+  return SMLA_OK;
+}
+
+// Splits: enough (row, split) workgroups to give every CU work when there are few rows,
+// chunks of at least 128 positions, and at most the per-workgroup position capacity.
+int choose_splits(const smla_problem* p, int num_cus) {
+  const int cap = smla::max_chunk_positions();
+  const int min_s = (p->topk + cap - 1) / cap;
+  int s = min_s;
+  const int64_t rows = p->num_rows > 0 ? p->num_rows : 1;
+  if (rows < num_cus) {
+    int want = (int)((num_cus + rows - 1) / rows);
+    const int by_len = p->topk / 128 > 0 ? p->topk / 128 : 1;
+    if (want > by_len) want = by_len;
+    if (want > s) s = want;
+  }
+  if (s > SMLA_MAX_SPLITS) s = SMLA_MAX_SPLITS;
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+smla_status sparse_mla_decode_plan(const smla_problem* p, int32_t num_cus, smla_plan* plan,
+                                   size_t* workspace_bytes) {
+  if (p == nullptr || plan == nullptr || workspace_bytes == nullptr) return SMLA_ERR_NULL_ARG;
+  const smla_status st = check_problem(p);
+  if (st != SMLA_OK) return st;
+  int cus = num_cus;
+  if (cus <= 0 && cu_count(&cus) != 0) return SMLA_ERR_HIP;
+  const int cap = smla::max_chunk_positions();
+  int s = p->num_splits > 0 ? p->num_splits : choose_splits(p, cus);
+  const int chunk = (p->topk + s - 1) / s;
+  if (chunk > cap) return SMLA_ERR_UNSUPPORTED;
+
+  PlanImpl pi;
+  memset(&pi, 0, sizeof(pi));
+  pi.magic = kPlanMagic;
+  pi.num_splits = s;
+  pi.chunk = chunk;
+  pi.ps_log2 = log2_exact(p->page_size);
+  pi.p = *p;
+  uint64_t off = 0;
+  const bool partials_in_ws = s > 1 && !(p->flags & SMLA_F_PARTIALS_ONLY);
+  if (partials_in_ws) {
+    const uint64_t rsh = (uint64_t)p->num_rows * s * p->num_heads;
+    pi.off_part_o = off;
+    off = round_up(off + rsh * SMLA_V_DIM * sizeof(float), 256);
+    pi.off_part_lse = off;
+    off = round_up(off + rsh * sizeof(float), 256);
+  }
+  if (p->flags & SMLA_F_CHECK_INDICES) {
+    pi.off_err = off;
+    off = round_up(off + sizeof(unsigned long long), 256);
+  }
+  pi.ws_bytes = off;
+  memset(plan, 0, sizeof(*plan));
+  memcpy(plan->opaque, &pi, sizeof(pi));
+  *workspace_bytes = (size_t)off;
+  return SMLA_OK;
+}
+
+int32_t sparse_mla_plan_num_splits(const smla_plan* plan) {
+  const PlanImpl* pi = as_impl(plan);
+  return pi ? pi->num_splits : -1;
+}
+
+smla_status sparse_mla_decode_run(const smla_plan* plan, const void* q, const void* kv_cache,
+                                  const int32_t* indices, const int32_t* row_req,
+                                  const int32_t* page_table, const float* sinks, void* out,
+                                  float* lse, float* partial_o, float* partial_lse,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  const PlanImpl* pi = as_impl(plan);
+  if (pi == nullptr) return SMLA_ERR_BAD_PLAN;
+  const smla_problem& p = pi->p;
+  const bool partials_only = (p.flags & SMLA_F_PARTIALS_ONLY) != 0;
+  const bool logical = p.index_mode == SMLA_IDX_LOGICAL;
+  if (q == nullptr || kv_cache == nullptr || indices == nullptr) return SMLA_ERR_NULL_ARG;
+  if (logical && (row_req == nullptr || page_table == nullptr)) return SMLA_ERR_NULL_ARG;
+  if (partials_only ? (partial_o == nullptr || partial_lse == nullptr) : out == nullptr)
+    return SMLA_ERR_NULL_ARG;
+  if (pi->ws_bytes > 0 && workspace == nullptr) return SMLA_ERR_NULL_ARG;
+  if (workspace_bytes < pi->ws_bytes) return SMLA_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(indices, 16) || !aligned(out, 16) ||
+      !aligned(partial_o, 16) || !aligned(partial_lse, 4) || !aligned(lse, 4) ||
+      !aligned(sinks, 4) || !aligned(row_req, 4) || !aligned(page_table, 4) ||
+      !aligned(workspace, 256))
+    return SMLA_ERR_MISALIGNED;
+  if (p.num_rows == 0) return SMLA_OK;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  smla::DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = reinterpret_cast<const uint16_t*>(q);
+  a.kv = reinterpret_cast<const uint8_t*>(kv_cache);
+  a.indices = indices;
+  a.row_req = row_req;
+  a.page_table = page_table;
+  a.sinks = sinks;
+  a.R = p.num_rows;
+  a.H = p.num_heads;
+  a.K = p.topk;
+  a.S = pi->num_splits;
+  a.chunk = pi->chunk;
+  a.B = logical ? p.num_requests : 0;
+  a.ps_log2 = pi->ps_log2;
+  a.num_pages = p.num_pages;
+  a.num_slots = p.num_pages * p.page_size;
+  a.max_pages = logical ? p.max_pages_per_req : 0;
+  a.index_mode = p.index_mode;
+  a.scale_log2 = p.softmax_scale * 1.4426950408889634f;
+  if (p.flags & SMLA_F_CHECK_INDICES) {
+    a.err = reinterpret_cast<unsigned long long*>(ws + pi->off_err);
+    if (smla::launch_fill_u64(a.err, ~0ull, st) != hipSuccess) return SMLA_ERR_HIP;
+  }
+  const bool merge = pi->num_splits > 1 && !partials_only;
+  if (partials_only) {
+    a.write_partials = 1;
+    a.part_o = partial_o;
+    a.part_lse = partial_lse;
+  } else if (merge) {
+    a.write_partials = 1;
+    a.part_o = reinterpret_cast<float*>(ws + pi->off_part_o);
+    a.part_lse = reinterpret_cast<float*>(ws + pi->off_part_lse);
+  } else {
+    a.write_partials = 0;
+    a.out = reinterpret_cast<uint16_t*>(out);
+    a.lse = lse;
+  }
+  if (smla::launch_decode(a, p.kv_format, st) != hipSuccess) return SMLA_ERR_HIP;
+  if (merge) {
+    if (smla::launch_merge(a.part_o, a.part_lse, a.R, a.S, a.H, sinks,
+                           reinterpret_cast<uint16_t*>(out), lse, st) != hipSuccess)
+      return SMLA_ERR_HIP;
+  }
+  return SMLA_OK;
+}
+
+smla_status sparse_mla_merge_partials(const float* partial_o, const float* partial_lse,
+                                      int32_t num_rows, int32_t num_splits, int32_t num_heads,
+                                      const float* sinks, void* out, float* lse, void* stream) {
+  if (num_rows < 0 || num_splits < 1 || num_splits > SMLA_MAX_SPLITS || num_heads < 1 ||
+      num_heads > 1024)
+    return SMLA_ERR_BAD_SHAPE;
+  if ((int64_t)num_rows * num_heads > INT32_MAX) return SMLA_ERR_BAD_SHAPE;
+  if (num_rows == 0) return SMLA_OK;
+  if (partial_o == nullptr || partial_lse == nullptr || out == nullptr) return SMLA_ERR_NULL_ARG;
+  if (!aligned(partial_o, 16) || !aligned(out, 16) || !aligned(partial_lse, 4) || !aligned(lse, 4) ||
+      !aligned(sinks, 4))
+    return SMLA_ERR_MISALIGNED;
+  if (smla::launch_merge(partial_o, partial_lse, num_rows, num_splits, num_heads, sinks,
+                         reinterpret_cast<uint16_t*>(out), lse,
+                         reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return SMLA_ERR_HIP;
+  return SMLA_OK;
+}
+
+smla_status sparse_mla_gather_debug(const void* kv_cache, int32_t kv_format, int32_t page_size,
+                                    int32_t num_pages, const int32_t* slots, int32_t n, void* out,
+                                    void* stream) {
+  if (kv_format != SMLA_KV_BF16 && kv_format != SMLA_KV_FP8_UE8M0) return SMLA_ERR_UNSUPPORTED;
+  const int l = log2_exact(page_size);
+  if (n < 0 || num_pages < 1 || page_size < 1 || page_size > 1024 || l < 0 ||
+      (int64_t)num_pages * page_size > INT32_MAX)
+    return SMLA_ERR_BAD_SHAPE;
+  if (n == 0) return SMLA_OK;
+  if (kv_cache == nullptr || slots == nullptr || out == nullptr) return SMLA_ERR_NULL_ARG;
+  if (!aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(slots, 4)) return SMLA_ERR_MISALIGNED;
+  if (smla::launch_gather_debug(reinterpret_cast<const uint8_t*>(kv_cache), kv_format, l,
+                                num_pages * page_size, slots, n, reinterpret_cast<uint16_t*>(out),
+                                reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return SMLA_ERR_HIP;
+  return SMLA_OK;
+}
+
+smla_status sparse_mla_read_index_error(const smla_plan* plan, const void* workspace,
+                                        int32_t* row_pos, void* stream) {
+  const PlanImpl* pi = as_impl(plan);
+  if (pi == nullptr) return SMLA_ERR_BAD_PLAN;
+  if (row_pos == nullptr || workspace == nullptr) return SMLA_ERR_NULL_ARG;
+  if (!(pi->p.flags & SMLA_F_CHECK_INDICES)) return SMLA_ERR_UNSUPPORTED;
+  unsigned long long v = 0;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(workspace) + pi->off_err;
+  if (hipMemcpyAsync(&v, src, sizeof(v), hipMemcpyDeviceToHost, st) != hipSuccess) return SMLA_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return SMLA_ERR_HIP;
+  if (v == ~0ull) {
+    row_pos[0] = -1;
+    row_pos[1] = -1;
+  } else {
+    row_pos[0] = (int32_t)(v >> 32);
+    row_pos[1] = (int32_t)(v & 0xffffffffu);
+  }
+  return SMLA_OK;
+}
+
+const char* sparse_mla_status_string(smla_status s) {
+  switch (s) {
+    case SMLA_OK: return "ok";
+    case SMLA_ERR_NULL_ARG: return "a required pointer is NULL";
+    case SMLA_ERR_BAD_SHAPE: return "invalid or inconsistent size";
+    case SMLA_ERR_UNSUPPORTED: return "unsupported head count, format, index mode, flag or split";
+    case SMLA_ERR_MISALIGNED: return "pointer or row stride breaks the alignment rule";
+    case SMLA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the plan requires";
+    case SMLA_ERR_HIP: return "HIP runtime error";
+    case SMLA_ERR_BAD_PLAN: return "plan was not produced by sparse_mla_decode_plan";
+    default: return "unknown status";
+  }
+}
+
+int32_t sparse_mla_version(void) { return 100; }
+
+}  // extern "C"

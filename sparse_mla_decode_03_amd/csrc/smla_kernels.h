@@ -1,0 +1,35 @@
+// Launch interface between the host API and the gfx950 kernels (library-internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+struct DecodeArgs {
+  const uint16_t* q;            // bf16 [R][H][576]
+  const uint8_t* kv;            // paged cache bytes
+  const int32_t* indices;       // [R][K]
+  const int32_t* row_req;       // [R]            (LOGICAL)
+  const int32_t* page_table;    // [B][max_pages] (LOGICAL)
+  const float* sinks;           // [H] or null
+  uint16_t* out;                // bf16 [R][H][512]      (final mode)
+  float* lse;                   // [R][H] or null        (final mode)
+  float* part_o;                // [R][S][H][512]        (partial mode)
+  float* part_lse;              // [R][S][H]             (partial mode)
+  unsigned long long* err;      // first bad (row << 32 | pos), or null
+  int32_t R, H, K, S, chunk, B;
+  int32_t ps_log2, num_pages, num_slots, max_pages, index_mode;
+  int32_t write_partials;
+  float scale_log2;             // softmax_scale * log2(e)
+};
+
+int max_chunk_positions();
+hipError_t launch_decode(const DecodeArgs& a, int kv_format, hipStream_t st);
+hipError_t launch_merge(const float* part_o, const float* part_lse, int R, int S, int H,
+                        const float* sinks, uint16_t* out, float* lse, hipStream_t st);
+hipError_t launch_gather_debug(const uint8_t* kv, int kv_format, int ps_log2, int num_slots,
+                               const int* slots, int n, uint16_t* out, hipStream_t st);
+hipError_t launch_fill_u64(unsigned long long* p, unsigned long long v, hipStream_t st);
+
+}  // namespace smla

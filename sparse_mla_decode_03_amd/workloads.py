@@ -237,12 +237,10 @@ def make_inputs(spec: WorkloadSpec, seed: int, device="cpu", cache_device=None) 
             sinks[: spec.num_heads // 2] = -np.inf
         sinks = torch.from_numpy(sinks)
     cache = make_cache(num_pages, ps, spec.kv_format, seed, device=cache_device)
-    inp = Inputs(spec, q, cache, torch.from_numpy(indices), torch.from_numpy(row_req),
-                 torch.from_numpy(page_table), sinks, torch.from_numpy(ctx.astype(np.int32)),
-                 {"seed": seed, "shared": shared})
-    small = inp.to(device)
-    small.kv_cache = cache
-    return small
+    mv = lambda t: None if t is None else t.to(device)  # noqa: E731
+    return Inputs(spec, mv(q), cache, mv(torch.from_numpy(indices)), mv(torch.from_numpy(row_req)),
+                  mv(torch.from_numpy(page_table)), mv(sinks),
+                  mv(torch.from_numpy(ctx.astype(np.int32))), {"seed": seed, "shared": shared})
 
 
 def compulsory_bytes(inp: Inputs) -> int:
