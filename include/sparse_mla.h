@@ -164,7 +164,8 @@ int32_t sparse_mla_plan_num_splits(const smla_plan* plan);
  *   partial_lse fp32 [R][S][H]       only with SMLA_F_PARTIALS_ONLY, else NULL
  *   workspace   device scratch of at least the planned size (may be NULL when it is 0);
  *               256-byte aligned; its contents need not be initialised
- * R == 0 returns SMLA_OK without launching.  No device-to-host traffic and no
+ * R == 0 returns SMLA_OK without launching or checking pointers (empty tensors may
+ * pass NULL).  No device-to-host traffic and no
  * allocation: the call can be captured in a HIP graph.
  * Errors: BAD_PLAN, NULL_ARG, MISALIGNED, WORKSPACE_TOO_SMALL, HIP. */
 smla_status sparse_mla_decode_run(const smla_plan* plan, const void* q, const void* kv_cache,

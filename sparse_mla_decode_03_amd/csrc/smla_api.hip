@@ -158,6 +158,7 @@ smla_status sparse_mla_decode_run(const smla_plan* plan, const void* q, const vo
   const smla_problem& p = pi->p;
   const bool partials_only = (p.flags & SMLA_F_PARTIALS_ONLY) != 0;
   const bool logical = p.index_mode == SMLA_IDX_LOGICAL;
+  if (p.num_rows == 0) return SMLA_OK;  // nothing to do; empty tensors may pass NULL
   if (q == nullptr || kv_cache == nullptr || indices == nullptr) return SMLA_ERR_NULL_ARG;
   if (logical && (row_req == nullptr || page_table == nullptr)) return SMLA_ERR_NULL_ARG;
   if (partials_only ? (partial_o == nullptr || partial_lse == nullptr) : out == nullptr)
@@ -169,7 +170,6 @@ smla_status sparse_mla_decode_run(const smla_plan* plan, const void* q, const vo
       !aligned(sinks, 4) || !aligned(row_req, 4) || !aligned(page_table, 4) ||
       !aligned(workspace, 256))
     return SMLA_ERR_MISALIGNED;
-  if (p.num_rows == 0) return SMLA_OK;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);

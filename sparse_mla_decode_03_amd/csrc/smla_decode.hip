@@ -237,11 +237,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       lse_v = -INFINITY;
     }
   } else {
-    const float sig2 = (a.sinks != nullptr) ? a.sinks[h] * kLog2e : -INFINITY;
+    const float sink = (a.sinks != nullptr) ? a.sinks[h] : -INFINITY;
+    const float sig2 = sink * kLog2e;
     const float M = fmaxf(m_used, sig2);
-    if (M == -INFINITY) {
+    if (m_used == -INFINITY) {
+      // no valid entry: out = 0 and the LSE is the sink itself
       factor = 0.f;
-      lse_v = -INFINITY;
+      lse_v = sink;
     } else {
       const float al = __builtin_amdgcn_exp2f(m_used - M);
       const float z = l_tot * al + __builtin_amdgcn_exp2f(sig2 - M);

@@ -21,13 +21,15 @@ __global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ po,
   const int r = (int)(rh / H);
   const int h = (int)(rh % H);
   const int lane = threadIdx.x;
-  const float sig2 = (sinks != nullptr) ? sinks[h] * kLog2e : -INFINITY;
+  const float sink = (sinks != nullptr) ? sinks[h] : -INFINITY;
+  const float sig2 = sink * kLog2e;
   const float* plr = pl + (size_t)r * S * H + h;
-  float M = sig2;
-  for (int c = 0; c < S; ++c) M = fmaxf(M, plr[(size_t)c * H] * kLog2e);
+  float mc = -INFINITY;
+  for (int c = 0; c < S; ++c) mc = fmaxf(mc, plr[(size_t)c * H] * kLog2e);
+  const float M = fmaxf(mc, sig2);
   u32x4 res = u32x4{0u, 0u, 0u, 0u};
-  float lse_v = -INFINITY;
-  if (M != -INFINITY) {
+  float lse_v = sink;  // every chunk empty: out = 0, LSE = the sink (or -inf)
+  if (mc != -INFINITY) {
     float z = (sig2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sig2 - M);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c < S; ++c) {
