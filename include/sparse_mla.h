@@ -122,7 +122,7 @@ typedef struct {
   int32_t topk;              /* K = index row stride in int32 elements; >= 4 and a multiple of 4
                                 (16-byte aligned rows, as the page prhub vllm#43827 notes for
                                 the FlashInfer sparse kernels, review highlights item 2) */
-  int32_t page_size;         /* tokens per page; a power of two in [1, 1024] */
+  int32_t page_size;         /* tokens per page; a power of two in [1, 1024] (>= 2 for FP8) */
   int32_t num_pages;         /* pages in kv_cache; >= 1 */
   int32_t max_pages_per_req; /* page_table row stride; >= 1 in LOGICAL mode */
   int32_t kv_format;         /* smla_kv_format */

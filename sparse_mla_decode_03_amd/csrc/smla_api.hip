@@ -72,6 +72,8 @@ smla_status check_problem(const smla_problem* p) {
   if (p->flags & ~(SMLA_F_PARTIALS_ONLY | SMLA_F_CHECK_INDICES)) return SMLA_ERR_UNSUPPORTED;
   const int l = log2_exact(p->page_size);
   if (p->page_size < 1 || p->page_size > 1024 || l < 0) return SMLA_ERR_BAD_SHAPE;
+  // FP8 pages are 648 * page_size bytes; the 16-byte copies need an even page size
+  if (p->kv_format == SMLA_KV_FP8_UE8M0 && p->page_size < 2) return SMLA_ERR_UNSUPPORTED;
   if ((int64_t)p->num_pages * p->page_size > INT32_MAX) return SMLA_ERR_BAD_SHAPE;
   if (p->index_mode == SMLA_IDX_LOGICAL) {
     if (p->num_requests < 1 || p->max_pages_per_req < 1) return SMLA_ERR_BAD_SHAPE;

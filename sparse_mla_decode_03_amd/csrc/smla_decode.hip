@@ -1,19 +1,24 @@
 // Fused top-k sparse MLA decode kernel for gfx950.
 //
-// One workgroup handles one (query row, split) pair with all H query heads, as H/16
-// waves of 16 heads each.  Steps, in the order of the Triton decode path described on
-// prhub sglang#24692 ("SM120 support for DeepSeek-V4", implementation breakdown 2-3):
+// One workgroup handles one (query row, split) pair with all H query heads, as
+// ceil(H/32) waves of 32 heads each.  Steps, in the order of the Triton decode path
+// described on prhub sglang#24692 ("SM120 support for DeepSeek-V4", implementation
+// breakdown 2-3):
 //   1. index translation + compaction: the row's top-k positions of this split are
 //      turned into cache slots through the page table (the block-table translation of
 //      prhub vllm#43477, key code excerpts: forward_mqa); -1 and out-of-range entries
 //      are dropped, the surviving slots are packed densely into LDS (order kept);
-//   2. per tile of 32 slots: gather the entries from HBM, dequantize FP8+UE8M0 (or take
-//      BF16) into bf16, store them in LDS twice - row-major K [32][576] for QK and
-//      transposed V^T [512][32] for PV;
-//   3. QK: S^T[32 tokens][16 heads] per wave on bf16 MFMA 16x16x32 with q in registers;
-//   4. online softmax in the exp2 domain with a lazily raised running max (rescaling O
-//      only when the tile max exceeds the max in use by more than 2^8);
-//   5. PV: O[16 heads][512] += P[16][32] V[32][512] on bf16 MFMA, O in registers;
+//   2. per tile of 32 slots: the entries' bytes are copied from HBM straight into LDS
+//      (global_load_lds, no registers held) while the previous tile is computed; FP8
+//      entries are then dequantized (e4m3fn code x 2^(scale-127)) by the lane that
+//      copied them into a bf16 tile K[32][576]; BF16 entries land in K directly;
+//   3. QK: S^T[32 tokens][32 heads] per wave on bf16 MFMA 32x32x16, K rows as the A
+//      operand, q (register resident) as B;
+//   4. softmax in the exp2 domain against a per-head reference max taken at the first
+//      tile (see kRestartLog2);
+//   5. PV: O[32 heads][512] += P[32][32] V[32][512] on bf16 MFMA with P straight from
+//      the QK accumulator registers and V read from the same K tile with LDS transpose
+//      reads (no separate V^T copy);
 //   6. epilogue: final output with the sink folded in, or the sink-free split partial.
 #include "smla_device.h"
 #include "smla_kernels.h"
@@ -22,35 +27,90 @@ namespace smla {
 
 namespace {
 
-constexpr int kT = 32;        // tokens per tile
-constexpr int kKStr = 584;    // bf16 per K row in LDS: 576 + 8 pad -> 1168 B, staggers banks
-constexpr int kCMax = 2048;   // positions per split handled by one workgroup
-constexpr float kRescaleLog2 = 8.0f;
+constexpr int kT = 32;                  // tokens per tile (MFMA M dimension)
+constexpr int kLatS = 520;              // bf16 per latent row of a K tile: 512 + 8 pad (1040 B)
+constexpr int kRopeOff = kT * kLatS;    // rope region: [32][64] bf16 after the latent rows
+constexpr int kTile = kRopeOff + kT * 64;  // bf16 per tile (37,376 bytes)
+constexpr int kCMax = 2048;             // positions per split handled by one workgroup
+constexpr int kDepth = 4;               // LDS operand loads kept in flight
+// Exponentials are taken against a per-head reference max fixed at the first tile, so P
+// may exceed 1.  When a later tile's max exceeds the reference by more than 2^32 the
+// workgroup repeats the pass over the row with the larger reference; fp32 and bf16 hold
+// P <= 2^32 without overflow.
+constexpr float kRestartLog2 = 32.0f;
 
-// V^T element (d, p) for tile position p in 0..31: rows of 32 bf16 (64 B) split into
-// four 16-byte chunks, the chunk index XOR-swizzled by d so that 8 consecutive rows
-// read at the same chunk hit 8 different bank groups.
-__device__ __forceinline__ int vt_off(int d, int p) {
-  const int sw = ((d >> 1) ^ (d >> 3)) & 3;
-  return d * kT + ((((p >> 3) ^ sw) & 3) << 3) + (p & 7);
+// K tile layout: latent rows padded to 1040 bytes, so 8 consecutive rows read at the same
+// column start 16 bytes apart in the 128-byte bank cycle (no conflicts for the MFMA
+// operand loads); rope rows of 128 bytes unpadded, so 8 of them form one contiguous
+// kilobyte for the DMA.  Every operand address is a lane base plus a constant.
+__device__ __forceinline__ int lat_at(int row, int col) { return row * kLatS + col; }
+__device__ __forceinline__ int rope_at(int row, int col) { return kRopeOff + row * 64 + col; }
+
+// Token position (0..31) held in accumulator register r (0..15) of lane group G (lane/32)
+// by a 32x32 MFMA whose rows are tokens.
+__device__ __forceinline__ int acc_row(int r, int G) { return 8 * (r >> 2) + 4 * G + (r & 3); }
+
+// Copy 16 (or 4) bytes per lane from global memory into LDS at dst + lane*size.
+__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
 }
+__device__ __forceinline__ void dma4(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_wave_base), 4, 0, 0);
+}
+// Wait until this wave's outstanding global loads (and LDS copies) have landed.
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Per-configuration LDS and work split.  A tile is gathered by 64-lane DMA instructions
+// that each fill 1 KB of LDS.  FP8: instructions 0..15 copy the latent codes of tokens
+// 2i, 2i+1 (32 units of 16 bytes each) and 16..19 the rope of tokens 8(i-16)..+7 into a
+// raw staging area laid out latent[32][512 B] | rope[32][128 B]; each wave also copies
+// the tile's 32 x 8 scale bytes for itself.  BF16: instructions 0..31 copy the latent row
+// of token i and 32..35 the rope of tokens 8(i-32)..+7 straight into the K tile.  Wave w
+// issues instructions w, w+NW, w+2NW, ...  With three or more waves (one workgroup per
+// CU) the K tile is double-buffered; with fewer, a single tile keeps the workgroup small
+// enough for two per CU.
+template <int NW, int FMT>
+struct Cfg {
+  static constexpr int NI = FMT == 1 ? 20 : 36;         // DMA instructions per tile
+  static constexpr int PER = (NI + NW - 1) / NW;        // per wave (the last ones may idle)
+  // Tiles in flight and K tile buffers.  FP8 stages raw bytes (NS stages) and dequantizes
+  // into NK bf16 K tiles; BF16 copies into a ring of NS + 1 K tiles, or synchronously
+  // (NS = 0) when the workgroup must stay small enough for two per CU.
+  static constexpr bool BIG = NW >= 3;                  // one workgroup per CU
+  static constexpr int NS = FMT == 1 ? (BIG ? 3 : 1) : (BIG ? 2 : 0);
+  static constexpr int NK = FMT == 1 ? (BIG ? 2 : 1) : (BIG ? NS + 1 : 1);
+  static constexpr int RAW_BYTES = FMT == 1 ? NS * 20 * 1024 : 16;
+  static constexpr int SCL_BYTES = FMT == 1 ? NS * NW * 256 : 16;
+  // DMA instructions every wave issues per tile (scale copy included), rounded down
+  static constexpr int PERW = NI / NW + (FMT == 1 ? 1 : 0);
+};
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are pending
+// (vmcnt split over bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 
 template <int NW, int FMT>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
+  using C = Cfg<NW, FMT>;
   constexpr int NT = NW * 64;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kT * kKStr];
-  __shared__ __attribute__((aligned(16))) uint16_t sVT[kV * kT];
+  constexpr int PER = C::PER;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[C::NK * kTile];
+  __shared__ __attribute__((aligned(16))) uint8_t sRaw[C::RAW_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sScl[C::SCL_BYTES];
   __shared__ int sSlots[kCMax];
   __shared__ int sWcnt[NW];
+  __shared__ int sRestart;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  const int lane_id = lane;
   const int wave = tid >> 6;
   const int row = blockIdx.x;
   const int split = blockIdx.y;
   const int p0 = split * a.chunk;
   const int p1 = min(p0 + a.chunk, a.K);
   const int ps_mask = (1 << a.ps_log2) - 1;
+  if (tid == 0) sRestart = 0;
 
   // ---- 1. translate and compact the split's indices --------------------------------
   int req = 0;
@@ -100,133 +160,275 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     __syncthreads();
   }
 
-  // ---- q fragments: lane holds head 16*wave + lane%16, dims 32*ks + 8*(lane/16) + 0..7
-  const int g = lane >> 4;
-  const int hl = lane & 15;
-  const int h = wave * 16 + hl;
-  u32x4 qf[18];
+  // ---- q fragments: lane holds head 32*wave + lane%32, dims 16*ks + 8*(lane/32) + 0..7
+  // (padded heads read a real head's q; their results are never written)
+  const int hl = lane & 31;
+  const int G = lane >> 5;
+  const int h = wave * 32 + hl;
+  const bool h_ok = h < a.H;
+  u32x4 qf[36];
   {
-    const uint16_t* qp = a.q + ((size_t)row * a.H + h) * kQK + 8 * g;
+    const uint16_t* qp = a.q + ((size_t)row * a.H + min(h, a.H - 1)) * kQK + 8 * G;
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qp + 32 * ks);
+    for (int ks = 0; ks < 36; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+    // land q before the tile loop, so no wait on the in-flight tile copies is placed at
+    // its first use inside the loop
+    wait_vm();
   }
 
-  f32x4 O[32];
-#pragma unroll
-  for (int b = 0; b < 32; ++b) O[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_used = -INFINITY;
-  float l_part = 0.f;
 
-  for (int t0 = 0; t0 < n_valid; t0 += kT) {
+  // ---- 2. gather (see Cfg for the DMA instruction map).  Every DMA instruction of a
+  // tile is issued, also for tokens past the valid count (they read a dummy address in
+  // the cache and are zeroed when the tile is finished), so that the number of pending
+  // copies per wave is fixed and vmcnt waits can target the oldest tile.
+  auto dma_tile = [&](int tile) {
+    // The lane id passes through an empty asm statement so that the per-lane address
+    // terms below are recomputed here instead of being hoisted out of the tile loop
+    // (which costs registers, then spills whose reloads would wait on the copies).
+    int lane = lane_id;
+    asm volatile("" : "+v"(lane));
+    const int t0 = tile * kT;
+    const int st = C::NS > 0 ? tile % (FMT == 1 ? C::NS : C::NK) : 0;
+    uint16_t* K = sK + (FMT == 1 ? 0 : st) * kTile;
+    uint8_t* raw = sRaw + (FMT == 1 ? st : 0) * (20 * 1024);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int ins = wave + NW * j;
+      if (ins < C::NI) {
+        int t, src_off;
+        uint8_t* dst;
+        if (FMT == 1) {
+          if (ins < 16) {
+            t = 2 * ins + (lane >> 5);
+            src_off = 16 * (lane & 31);
+          } else {
+            t = 8 * (ins - 16) + (lane >> 3);
+            src_off = -1 - 16 * (lane & 7);          // rope chunk, marked negative
+          }
+          dst = raw + ins * 1024;
+        } else {
+          if (ins < 32) {
+            t = ins;
+            src_off = 16 * lane;
+            dst = reinterpret_cast<uint8_t*>(K + lat_at(t, 0));
+          } else {
+            t = 8 * (ins - 32) + (lane >> 3);
+            src_off = 1024 + 16 * (lane & 7);
+            dst = reinterpret_cast<uint8_t*>(K + kRopeOff) + (ins - 32) * 1024;
+          }
+        }
+        const uint8_t* src = a.kv + 16 * lane;       // dummy for tokens past the end
+        if (t0 + t < n_valid) {
+          const SlotAddr sa = slot_addr<FMT>(sSlots[t0 + t], a.ps_log2);
+          src = (FMT == 1 && src_off < 0) ? a.kv + sa.rope + (-1 - src_off) : a.kv + sa.latent + src_off;
+        }
+        dma16(src, dst);
+      }
+    }
+    if (FMT == 1) {
+      // this wave's copy of the tile's scale bytes: lane l copies 4 bytes of token l/2
+      const int t = lane >> 1;
+      const uint8_t* src = a.kv + 4 * (lane & 1);
+      if (t0 + t < n_valid) src = a.kv + slot_addr<FMT>(sSlots[t0 + t], a.ps_log2).scales + 4 * (lane & 1);
+      dma4(src, sScl + (st * NW + wave) * 256);
+    }
+  };
+  // Wait for the oldest tile in flight; the NS - 1 younger ones may stay pending.
+  auto wait_oldest = [&]() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::NS > 1 ? (C::NS - 1) * C::PERW : 0)); };
+
+  // After this lane's copies of `tile` have landed: FP8 dequantizes the units it copied
+  // into the tile's K buffer, BF16 zeroes the units of tokens past the valid count.
+  auto kbuf_of = [&](int tile) { return C::NK > 1 ? tile % C::NK : 0; };
+  auto finish_tile = [&](int tile) {
+    int lane = lane_id;
+    asm volatile("" : "+v"(lane));
+    const int t0 = tile * kT;
+    uint16_t* K = sK + kbuf_of(tile) * kTile;
+    const int st = C::NS > 0 ? tile % (FMT == 1 ? C::NS : C::NK) : 0;
+    const uint8_t* raw = sRaw + (FMT == 1 ? st : 0) * (20 * 1024);
+    const uint8_t* scl = sScl + (st * NW + wave) * 256;
+    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int ins = wave + NW * j;
+      if (ins < C::NI) {
+        if (FMT == 1) {
+          const u32x4 rv = *reinterpret_cast<const u32x4*>(raw + ins * 1024 + 16 * lane);
+          if (ins < 16) {
+            const int t = 2 * ins + (lane >> 5);
+            const int c = lane & 31;
+            const bool ok = t0 + t < n_valid;
+            const float sc = ue8m0_scale(scl[8 * t + (c >> 2)]);
+            *reinterpret_cast<u32x4*>(K + lat_at(t, 16 * c)) = ok ? dequant8_fp8(u32x2{rv[0], rv[1]}, sc) : z;
+            *reinterpret_cast<u32x4*>(K + lat_at(t, 16 * c + 8)) = ok ? dequant8_fp8(u32x2{rv[2], rv[3]}, sc) : z;
+          } else {
+            const int t = 8 * (ins - 16) + (lane >> 3);
+            const bool ok = t0 + t < n_valid;
+            *reinterpret_cast<u32x4*>(K + rope_at(t, 8 * (lane & 7))) = ok ? rv : z;
+          }
+        } else {
+          if (ins < 32) {
+            if (t0 + ins >= n_valid) *reinterpret_cast<u32x4*>(K + lat_at(ins, 8 * lane)) = z;
+          } else {
+            const int t = 8 * (ins - 32) + (lane >> 3);
+            if (t0 + t >= n_valid)
+              *reinterpret_cast<u32x4*>(K + kRopeOff + (ins - 32) * 512 + 8 * lane) = z;
+          }
+        }
+      }
+    }
+  };
+
+  // Lane bases of the LDS operand addresses (element offsets); the rest is constant.
+  // QK k-step ks reads dims 16ks + 8G .. +7 of token row hl (latent for ks < 32, rope
+  // after).  PV: see the B-operand note in the loop.
+  const int qk_lat = lat_at(hl, 8 * G);
+  const int qk_rope = rope_at(hl, 8 * G);
+  int pv_base;
+  {
+    const int gam = lane >> 4;
+    const int jj = lane & 15;
+    const int tr_row = 4 * G + (jj >> 2);
+    const int tr_col = 16 * (gam & 1) + 4 * (jj & 3);
+    pv_base = lat_at(tr_row, tr_col);
+  }
+
+  f32x16 O[16];
+  float l_part;
+  const int ntiles = (n_valid + kT - 1) / kT;
+  // The pass over the tiles is repeated only if some head's reference max had to be
+  // raised (kRestartLog2); O is dead across the repeat.
+  for (;;) {
+#pragma unroll
+  for (int b = 0; b < 16; ++b) O[b] = f32x16{};
+  l_part = 0.f;
+  if (ntiles > 0) {
+    if (C::NS > 0) {
+#pragma unroll
+      for (int i = 0; i < C::NS; ++i) dma_tile(i);
+      wait_oldest();
+    } else {
+      dma_tile(0);
+      wait_vm();
+    }
+    finish_tile(0);
+  }
+  __syncthreads();
+
+  bool restart = false;
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int t0 = tile * kT;
     const int nt = min(kT, n_valid - t0);
+    const bool has_next = tile + 1 < ntiles;
+    if (C::NS > 0) dma_tile(tile + C::NS);
+    const uint16_t* K = sK + kbuf_of(tile) * kTile;
 
-    // ---- 2. gather + dequantize: latent items (token quad, 8-dim chunk) -------------
-    for (int it = tid; it < (kT / 4) * 64; it += NT) {
-      const int qd = it >> 6;
-      const int c = it & 63;
-      u32x4 v[4];
+    // ---- 3. QK: S^T[token][head]; lane holds head hl, tokens acc_row(r, G) -------------
+    // The A operand (K rows) is software pipelined kDepth loads ahead; scheduling fences
+    // keep the compiler from hoisting more loads than that into registers.
+    f32x16 s = f32x16{};
+    {
+      auto kload = [&](int ks) {
+        return *reinterpret_cast<const u32x4*>(K + (ks < 32 ? qk_lat + 16 * ks : qk_rope + 16 * (ks - 32)));
+      };
+      u32x4 kq[kDepth];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int tau = 4 * qd + k;
-        if (tau < nt) {
-          const SlotAddr sa = slot_addr<FMT>(sSlots[t0 + tau], a.ps_log2);
-          v[k] = load_latent8<FMT>(a.kv, sa, c);
-        } else {
-          v[k] = u32x4{0u, 0u, 0u, 0u};
-        }
-        *reinterpret_cast<u32x4*>(sK + tau * kKStr + 8 * c) = v[k];
-      }
-      // tile position of token tau = 16*sub + 4*gq + r is 8*gq + 4*sub + r, so the
-      // PV k-slice of lane group gq (tokens 4gq..4gq+3 and 16+4gq..16+4gq+3) is one chunk
-      const int phys = 8 * (qd & 3) + 4 * (qd >> 2);
+      for (int i = 0; i < kDepth; ++i) kq[i] = kload(i);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int w = i >> 1;
-        uint32_t x0, x1;
-        if (i & 1) {
-          x0 = (v[0][w] >> 16) | (v[1][w] & 0xffff0000u);
-          x1 = (v[2][w] >> 16) | (v[3][w] & 0xffff0000u);
-        } else {
-          x0 = (v[0][w] & 0xffffu) | (v[1][w] << 16);
-          x1 = (v[2][w] & 0xffffu) | (v[3][w] << 16);
-        }
-        *reinterpret_cast<u32x2*>(sVT + vt_off(8 * c + i, phys)) = u32x2{x0, x1};
+      for (int ks = 0; ks < 36; ++ks) {
+        const u32x4 kv = kq[ks % kDepth];
+        if (ks + kDepth < 36) kq[ks % kDepth] = kload(ks + kDepth);
+        s = mfma32x32x16(kv, qf[ks], s);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // rope items (token, 8-dim chunk)
-    for (int it = tid; it < kT * 8; it += NT) {
-      const int tau = it >> 3;
-      const int j = it & 7;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (tau < nt) {
-        const SlotAddr sa = slot_addr<FMT>(sSlots[t0 + tau], a.ps_log2);
-        v = load_rope8<FMT>(a.kv, sa, j);
-      }
-      *reinterpret_cast<u32x4*>(sK + tau * kKStr + kV + 8 * j) = v;
-    }
-    __syncthreads();
 
-    // ---- 3. QK: S^T[token][head], lane holds head hl, tokens 16*sub + 4g + r --------
-    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 s1 = f32x4{0.f, 0.f, 0.f, 0.f};
+    // PV B-operand: dv block b, k-step s2: lane l needs V[acc_row(8*s2 + kk, G)][32b + l%32]
+    // for kk = 0..7.  Two transpose reads give kk 0..3 and 4..7: in each 16-lane group
+    // (gamma = l/16, j = l%16) lane j addresses row 16*s2 + 8*hh + 4*G + j/4 at columns
+    // 32b + 16*(gamma%2) + 4*(j%4) .. +3.
+    auto vaddr = [&](int step, int hh) {
+      const int b = step >> 1, s2 = step & 1;
+      return K + pv_base + (16 * s2 + 8 * hh) * kLatS + 32 * b;
+    };
+    u32x2 vq[kDepth][2];
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      const u32x4 k0 = *reinterpret_cast<const u32x4*>(sK + hl * kKStr + 32 * ks + 8 * g);
-      const u32x4 k1 = *reinterpret_cast<const u32x4*>(sK + (16 + hl) * kKStr + 32 * ks + 8 * g);
-      s0 = mfma16x16x32(k0, qf[ks], s0);
-      s1 = mfma16x16x32(k1, qf[ks], s1);
+    for (int i = 0; i < kDepth; ++i) {
+      vq[i][0] = lds_read_tr16(vaddr(i, 0));
+      vq[i][1] = lds_read_tr16(vaddr(i, 1));
     }
 
-    // ---- 4. online softmax (exp2 domain) ---------------------------------------------
-    float t[8];
+    // ---- 4. softmax (exp2 domain) against a per-head reference max m_used ------------
+    float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      t[r] = (4 * g + r < nt) ? s0[r] * a.scale_log2 : -INFINITY;
-      t[4 + r] = (16 + 4 * g + r < nt) ? s1[r] * a.scale_log2 : -INFINITY;
+    for (int r = 0; r < 16; ++r) {
+      s[r] = (acc_row(r, G) < nt) ? s[r] * a.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, s[r]);
     }
-    float mx = t[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, t[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool need = mx > m_used + kRescaleLog2;
-    if (__ballot(need)) {
-      const float m_new = need ? mx : m_used;
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_used - m_new) : 1.0f;
-      m_used = m_new;
-      l_part *= alpha;
-      float ar[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * g + r);
-#pragma unroll
-      for (int b = 0; b < 32; ++b) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) O[b][r] *= ar[r];
-      }
+    if (m_used == -INFINITY) m_used = mx;       // first tile: O and l are still zero
+    if (mx > m_used + kRestartLog2) {           // rare: raise the reference and restart
+      m_used = mx;
+      sRestart = 1;
     }
-    float p[8];
     float ls = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = (t[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(t[i] - m_used);
-      ls += p[i];
+    for (int r = 0; r < 16; ++r) {
+      s[r] = (s[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[r] - m_used);
+      ls += s[r];
     }
     l_part += ls;
-    const u32x4 pa = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                           pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-
-    // ---- 5. PV: O[head][dv] += P[head][token] V[token][dv] --------------------------
+    // P as the PV A operand: k-step s2 uses the lane's tokens acc_row(8*s2 + kk, G)
+    u32x4 pa[2];
 #pragma unroll
-    for (int b = 0; b < 32; ++b) {
-      const u32x4 vb = *reinterpret_cast<const u32x4*>(sVT + vt_off(16 * b + hl, 8 * g));
-      O[b] = mfma16x16x32(pa, vb, O[b]);
+    for (int s2 = 0; s2 < 2; ++s2)
+      pa[s2] = u32x4{pack_bf16x2(s[8 * s2 + 0], s[8 * s2 + 1]), pack_bf16x2(s[8 * s2 + 2], s[8 * s2 + 3]),
+                     pack_bf16x2(s[8 * s2 + 4], s[8 * s2 + 5]), pack_bf16x2(s[8 * s2 + 6], s[8 * s2 + 7])};
+
+    // ---- 5. PV: O[head][dv] += P[head][token] V[token][dv] ---------------------------
+#pragma unroll
+    for (int step = 0; step < 32; ++step) {
+      const u32x2 v0 = vq[step % kDepth][0];
+      const u32x2 v1 = vq[step % kDepth][1];
+      if (step + kDepth < 32) {
+        vq[step % kDepth][0] = lds_read_tr16(vaddr(step + kDepth, 0));
+        vq[step % kDepth][1] = lds_read_tr16(vaddr(step + kDepth, 1));
+      }
+      O[step >> 1] = mfma32x32x16(pa[step & 1], u32x4{v0[0], v0[1], v1[0], v1[1]}, O[step >> 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- next tile: finish its gather -------------------------------------------------
+    if (has_next) {
+      if (C::NK > 1) {
+        wait_oldest();
+        finish_tile(tile + 1);
+      } else {
+        __syncthreads();                 // everyone is done reading the single K tile
+        if (C::NS == 0) {
+          dma_tile(tile + 1);
+          wait_vm();
+        } else {
+          wait_oldest();
+        }
+        finish_tile(tile + 1);
+      }
     }
     __syncthreads();
+    if (sRestart) {  // the same value in every thread: it was written before the barrier
+      restart = true;
+      break;
+    }
+  }
+  wait_vm();  // drain the copies issued past the last tile
+  if (!restart) break;
+  __syncthreads();  // every thread has seen the flag
+  if (tid == 0) sRestart = 0;
   }
 
   // ---- 6. epilogue ----------------------------------------------------------------------
-  float l_tot = l_part + __shfl_xor(l_part, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = l_part + __shfl_xor(l_part, 32);
   float factor, lse_v;
   if (a.write_partials) {
     if (l_tot > 0.f) {
@@ -237,7 +439,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       lse_v = -INFINITY;
     }
   } else {
-    const float sink = (a.sinks != nullptr) ? a.sinks[h] : -INFINITY;
+    const float sink = (a.sinks != nullptr && h_ok) ? a.sinks[h] : -INFINITY;
     const float sig2 = sink * kLog2e;
     const float M = fmaxf(m_used, sig2);
     if (m_used == -INFINITY) {
@@ -251,27 +453,39 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       lse_v = (M + __log2f(z)) * kLn2;
     }
   }
-  float fr[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) fr[r] = __shfl(factor, 4 * g + r);
 
+  // Accumulator register r of lane l holds head 32*wave + acc_row(r, G), dv 32b + hl.
+  float fr[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) fr[r] = __shfl(factor, acc_row(r, G));
+  const int hbase = 32 * wave + 4 * G;
   if (a.write_partials) {
     const size_t rs = (size_t)row * a.S + split;
-    float* po = a.part_o + (rs * a.H + 16 * wave) * kV;
+    float* po = a.part_o + (rs * a.H) * kV + hl;
 #pragma unroll
-    for (int b = 0; b < 32; ++b) {
+    for (int b = 0; b < 16; ++b) {
+      const f32x16 ob = O[b];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) po[(4 * g + r) * kV + 16 * b + hl] = O[b][r] * fr[r];
+      for (int r = 0; r < 16; ++r) {
+        const int hr = hbase + 8 * (r >> 2) + (r & 3);
+        if (hr < a.H) po[(size_t)hr * kV + 32 * b] = ob[r] * fr[r];
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (g == 0) a.part_lse[rs * a.H + h] = lse_v;
+    if (G == 0 && h_ok) a.part_lse[rs * a.H + h] = lse_v;
   } else {
-    __bf16* ob = reinterpret_cast<__bf16*>(a.out) + ((size_t)row * a.H + 16 * wave) * kV;
+    __bf16* ob_ptr = reinterpret_cast<__bf16*>(a.out) + ((size_t)row * a.H) * kV + hl;
 #pragma unroll
-    for (int b = 0; b < 32; ++b) {
+    for (int b = 0; b < 16; ++b) {
+      const f32x16 ob = O[b];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ob[(4 * g + r) * kV + 16 * b + hl] = (__bf16)(O[b][r] * fr[r]);
+      for (int r = 0; r < 16; ++r) {
+        const int hr = hbase + 8 * (r >> 2) + (r & 3);
+        if (hr < a.H) ob_ptr[(size_t)hr * kV + 32 * b] = (__bf16)(ob[r] * fr[r]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (a.lse != nullptr && g == 0) a.lse[(size_t)row * a.H + h] = lse_v;
+    if (a.lse != nullptr && G == 0 && h_ok) a.lse[(size_t)row * a.H + h] = lse_v;
   }
 }
 
@@ -309,10 +523,6 @@ hipError_t launch_fmt(const DecodeArgs& a, int nw, hipStream_t st) {
     case 2: return launch_nw<2, FMT>(a, st);
     case 3: return launch_nw<3, FMT>(a, st);
     case 4: return launch_nw<4, FMT>(a, st);
-    case 5: return launch_nw<5, FMT>(a, st);
-    case 6: return launch_nw<6, FMT>(a, st);
-    case 7: return launch_nw<7, FMT>(a, st);
-    case 8: return launch_nw<8, FMT>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -322,7 +532,7 @@ hipError_t launch_fmt(const DecodeArgs& a, int nw, hipStream_t st) {
 int max_chunk_positions() { return kCMax; }
 
 hipError_t launch_decode(const DecodeArgs& a, int kv_format, hipStream_t st) {
-  const int nw = a.H / 16;
+  const int nw = (a.H + 31) / 32;
   return kv_format == 1 ? launch_fmt<1>(a, nw, st) : launch_fmt<0>(a, nw, st);
 }
 

@@ -73,6 +73,7 @@ def _plan_status(lib, prob, cus=256):
     (dict(num_rows=-1), B.ERR_BAD_SHAPE),
     (dict(page_size=48), B.ERR_BAD_SHAPE),
     (dict(page_size=2048), B.ERR_BAD_SHAPE),
+    (dict(page_size=1), B.ERR_UNSUPPORTED),
     (dict(num_pages=0), B.ERR_BAD_SHAPE),
     (dict(num_pages=1 << 26, page_size=64), B.ERR_BAD_SHAPE),
     (dict(kv_format=7), B.ERR_UNSUPPORTED),

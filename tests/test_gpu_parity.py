@@ -248,9 +248,10 @@ def test_head_counts(heads):
     compare(out, lse, o, l, what=f"H={heads}")
 
 
-@pytest.mark.parametrize("ps", [1, 16, 256])
-def test_page_sizes(ps):
-    inp = _small(heads=16, topk=100, nreq=2, rows=(1,), ctx=(600, 1000), ps=ps, seed=50 + ps)
+@pytest.mark.parametrize("fmt,ps", [("bf16", 1), ("fp8", 2), ("fp8", 16), ("bf16", 256)])
+def test_page_sizes(fmt, ps):
+    inp = _small(fmt=fmt, heads=16, topk=100, nreq=2, rows=(1,), ctx=(600, 1000), ps=ps,
+                 seed=50 + ps)
     announce(f"page size {ps}")
     out, lse = gpu_decode(inp)
     o, l = oracle_decode(inp)
