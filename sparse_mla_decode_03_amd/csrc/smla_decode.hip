@@ -28,9 +28,9 @@ namespace smla {
 namespace {
 
 constexpr int kT = 32;                  // tokens per tile (MFMA M dimension)
-constexpr int kLatS = 520;              // bf16 per latent row of a K tile: 512 + 8 pad (1040 B)
-constexpr int kRopeOff = kT * kLatS;    // rope region: [32][64] bf16 after the latent rows
-constexpr int kTile = kRopeOff + kT * 64;  // bf16 per tile (37,376 bytes)
+constexpr int kLat = 512;               // bf16 per latent row of a K tile (1024 B, 64 chunks)
+constexpr int kRopeOff = kT * kLat;     // rope region: [32][64] bf16 after the latent rows
+constexpr int kTile = kRopeOff + kT * 64;  // bf16 per tile (36,864 bytes)
 constexpr int kCMax = 2048;             // positions per split handled by one workgroup
 constexpr int kDepth = 4;               // LDS operand loads kept in flight
 // Exponentials are taken against a per-head reference max fixed at the first tile, so P
@@ -39,26 +39,52 @@ constexpr int kDepth = 4;               // LDS operand loads kept in flight
 // P <= 2^32 without overflow.
 constexpr float kRestartLog2 = 32.0f;
 
-// K tile layout: latent rows padded to 1040 bytes, so 8 consecutive rows read at the same
-// column start 16 bytes apart in the 128-byte bank cycle (no conflicts for the MFMA
-// operand loads); rope rows of 128 bytes unpadded, so 8 of them form one contiguous
-// kilobyte for the DMA.  Every operand address is a lane base plus a constant.
-__device__ __forceinline__ int lat_at(int row, int col) { return row * kLatS + col; }
-__device__ __forceinline__ int rope_at(int row, int col) { return kRopeOff + row * 64 + col; }
+// K tile layout.  LDS serves 64 banks of 4 bytes: 16 lanes per cycle for 16-byte reads
+// and 32 lanes per cycle for 8-byte (and transpose) reads.  Latent rows are 1024 bytes of
+// 64 chunks of 16 bytes; within each 256-byte bank row the chunk index is XORed with
+// lat_swz(row) = (row%4)*4 + (row/4)%4, which keeps both operand patterns conflict free:
+//   QK A operand: 16 consecutive rows at one chunk -> 16 different chunk slots;
+//   PV transpose reads: 4 consecutive rows x 4 consecutive chunks -> 16 different slots.
+// Rope rows are 128 bytes (two per bank row) with the chunk XORed with (row/2)%8.
+// Offsets are in bf16 elements; `chunk` is the logical 16-byte chunk (dims 8c..8c+7).
+__device__ __forceinline__ int lat_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ int lat_at(int row, int chunk) { return row * kLat + ((chunk ^ lat_swz(row)) << 3); }
+__device__ __forceinline__ int rope_at(int row, int chunk) {
+  return kRopeOff + row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
+}
 
 // Token position (0..31) held in accumulator register r (0..15) of lane group G (lane/32)
 // by a 32x32 MFMA whose rows are tokens.
 __device__ __forceinline__ int acc_row(int r, int G) { return 8 * (r >> 2) + 4 * G + (r & 3); }
 
-// Copy 16 (or 4) bytes per lane from global memory into LDS at dst + lane*size.
-__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
+// Copy 16 (or 4) bytes per lane from global memory into LDS at dst + lane*size
+// (global_load_lds; dst is the same for the whole wave).  Written as inline asm so that
+// the compiler does not track these LDS writes: it would otherwise wait for every copy in
+// flight (vmcnt(0)) before any read of the staging area, exposing the full memory latency
+// once per tile.  The kernel orders the copies itself with explicit vmcnt waits (wait_vm,
+// wait_vm_le) before reading what they wrote.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)(p));
 }
-__device__ __forceinline__ void dma4(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_wave_base), 4, 0, 0);
+__device__ __forceinline__ void dma16(const void* src, const void* lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_offset(lds_wave_base)) : "memory");
 }
-// Wait until this wave's outstanding global loads (and LDS copies) have landed.
-__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void dma4(const void* src, const void* lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(lds_offset(lds_wave_base)) : "memory");
+}
+// Wait until at most N of this wave's global loads (LDS copies included) are pending.
+// The builtin lets the compiler's own wait insertion see the wait; the empty asm with a
+// memory clobber keeps LDS reads of the copied data below it.
+template <int N>
+__device__ __forceinline__ void wait_vm_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  // vmcnt is split over bits 3:0 and 15:14; expcnt and lgkmcnt stay at their maxima
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void wait_vm() { wait_vm_le<0>(); }
 
 // Per-configuration LDS and work split.  A tile is gathered by 64-lane DMA instructions
 // that each fill 1 KB of LDS.  FP8: instructions 0..15 copy the latent codes of tokens
@@ -77,17 +103,13 @@ struct Cfg {
   // into NK bf16 K tiles; BF16 copies into a ring of NS + 1 K tiles, or synchronously
   // (NS = 0) when the workgroup must stay small enough for two per CU.
   static constexpr bool BIG = NW >= 3;                  // one workgroup per CU
-  static constexpr int NS = FMT == 1 ? (BIG ? 3 : 1) : (BIG ? 2 : 0);
+  static constexpr int NS = FMT == 1 ? (BIG ? 2 : 1) : (BIG ? 2 : 0);
   static constexpr int NK = FMT == 1 ? (BIG ? 2 : 1) : (BIG ? NS + 1 : 1);
   static constexpr int RAW_BYTES = FMT == 1 ? NS * 20 * 1024 : 16;
   static constexpr int SCL_BYTES = FMT == 1 ? NS * NW * 256 : 16;
   // DMA instructions every wave issues per tile (scale copy included), rounded down
   static constexpr int PERW = NI / NW + (FMT == 1 ? 1 : 0);
 };
-
-// s_waitcnt immediate that waits until at most n vector-memory operations are pending
-// (vmcnt split over bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 
 template <int NW, int FMT>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
@@ -104,7 +126,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int lane_id = lane;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int row = blockIdx.x;
   const int split = blockIdx.y;
   const int p0 = split * a.chunk;
@@ -181,118 +203,151 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // ---- 2. gather (see Cfg for the DMA instruction map).  Every DMA instruction of a
   // tile is issued, also for tokens past the valid count (they read a dummy address in
   // the cache and are zeroed when the tile is finished), so that the number of pending
-  // copies per wave is fixed and vmcnt waits can target the oldest tile.
-  auto dma_tile = [&](int tile) {
+  // copies per wave is fixed and vmcnt waits can target the oldest tile.  A tile's copy
+  // is split in two steps: its slots are read from LDS into registers first (load_slots),
+  // and the copies are issued one phase later (issue_dma), so no LDS round trip sits in
+  // front of each copy.
+  constexpr int NDMA = PER + (FMT == 1 ? 1 : 0);   // slot registers per tile (scales last)
+  // token (within the tile) copied by this lane in DMA instruction `ins` (wave uniform)
+  auto ins_token = [&](int ins, int ln) {
+    if (FMT == 1) return ins < 16 ? 2 * ins + (ln >> 5) : 8 * (ins - 16) + (ln >> 3);
+    return ins < 32 ? ins : 8 * (ins - 32) + (ln >> 3);
+  };
+  auto load_slots = [&](int tile, int (&sl)[NDMA]) {
+    int ln = lane_id;
+    asm volatile("" : "+v"(ln));
+    const int t0 = tile * kT;
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) {
+      const int ins = wave + NW * j;
+      const int t = (FMT == 1 && j == PER) ? (ln >> 1) : ins_token(min(ins, C::NI - 1), ln);
+      // positions past the valid count read a stale (in-bounds) word; issue_dma drops it
+      sl[j] = sSlots[min(t0 + t, kCMax - 1)];
+    }
+  };
+  auto issue_dma = [&](int tile, const int (&sl)[NDMA]) {
     // The lane id passes through an empty asm statement so that the per-lane address
     // terms below are recomputed here instead of being hoisted out of the tile loop
     // (which costs registers, then spills whose reloads would wait on the copies).
-    int lane = lane_id;
-    asm volatile("" : "+v"(lane));
+    int ln = lane_id;
+    asm volatile("" : "+v"(ln));
     const int t0 = tile * kT;
     const int st = C::NS > 0 ? tile % (FMT == 1 ? C::NS : C::NK) : 0;
     uint16_t* K = sK + (FMT == 1 ? 0 : st) * kTile;
     uint8_t* raw = sRaw + (FMT == 1 ? st : 0) * (20 * 1024);
+    const uint32_t psl = (uint32_t)a.ps_log2;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int ins = wave + NW * j;
       if (ins < C::NI) {
-        int t, src_off;
+        const int t = ins_token(ins, ln);
+        const uint32_t slot = (uint32_t)sl[j];
+        size_t off;
         uint8_t* dst;
         if (FMT == 1) {
-          if (ins < 16) {
-            t = 2 * ins + (lane >> 5);
-            src_off = 16 * (lane & 31);
-          } else {
-            t = 8 * (ins - 16) + (lane >> 3);
-            src_off = -1 - 16 * (lane & 7);          // rope chunk, marked negative
-          }
+          const size_t base = (size_t)(slot >> psl) * ((size_t)kFp8Entry << psl);
+          const uint32_t r = slot & ((1u << psl) - 1u);
+          off = ins < 16 ? base + r * 512u + 16u * (ln & 31)
+                         : base + ((size_t)512 << psl) + r * 128u + 16u * (ln & 7);
           dst = raw + ins * 1024;
         } else {
-          if (ins < 32) {
-            t = ins;
-            src_off = 16 * lane;
-            dst = reinterpret_cast<uint8_t*>(K + lat_at(t, 0));
-          } else {
-            t = 8 * (ins - 32) + (lane >> 3);
-            src_off = 1024 + 16 * (lane & 7);
-            dst = reinterpret_cast<uint8_t*>(K + kRopeOff) + (ins - 32) * 1024;
-          }
+          const size_t base = (size_t)slot * kBf16Entry;
+          // lane = physical chunk of the destination row; it copies logical chunk lane ^ swz
+          off = ins < 32 ? base + 16u * (ln ^ lat_swz(t)) : base + 1024u + 16u * ((ln & 7) ^ ((t >> 1) & 7));
+          dst = ins < 32 ? reinterpret_cast<uint8_t*>(K + t * kLat)
+                         : reinterpret_cast<uint8_t*>(K + kRopeOff) + (ins - 32) * 1024;
         }
-        const uint8_t* src = a.kv + 16 * lane;       // dummy for tokens past the end
-        if (t0 + t < n_valid) {
-          const SlotAddr sa = slot_addr<FMT>(sSlots[t0 + t], a.ps_log2);
-          src = (FMT == 1 && src_off < 0) ? a.kv + sa.rope + (-1 - src_off) : a.kv + sa.latent + src_off;
-        }
-        dma16(src, dst);
+        dma16(a.kv + (t0 + t < n_valid ? off : (size_t)(16 * ln)), dst);
       }
     }
     if (FMT == 1) {
       // this wave's copy of the tile's scale bytes: lane l copies 4 bytes of token l/2
-      const int t = lane >> 1;
-      const uint8_t* src = a.kv + 4 * (lane & 1);
-      if (t0 + t < n_valid) src = a.kv + slot_addr<FMT>(sSlots[t0 + t], a.ps_log2).scales + 4 * (lane & 1);
-      dma4(src, sScl + (st * NW + wave) * 256);
+      const int t = ln >> 1;
+      const uint32_t slot = (uint32_t)sl[PER];
+      const size_t off = (size_t)(slot >> psl) * ((size_t)kFp8Entry << psl) + ((size_t)640 << psl) +
+                         (slot & ((1u << psl) - 1u)) * 8u + 4u * (ln & 1);
+      dma4(a.kv + (t0 + t < n_valid ? off : (size_t)(4 * (ln & 1))), sScl + (st * NW + wave) * 256);
     }
   };
   // Wait for the oldest tile in flight; the NS - 1 younger ones may stay pending.
-  auto wait_oldest = [&]() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::NS > 1 ? (C::NS - 1) * C::PERW : 0)); };
+  auto wait_oldest = [&]() { wait_vm_le<(C::NS > 1 ? (C::NS - 1) * C::PERW : 0)>(); };
 
   // After this lane's copies of `tile` have landed: FP8 dequantizes the units it copied
-  // into the tile's K buffer, BF16 zeroes the units of tokens past the valid count.
+  // into the tile's K buffer, BF16 zeroes the units of tokens past the valid count.  All
+  // LDS reads of a tile are issued before the first conversion.
   auto kbuf_of = [&](int tile) { return C::NK > 1 ? tile % C::NK : 0; };
   auto finish_tile = [&](int tile) {
-    int lane = lane_id;
-    asm volatile("" : "+v"(lane));
+    int ln = lane_id;
+    asm volatile("" : "+v"(ln));
     const int t0 = tile * kT;
     uint16_t* K = sK + kbuf_of(tile) * kTile;
     const int st = C::NS > 0 ? tile % (FMT == 1 ? C::NS : C::NK) : 0;
-    const uint8_t* raw = sRaw + (FMT == 1 ? st : 0) * (20 * 1024);
-    const uint8_t* scl = sScl + (st * NW + wave) * 256;
     const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+    if (FMT == 1) {
+      const uint8_t* raw = sRaw + st * (20 * 1024);
+      const uint8_t* scl = sScl + (st * NW + wave) * 256;
+      u32x4 rv[PER];
+      uint32_t e[PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int ins = wave + NW * j;
-      if (ins < C::NI) {
-        if (FMT == 1) {
-          const u32x4 rv = *reinterpret_cast<const u32x4*>(raw + ins * 1024 + 16 * lane);
+      for (int j = 0; j < PER; ++j) {
+        const int ins = wave + NW * j;
+        if (ins < C::NI) {
+          rv[j] = *reinterpret_cast<const u32x4*>(raw + ins * 1024 + 16 * ln);
+          e[j] = scl[8 * ins_token(min(ins, 15), ln) + ((ln & 31) >> 2)];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int ins = wave + NW * j;
+        if (ins < C::NI) {
+          const int t = ins_token(ins, ln);
+          const bool ok = t0 + t < n_valid;
           if (ins < 16) {
-            const int t = 2 * ins + (lane >> 5);
-            const int c = lane & 31;
-            const bool ok = t0 + t < n_valid;
-            const float sc = ue8m0_scale(scl[8 * t + (c >> 2)]);
-            *reinterpret_cast<u32x4*>(K + lat_at(t, 16 * c)) = ok ? dequant8_fp8(u32x2{rv[0], rv[1]}, sc) : z;
-            *reinterpret_cast<u32x4*>(K + lat_at(t, 16 * c + 8)) = ok ? dequant8_fp8(u32x2{rv[2], rv[3]}, sc) : z;
+            const int c = ln & 31;
+            const float sc = ue8m0_scale(e[j]);
+            *reinterpret_cast<u32x4*>(K + lat_at(t, 2 * c)) = ok ? dequant8_fp8(u32x2{rv[j][0], rv[j][1]}, sc) : z;
+            *reinterpret_cast<u32x4*>(K + lat_at(t, 2 * c + 1)) = ok ? dequant8_fp8(u32x2{rv[j][2], rv[j][3]}, sc) : z;
           } else {
-            const int t = 8 * (ins - 16) + (lane >> 3);
-            const bool ok = t0 + t < n_valid;
-            *reinterpret_cast<u32x4*>(K + rope_at(t, 8 * (lane & 7))) = ok ? rv : z;
+            *reinterpret_cast<u32x4*>(K + rope_at(t, ln & 7)) = ok ? rv[j] : z;
           }
-        } else {
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int ins = wave + NW * j;
+        if (ins < C::NI) {
           if (ins < 32) {
-            if (t0 + ins >= n_valid) *reinterpret_cast<u32x4*>(K + lat_at(ins, 8 * lane)) = z;
+            if (t0 + ins >= n_valid) *reinterpret_cast<u32x4*>(K + ins * kLat + 8 * ln) = z;
           } else {
-            const int t = 8 * (ins - 32) + (lane >> 3);
+            const int t = 8 * (ins - 32) + (ln >> 3);
             if (t0 + t >= n_valid)
-              *reinterpret_cast<u32x4*>(K + kRopeOff + (ins - 32) * 512 + 8 * lane) = z;
+              *reinterpret_cast<u32x4*>(K + kRopeOff + (ins - 32) * 512 + 8 * ln) = z;
           }
         }
       }
     }
   };
 
-  // Lane bases of the LDS operand addresses (element offsets); the rest is constant.
-  // QK k-step ks reads dims 16ks + 8G .. +7 of token row hl (latent for ks < 32, rope
-  // after).  PV: see the B-operand note in the loop.
-  const int qk_lat = lat_at(hl, 8 * G);
-  const int qk_rope = rope_at(hl, 8 * G);
-  int pv_base;
-  {
-    const int gam = lane >> 4;
-    const int jj = lane & 15;
-    const int tr_row = 4 * G + (jj >> 2);
-    const int tr_col = 16 * (gam & 1) + 4 * (jj & 3);
-    pv_base = lat_at(tr_row, tr_col);
-  }
+  // Lane parts of the LDS operand addresses (bf16 elements).  The swizzle only touches
+  // address bits 3..6, so each operand address is (lane base XOR constant) + constant.
+  //   QK step ks < 32: logical chunk 2ks + G of row hl -> (qk_base ^ 16(ks%8)) + 128(ks/8);
+  //   QK rope step 32 + i: (rope_base ^ 16i);
+  //   PV (see the B-operand note in the loop): (pv_base ^ 8(4(b%4) + 2hh)) + 8192 s2 +
+  //   4096 hh + 128 (b/4).
+  auto qk_base_of = [&](int ln) {
+    const int hl_ = ln & 31, G_ = ln >> 5;
+    return hl_ * kLat + ((G_ ^ lat_swz(hl_)) << 3);
+  };
+  auto rope_base_of = [&](int ln) {
+    const int hl_ = ln & 31, G_ = ln >> 5;
+    return kRopeOff + hl_ * 64 + ((G_ ^ ((hl_ >> 1) & 7)) << 3);
+  };
+  auto pv_base_of = [&](int ln) {
+    const int pj = ln & 15, G_ = ln >> 5, jq = pj >> 2;
+    const int cl = 2 * ((ln >> 4) & 1) + ((pj & 3) >> 1);
+    return (4 * G_ + jq) * kLat + ((4 * jq + (cl ^ G_)) << 3) + 4 * (pj & 1);
+  };
 
   f32x16 O[16];
   float l_part;
@@ -306,10 +361,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   if (ntiles > 0) {
     if (C::NS > 0) {
 #pragma unroll
-      for (int i = 0; i < C::NS; ++i) dma_tile(i);
+      for (int i = 0; i < C::NS; ++i) {
+        int sl[NDMA];
+        load_slots(i, sl);
+        issue_dma(i, sl);
+      }
       wait_oldest();
     } else {
-      dma_tile(0);
+      int sl[NDMA];
+      load_slots(0, sl);
+      issue_dma(0, sl);
       wait_vm();
     }
     finish_tile(0);
@@ -321,7 +382,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     const int t0 = tile * kT;
     const int nt = min(kT, n_valid - t0);
     const bool has_next = tile + 1 < ntiles;
-    if (C::NS > 0) dma_tile(tile + C::NS);
+    // slots of the tile copied during this one (issued after QK, landed by then)
+    int sl[NDMA];
+    if (C::NS > 0) load_slots(tile + C::NS, sl);
     const uint16_t* K = sK + kbuf_of(tile) * kTile;
 
     // ---- 3. QK: S^T[token][head]; lane holds head hl, tokens acc_row(r, G) -------------
@@ -329,8 +392,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     // keep the compiler from hoisting more loads than that into registers.
     f32x16 s = f32x16{};
     {
+      int ln = lane_id;
+      asm volatile("" : "+v"(ln));
+      const int qk_base = qk_base_of(ln);
+      const int rope_base = rope_base_of(ln);
       auto kload = [&](int ks) {
-        return *reinterpret_cast<const u32x4*>(K + (ks < 32 ? qk_lat + 16 * ks : qk_rope + 16 * (ks - 32)));
+        const int off = ks < 32 ? (qk_base ^ (16 * (ks & 7))) + 128 * (ks >> 3) : rope_base ^ (16 * (ks - 32));
+        return *reinterpret_cast<const u32x4*>(K + off);
       };
       u32x4 kq[kDepth];
 #pragma unroll
@@ -343,14 +411,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    if (C::NS > 0) issue_dma(tile + C::NS, sl);
 
     // PV B-operand: dv block b, k-step s2: lane l needs V[acc_row(8*s2 + kk, G)][32b + l%32]
     // for kk = 0..7.  Two transpose reads give kk 0..3 and 4..7: in each 16-lane group
     // (gamma = l/16, j = l%16) lane j addresses row 16*s2 + 8*hh + 4*G + j/4 at columns
-    // 32b + 16*(gamma%2) + 4*(j%4) .. +3.
+    // 32b + 16*(gamma%2) + 4*(j%4) .. +3, i.e. logical chunk 4b + 2*(gamma%2) + (j%4)/2.
+    int pln = lane_id;
+    asm volatile("" : "+v"(pln));
+    const int pv_base = pv_base_of(pln);
     auto vaddr = [&](int step, int hh) {
       const int b = step >> 1, s2 = step & 1;
-      return K + pv_base + (16 * s2 + 8 * hh) * kLatS + 32 * b;
+      return K + ((pv_base ^ (8 * (4 * (b & 3) + 2 * hh))) + 8192 * s2 + 4096 * hh + 128 * (b >> 2));
     };
     u32x2 vq[kDepth][2];
 #pragma unroll
@@ -407,7 +479,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       } else {
         __syncthreads();                 // everyone is done reading the single K tile
         if (C::NS == 0) {
-          dma_tile(tile + 1);
+          int sl1[NDMA];
+          load_slots(tile + 1, sl1);
+          issue_dma(tile + 1, sl1);
           wait_vm();
         } else {
           wait_oldest();
