@@ -87,18 +87,22 @@ __device__ __forceinline__ void wait_vm_le() {
 __device__ __forceinline__ void wait_vm() { wait_vm_le<0>(); }
 
 // Per-configuration LDS and work split.  A tile is gathered by 64-lane DMA instructions
-// that each fill 1 KB of LDS.  FP8: instructions 0..15 copy the latent codes of tokens
-// 2i, 2i+1 (32 units of 16 bytes each) and 16..19 the rope of tokens 8(i-16)..+7 into a
-// raw staging area laid out latent[32][512 B] | rope[32][128 B]; each wave also copies
-// the tile's 32 x 8 scale bytes for itself.  BF16: instructions 0..31 copy the latent row
-// of token i and 32..35 the rope of tokens 8(i-32)..+7 straight into the K tile.  Wave w
-// issues instructions w, w+NW, w+2NW, ...  With three or more waves (one workgroup per
-// CU) the K tile is double-buffered; with fewer, a single tile keeps the workgroup small
-// enough for two per CU.
+// that each fill 1 KB of LDS, of two kinds:
+//   latent: FP8 instruction i (0..15) copies the 512 latent codes of tokens 2i, 2i+1 into
+//           a raw staging area; BF16 instruction i (0..31) copies token i's 1024-byte
+//           latent row straight into the K tile;
+//   rope:   instruction r (0..3) copies the 128-byte rope rows of tokens 8r..8r+7.
+// Wave w issues latent instructions w, w+NW, ... and rope instructions w, w+NW, ..., so
+// the kind of every part is known at compile time.  FP8 tiles also need their 32 x 8
+// scale bytes: one wave (the scale wave, NW-1) copies them into a shared ring, one tile
+// ahead of the codes, and the other waves read them after the end-of-tile barrier.
+// With three or more waves (one workgroup per CU) the K tile is double-buffered; with
+// fewer, a single tile keeps the workgroup small enough for two per CU.
 template <int NW, int FMT>
 struct Cfg {
-  static constexpr int NI = FMT == 1 ? 20 : 36;         // DMA instructions per tile
-  static constexpr int PER = (NI + NW - 1) / NW;        // per wave (the last ones may idle)
+  static constexpr int NL = FMT == 1 ? 16 : 32;         // latent instructions per tile
+  static constexpr int LP = (NL + NW - 1) / NW;         // latent parts per wave
+  static constexpr int RP = (4 + NW - 1) / NW;          // rope parts per wave
   // Tiles in flight and K tile buffers.  FP8 stages raw bytes (NS stages) and dequantizes
   // into NK bf16 K tiles; BF16 copies into a ring of NS + 1 K tiles, or synchronously
   // (NS = 0) when the workgroup must stay small enough for two per CU.
@@ -106,21 +110,20 @@ struct Cfg {
   static constexpr int NS = FMT == 1 ? (BIG ? 2 : 1) : (BIG ? 2 : 0);
   static constexpr int NK = FMT == 1 ? (BIG ? 2 : 1) : (BIG ? NS + 1 : 1);
   static constexpr int RAW_BYTES = FMT == 1 ? NS * 20 * 1024 : 16;
-  static constexpr int SCL_BYTES = FMT == 1 ? NS * NW * 256 : 16;
-  // DMA instructions every wave issues per tile (scale copy included), rounded down
-  static constexpr int PERW = NI / NW + (FMT == 1 ? 1 : 0);
+  static constexpr int SCL_BYTES = FMT == 1 ? (NS + 1) * 256 : 16;
+  // copies every wave issues per tile at least (the scale wave one more)
+  static constexpr int NMIN = NL / NW + 4 / NW;
 };
 
 template <int NW, int FMT>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   using C = Cfg<NW, FMT>;
   constexpr int NT = NW * 64;
-  constexpr int PER = C::PER;
   __shared__ __attribute__((aligned(16))) uint16_t sK[C::NK * kTile];
   __shared__ __attribute__((aligned(16))) uint8_t sRaw[C::RAW_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sScl[C::SCL_BYTES];
   __shared__ int sSlots[kCMax];
-  __shared__ int sWcnt[NW];
+  __shared__ int sWcnt[8 * NW];
   __shared__ int sRestart;
 
   const int tid = threadIdx.x;
@@ -135,50 +138,73 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   if (tid == 0) sRestart = 0;
 
   // ---- 1. translate and compact the split's indices --------------------------------
+  // Positions are taken in batches of kCB per thread; all index loads of a batch, then all
+  // its page-table loads, are in flight together.
   int req = 0;
   bool req_ok = true;
   if (a.index_mode == 0) {
     req = a.row_req[row];
     req_ok = req >= 0 && req < a.B;
   }
+  constexpr int kCB = 8;
   int n_valid = 0;
-  for (int base = p0; base < p1; base += NT) {
-    const int p = base + tid;
-    bool ok = false;
-    int slot = 0;
-    if (p < p1) {
-      const int t = a.indices[(size_t)row * a.K + p];
-      if (t != -1) {
-        if (a.index_mode == 0) {
-          if (req_ok && t >= 0 && (t >> a.ps_log2) < a.max_pages) {
-            const int pg = a.page_table[(size_t)req * a.max_pages + (t >> a.ps_log2)];
-            if (pg >= 0 && pg < a.num_pages) {
-              slot = (pg << a.ps_log2) | (t & ps_mask);
-              ok = true;
-            }
-          }
-        } else if (t >= 0 && t < a.num_slots) {
-          slot = t;
-          ok = true;
-        }
-        if (!ok && a.err != nullptr)
-          atomicMin(a.err, ((unsigned long long)(unsigned)row << 32) | (unsigned)p);
+  for (int base = p0; base < p1; base += kCB * NT) {
+    int tv[kCB];
+#pragma unroll
+    for (int i = 0; i < kCB; ++i) {
+      const int p = base + i * NT + tid;
+      tv[i] = p < p1 ? a.indices[(size_t)row * a.K + p] : -1;
+    }
+    int slot[kCB];
+    bool ok[kCB];
+#pragma unroll
+    for (int i = 0; i < kCB; ++i) {
+      const int t = tv[i];
+      ok[i] = false;
+      slot[i] = 0;
+      if (a.index_mode == 0) {
+        if (req_ok && t >= 0 && (t >> a.ps_log2) < a.max_pages)
+          slot[i] = a.page_table[(size_t)req * a.max_pages + (t >> a.ps_log2)];   // page for now
+        ok[i] = req_ok && t >= 0 && (t >> a.ps_log2) < a.max_pages;
+      } else {
+        ok[i] = t >= 0 && t < a.num_slots;
+        slot[i] = t;
       }
     }
-    const unsigned long long m = __ballot(ok);
-    const int before = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
-                                                 __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
-    if (lane == 0) sWcnt[wave] = __popcll(m);
-    __syncthreads();
-    int off = n_valid, tot = 0;
+    unsigned long long m[kCB];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const int c = sWcnt[w];
-      off += (w < wave) ? c : 0;
-      tot += c;
+    for (int i = 0; i < kCB; ++i) {
+      const int t = tv[i];
+      if (a.index_mode == 0 && ok[i]) {
+        const int pg = slot[i];
+        ok[i] = pg >= 0 && pg < a.num_pages;
+        slot[i] = (pg << a.ps_log2) | (t & ps_mask);
+      }
+      if (t != -1 && !ok[i] && a.err != nullptr) {
+        const int p = base + i * NT + tid;
+        atomicMin(a.err, ((unsigned long long)(unsigned)row << 32) | (unsigned)p);
+      }
+      m[i] = __ballot(ok[i]);
+      if (lane == 0) sWcnt[i * NW + wave] = __popcll(m[i]);
     }
-    if (ok) sSlots[off + before] = slot;
-    n_valid += tot;
+    __syncthreads();
+    // slots keep position order: batch i, then wave, then lane
+    int off = n_valid;
+#pragma unroll
+    for (int i = 0; i < kCB; ++i) {
+      int before_w = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int c = sWcnt[i * NW + w];
+        before_w += (w < wave) ? c : 0;
+        tot += c;
+      }
+      const int before = __builtin_amdgcn_mbcnt_hi((unsigned)(m[i] >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((unsigned)m[i], 0u));
+      if (ok[i]) sSlots[off + before_w + before] = slot[i];
+      off += tot;
+    }
+    n_valid = off;
     __syncthreads();
   }
 
@@ -207,24 +233,26 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // is split in two steps: its slots are read from LDS into registers first (load_slots),
   // and the copies are issued one phase later (issue_dma), so no LDS round trip sits in
   // front of each copy.
-  constexpr int NDMA = PER + (FMT == 1 ? 1 : 0);   // slot registers per tile (scales last)
-  // token (within the tile) copied by this lane in DMA instruction `ins` (wave uniform)
-  auto ins_token = [&](int ins, int ln) {
-    if (FMT == 1) return ins < 16 ? 2 * ins + (ln >> 5) : 8 * (ins - 16) + (ln >> 3);
-    return ins < 32 ? ins : 8 * (ins - 32) + (ln >> 3);
-  };
+  constexpr int LP = C::LP, RP = C::RP;
+  constexpr int NDMA = LP + RP + (FMT == 1 ? 1 : 0);   // slot registers (scales last)
+  const bool scale_wave = FMT == 1 && wave == NW - 1;
+  auto lat_token = [&](int ins, int ln) { return FMT == 1 ? 2 * ins + (ln >> 5) : ins; };
+  auto rope_token = [&](int ins, int ln) { return 8 * ins + (ln >> 3); };
   auto load_slots = [&](int tile, int (&sl)[NDMA]) {
     int ln = lane_id;
     asm volatile("" : "+v"(ln));
     const int t0 = tile * kT;
+    // positions past the valid count read a stale (in-bounds) word; issue_dma drops it
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j) {
-      const int ins = wave + NW * j;
-      const int t = (FMT == 1 && j == PER) ? (ln >> 1) : ins_token(min(ins, C::NI - 1), ln);
-      // positions past the valid count read a stale (in-bounds) word; issue_dma drops it
-      sl[j] = sSlots[min(t0 + t, kCMax - 1)];
-    }
+    for (int j = 0; j < LP; ++j) sl[j] = sSlots[min(t0 + lat_token(min(wave + NW * j, C::NL - 1), ln), kCMax - 1)];
+#pragma unroll
+    for (int j = 0; j < RP; ++j) sl[LP + j] = sSlots[min(t0 + rope_token(min(wave + NW * j, 3), ln), kCMax - 1)];
+    // the scale wave copies the scales of the following tile
+    if (FMT == 1) sl[LP + RP] = sSlots[min(t0 + kT + (ln >> 1), kCMax - 1)];
   };
+  // FP8 byte offset of a slot's page and row: the page base, and the row within it
+  auto fp8_page = [&](uint32_t slot) { return (size_t)(slot >> a.ps_log2) * ((size_t)kFp8Entry << a.ps_log2); };
+  auto fp8_row = [&](uint32_t slot) { return slot & ((1u << a.ps_log2) - 1u); };
   auto issue_dma = [&](int tile, const int (&sl)[NDMA]) {
     // The lane id passes through an empty asm statement so that the per-lane address
     // terms below are recomputed here instead of being hoisted out of the tile loop
@@ -235,46 +263,75 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     const int st = C::NS > 0 ? tile % (FMT == 1 ? C::NS : C::NK) : 0;
     uint16_t* K = sK + (FMT == 1 ? 0 : st) * kTile;
     uint8_t* raw = sRaw + (FMT == 1 ? st : 0) * (20 * 1024);
-    const uint32_t psl = (uint32_t)a.ps_log2;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
+    for (int j = 0; j < LP; ++j) {
       const int ins = wave + NW * j;
-      if (ins < C::NI) {
-        const int t = ins_token(ins, ln);
+      if (ins < C::NL) {
+        const int t = lat_token(ins, ln);
         const uint32_t slot = (uint32_t)sl[j];
         size_t off;
         uint8_t* dst;
         if (FMT == 1) {
-          const size_t base = (size_t)(slot >> psl) * ((size_t)kFp8Entry << psl);
-          const uint32_t r = slot & ((1u << psl) - 1u);
-          off = ins < 16 ? base + r * 512u + 16u * (ln & 31)
-                         : base + ((size_t)512 << psl) + r * 128u + 16u * (ln & 7);
+          off = fp8_page(slot) + fp8_row(slot) * 512u + 16u * (ln & 31);
           dst = raw + ins * 1024;
         } else {
-          const size_t base = (size_t)slot * kBf16Entry;
           // lane = physical chunk of the destination row; it copies logical chunk lane ^ swz
-          off = ins < 32 ? base + 16u * (ln ^ lat_swz(t)) : base + 1024u + 16u * ((ln & 7) ^ ((t >> 1) & 7));
-          dst = ins < 32 ? reinterpret_cast<uint8_t*>(K + t * kLat)
-                         : reinterpret_cast<uint8_t*>(K + kRopeOff) + (ins - 32) * 1024;
+          off = (size_t)slot * kBf16Entry + 16u * (ln ^ lat_swz(t));
+          dst = reinterpret_cast<uint8_t*>(K + t * kLat);
         }
         dma16(a.kv + (t0 + t < n_valid ? off : (size_t)(16 * ln)), dst);
       }
     }
-    if (FMT == 1) {
-      // this wave's copy of the tile's scale bytes: lane l copies 4 bytes of token l/2
+#pragma unroll
+    for (int j = 0; j < RP; ++j) {
+      const int ins = wave + NW * j;
+      if (ins < 4) {
+        const int t = rope_token(ins, ln);
+        const uint32_t slot = (uint32_t)sl[LP + j];
+        size_t off;
+        uint8_t* dst;
+        if (FMT == 1) {
+          off = fp8_page(slot) + ((size_t)512 << a.ps_log2) + fp8_row(slot) * 128u + 16u * (ln & 7);
+          dst = raw + (16 + ins) * 1024;
+        } else {
+          off = (size_t)slot * kBf16Entry + 1024u + 16u * ((ln & 7) ^ ((t >> 1) & 7));
+          dst = reinterpret_cast<uint8_t*>(K + kRopeOff) + ins * 1024;
+        }
+        dma16(a.kv + (t0 + t < n_valid ? off : (size_t)(16 * ln)), dst);
+      }
+    }
+    if (scale_wave) {
+      // scales of tile + 1: lane l copies 4 bytes of token l/2
       const int t = ln >> 1;
-      const uint32_t slot = (uint32_t)sl[PER];
-      const size_t off = (size_t)(slot >> psl) * ((size_t)kFp8Entry << psl) + ((size_t)640 << psl) +
-                         (slot & ((1u << psl) - 1u)) * 8u + 4u * (ln & 1);
-      dma4(a.kv + (t0 + t < n_valid ? off : (size_t)(4 * (ln & 1))), sScl + (st * NW + wave) * 256);
+      const uint32_t slot = (uint32_t)sl[LP + RP];
+      const size_t off = fp8_page(slot) + ((size_t)640 << a.ps_log2) + fp8_row(slot) * 8u + 4u * (ln & 1);
+      dma4(a.kv + (t0 + kT + t < n_valid ? off : (size_t)(4 * (ln & 1))), sScl + ((tile + 1) % (C::NS + 1)) * 256);
     }
   };
+  // The scales of tile 0 (FP8), copied by the scale wave before anything else.
+  auto issue_first_scales = [&]() {
+    if (!scale_wave) return;
+    int ln = lane_id;
+    asm volatile("" : "+v"(ln));
+    const int t = ln >> 1;
+    const uint32_t slot = (uint32_t)sSlots[t];
+    const size_t off = fp8_page(slot) + ((size_t)640 << a.ps_log2) + fp8_row(slot) * 8u + 4u * (ln & 1);
+    dma4(a.kv + (t < n_valid ? off : (size_t)(4 * (ln & 1))), sScl);
+  };
   // Wait for the oldest tile in flight; the NS - 1 younger ones may stay pending.
-  auto wait_oldest = [&]() { wait_vm_le<(C::NS > 1 ? (C::NS - 1) * C::PERW : 0)>(); };
+  auto wait_oldest = [&]() {
+    if (C::NS <= 1) {
+      wait_vm();
+    } else if (scale_wave) {
+      wait_vm_le<(C::NS > 1 ? (C::NS - 1) * (C::NMIN + 1) : 0)>();
+    } else {
+      wait_vm_le<(C::NS > 1 ? (C::NS - 1) * C::NMIN : 0)>();
+    }
+  };
 
   // After this lane's copies of `tile` have landed: FP8 dequantizes the units it copied
-  // into the tile's K buffer, BF16 zeroes the units of tokens past the valid count.  All
-  // LDS reads of a tile are issued before the first conversion.
+  // into the tile's K buffer (rows past the valid count become zero), BF16 zeroes the
+  // units of tokens past the valid count.  All LDS reads come before the first write.
   auto kbuf_of = [&](int tile) { return C::NK > 1 ? tile % C::NK : 0; };
   auto finish_tile = [&](int tile) {
     int ln = lane_id;
@@ -285,46 +342,45 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     const u32x4 z = u32x4{0u, 0u, 0u, 0u};
     if (FMT == 1) {
       const uint8_t* raw = sRaw + st * (20 * 1024);
-      const uint8_t* scl = sScl + (st * NW + wave) * 256;
-      u32x4 rv[PER];
-      uint32_t e[PER];
+      const uint8_t* scl = sScl + (tile % (C::NS + 1)) * 256;
+      const int c = ln & 31;
+      u32x4 rv[LP + RP];
+      uint32_t e[LP];
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
+      for (int j = 0; j < LP; ++j) {
+        const int ins = min(wave + NW * j, C::NL - 1);
+        rv[j] = *reinterpret_cast<const u32x4*>(raw + ins * 1024 + 16 * ln);
+        e[j] = scl[8 * lat_token(ins, ln) + (c >> 2)];
+      }
+#pragma unroll
+      for (int j = 0; j < RP; ++j)
+        rv[LP + j] = *reinterpret_cast<const u32x4*>(raw + (16 + min(wave + NW * j, 3)) * 1024 + 16 * ln);
+#pragma unroll
+      for (int j = 0; j < LP; ++j) {
         const int ins = wave + NW * j;
-        if (ins < C::NI) {
-          rv[j] = *reinterpret_cast<const u32x4*>(raw + ins * 1024 + 16 * ln);
-          e[j] = scl[8 * ins_token(min(ins, 15), ln) + ((ln & 31) >> 2)];
+        if (ins < C::NL) {
+          const int t = lat_token(ins, ln);
+          const uint32_t m = t0 + t < n_valid ? 0xffffffffu : 0u;   // rows past the end: zero
+          const float sc = ue8m0_scale(e[j] & m);
+          *reinterpret_cast<u32x4*>(K + lat_at(t, 2 * c)) = dequant8_fp8(u32x2{rv[j][0] & m, rv[j][1] & m}, sc);
+          *reinterpret_cast<u32x4*>(K + lat_at(t, 2 * c + 1)) = dequant8_fp8(u32x2{rv[j][2] & m, rv[j][3] & m}, sc);
         }
       }
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
+      for (int j = 0; j < RP; ++j) {
         const int ins = wave + NW * j;
-        if (ins < C::NI) {
-          const int t = ins_token(ins, ln);
-          const bool ok = t0 + t < n_valid;
-          if (ins < 16) {
-            const int c = ln & 31;
-            const float sc = ue8m0_scale(e[j]);
-            *reinterpret_cast<u32x4*>(K + lat_at(t, 2 * c)) = ok ? dequant8_fp8(u32x2{rv[j][0], rv[j][1]}, sc) : z;
-            *reinterpret_cast<u32x4*>(K + lat_at(t, 2 * c + 1)) = ok ? dequant8_fp8(u32x2{rv[j][2], rv[j][3]}, sc) : z;
-          } else {
-            *reinterpret_cast<u32x4*>(K + rope_at(t, ln & 7)) = ok ? rv[j] : z;
-          }
+        if (ins < 4) {
+          // rope of rows past the end only meets masked scores; it is copied as it is
+          const int t = rope_token(ins, ln);
+          *reinterpret_cast<u32x4*>(K + rope_at(t, ln & 7)) = rv[LP + j];
         }
       }
     } else {
+      // latent rows past the end must be finite (they meet P = 0 in PV); rope need not be
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
+      for (int j = 0; j < LP; ++j) {
         const int ins = wave + NW * j;
-        if (ins < C::NI) {
-          if (ins < 32) {
-            if (t0 + ins >= n_valid) *reinterpret_cast<u32x4*>(K + ins * kLat + 8 * ln) = z;
-          } else {
-            const int t = 8 * (ins - 32) + (ln >> 3);
-            if (t0 + t >= n_valid)
-              *reinterpret_cast<u32x4*>(K + kRopeOff + (ins - 32) * 512 + 8 * ln) = z;
-          }
-        }
+        if (ins < C::NL && t0 + ins >= n_valid) *reinterpret_cast<u32x4*>(K + ins * kLat + 8 * ln) = z;
       }
     }
   };
@@ -359,6 +415,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   for (int b = 0; b < 16; ++b) O[b] = f32x16{};
   l_part = 0.f;
   if (ntiles > 0) {
+    if (FMT == 1) issue_first_scales();
     if (C::NS > 0) {
 #pragma unroll
       for (int i = 0; i < C::NS; ++i) {
@@ -373,6 +430,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       issue_dma(0, sl);
       wait_vm();
     }
+    if (FMT == 1) __syncthreads();   // the scale wave's copy of tile 0's scales is visible
     finish_tile(0);
   }
   __syncthreads();
