@@ -129,7 +129,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int lane_id = lane;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
+  // wave-uniform, in an SGPR; the clamp tells the compiler its range
+  const int wave = NW == 4 ? (int)((unsigned)__builtin_amdgcn_readfirstlane(tid >> 6) & 3u)
+                           : __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row = blockIdx.x;
   const int split = blockIdx.y;
   const int p0 = split * a.chunk;
