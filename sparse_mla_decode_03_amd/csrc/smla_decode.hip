@@ -255,18 +255,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // FP8 byte offset of a slot's page and row: the page base, and the row within it
   auto fp8_page = [&](uint32_t slot) { return (size_t)(slot >> a.ps_log2) * ((size_t)kFp8Entry << a.ps_log2); };
   auto fp8_row = [&](uint32_t slot) { return slot & ((1u << a.ps_log2) - 1u); };
-  auto issue_dma = [&](int tile, const int (&sl)[NDMA]) {
-    // The lane id passes through an empty asm statement so that the per-lane address
-    // terms below are recomputed here instead of being hoisted out of the tile loop
-    // (which costs registers, then spills whose reloads would wait on the copies).
-    int ln = lane_id;
-    asm volatile("" : "+v"(ln));
+  // Copy part j of `tile`: latent parts 0..LP-1, rope parts LP..LP+RP-1, then (scale wave
+  // only) the scales of tile + 1.  `ln` is an opaque copy of the lane id: the per-lane
+  // address terms are recomputed at each part instead of being hoisted out of the tile loop
+  // (which costs registers, then spills whose reloads would wait on the copies).
+  auto issue_part = [&](int tile, int j, const int (&sl)[NDMA], int ln) {
     const int t0 = tile * kT;
     const int st = C::NS > 0 ? tile % (FMT == 1 ? C::NS : C::NK) : 0;
     uint16_t* K = sK + (FMT == 1 ? 0 : st) * kTile;
     uint8_t* raw = sRaw + (FMT == 1 ? st : 0) * (20 * 1024);
-#pragma unroll
-    for (int j = 0; j < LP; ++j) {
+    if (j < LP) {
       const int ins = wave + NW * j;
       if (ins < C::NL) {
         const int t = lat_token(ins, ln);
@@ -283,13 +281,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         }
         dma16(a.kv + (t0 + t < n_valid ? off : (size_t)(16 * ln)), dst);
       }
-    }
-#pragma unroll
-    for (int j = 0; j < RP; ++j) {
-      const int ins = wave + NW * j;
+    } else if (j < LP + RP) {
+      const int ins = wave + NW * (j - LP);
       if (ins < 4) {
         const int t = rope_token(ins, ln);
-        const uint32_t slot = (uint32_t)sl[LP + j];
+        const uint32_t slot = (uint32_t)sl[j];
         size_t off;
         uint8_t* dst;
         if (FMT == 1) {
@@ -301,14 +297,19 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         }
         dma16(a.kv + (t0 + t < n_valid ? off : (size_t)(16 * ln)), dst);
       }
-    }
-    if (scale_wave) {
+    } else if (scale_wave) {
       // scales of tile + 1: lane l copies 4 bytes of token l/2
       const int t = ln >> 1;
       const uint32_t slot = (uint32_t)sl[LP + RP];
       const size_t off = fp8_page(slot) + ((size_t)640 << a.ps_log2) + fp8_row(slot) * 8u + 4u * (ln & 1);
       dma4(a.kv + (t0 + kT + t < n_valid ? off : (size_t)(4 * (ln & 1))), sScl + ((tile + 1) % (C::NS + 1)) * 256);
     }
+  };
+  auto issue_dma = [&](int tile, const int (&sl)[NDMA]) {
+    int ln = lane_id;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) issue_part(tile, j, sl, ln);
   };
   // The scales of tile 0 (FP8), copied by the scale wave before anything else.
   auto issue_first_scales = [&]() {
@@ -468,10 +469,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         const u32x4 kv = kq[ks % kDepth];
         if (ks + kDepth < 36) kq[ks % kDepth] = kload(ks + kDepth);
         s = mfma32x32x16(kv, qf[ks], s);
+        // the copies of tile + NS are spread over the QK MFMAs, one part every few
+        // steps, so that the waves' copies reach the memory pipeline evenly
+        if (C::NS > 0) {
+#pragma unroll
+          for (int j = 0; j < NDMA; ++j)
+            if (ks == 2 + (j * 33) / NDMA) issue_part(tile + C::NS, j, sl, ln);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (C::NS > 0) issue_dma(tile + C::NS, sl);
 
     // PV B-operand: dv block b, k-step s2: lane l needs V[acc_row(8*s2 + kk, G)][32b + l%32]
     // for kk = 0..7.  Two transpose reads give kk 0..3 and 4..7: in each 16-lane group
