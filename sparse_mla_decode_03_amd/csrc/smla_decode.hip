@@ -32,7 +32,8 @@ constexpr int kLat = 512;               // bf16 per latent row of a K tile (1024
 constexpr int kRopeOff = kT * kLat;     // rope region: [32][64] bf16 after the latent rows
 constexpr int kTile = kRopeOff + kT * 64;  // bf16 per tile (36,864 bytes)
 constexpr int kCMax = 2048;             // positions per split handled by one workgroup
-constexpr int kDepth = 4;               // LDS operand loads kept in flight
+constexpr int kDepth = 4;               // LDS operand loads kept in flight (QK)
+constexpr int kDepthV = 3;              // LDS operand load pairs kept in flight (PV)
 // Exponentials are taken against a per-head reference max fixed at the first tile, so P
 // may exceed 1.  When a later tile's max exceeds the reference by more than 2^32 the
 // workgroup repeats the pass over the row with the larger reference; fp32 and bf16 hold
@@ -209,6 +210,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     n_valid = off;
     __syncthreads();
   }
+  // Slots past the valid count read as slot 0 (a real cache slot), so the copies of the
+  // last tile and of the tiles past the end need no per-lane selection; what they copy
+  // is masked when the tile is finished.
+  for (int i = n_valid + tid; i < kCMax; i += NT) sSlots[i] = 0;
+  __syncthreads();
 
   // ---- q fragments: lane holds head 32*wave + lane%32, dims 16*ks + 8*(lane/32) + 0..7
   // (padded heads read a real head's q; their results are never written)
@@ -237,14 +243,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // front of each copy.
   constexpr int LP = C::LP, RP = C::RP;
   constexpr int NDMA = LP + RP + (FMT == 1 ? 1 : 0);   // slot registers (scales last)
-  const bool scale_wave = FMT == 1 && wave == NW - 1;
+  // recomputed from the wave index where needed (cheaper than keeping the flag live)
+  auto scale_wave = [&]() { return FMT == 1 && __builtin_amdgcn_readfirstlane(tid >> 6) == NW - 1; };
   auto lat_token = [&](int ins, int ln) { return FMT == 1 ? 2 * ins + (ln >> 5) : ins; };
   auto rope_token = [&](int ins, int ln) { return 8 * ins + (ln >> 3); };
   auto load_slots = [&](int tile, int (&sl)[NDMA]) {
     int ln = lane_id;
     asm volatile("" : "+v"(ln));
     const int t0 = tile * kT;
-    // positions past the valid count read a stale (in-bounds) word; issue_dma drops it
+    // positions past the valid count read slot 0
 #pragma unroll
     for (int j = 0; j < LP; ++j) sl[j] = sSlots[min(t0 + lat_token(min(wave + NW * j, C::NL - 1), ln), kCMax - 1)];
 #pragma unroll
@@ -252,15 +259,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     // the scale wave copies the scales of the following tile
     if (FMT == 1) sl[LP + RP] = sSlots[min(t0 + kT + (ln >> 1), kCMax - 1)];
   };
-  // FP8 byte offset of a slot's page and row: the page base, and the row within it
-  auto fp8_page = [&](uint32_t slot) { return (size_t)(slot >> a.ps_log2) * ((size_t)kFp8Entry << a.ps_log2); };
+  // FP8 byte offset of a region of a slot's page: page * (648 << ps_log2) + add, with the
+  // 32-bit page stride (at most 648 KB) in one 32 x 32 -> 64-bit multiply-add
+  const uint32_t fp8_stride = (uint32_t)kFp8Entry << a.ps_log2;
+  auto fp8_off = [&](uint32_t slot, uint32_t add) {
+    return (size_t)((uint64_t)(slot >> a.ps_log2) * fp8_stride + add);
+  };
   auto fp8_row = [&](uint32_t slot) { return slot & ((1u << a.ps_log2) - 1u); };
   // Copy part j of `tile`: latent parts 0..LP-1, rope parts LP..LP+RP-1, then (scale wave
   // only) the scales of tile + 1.  `ln` is an opaque copy of the lane id: the per-lane
   // address terms are recomputed at each part instead of being hoisted out of the tile loop
   // (which costs registers, then spills whose reloads would wait on the copies).
   auto issue_part = [&](int tile, int j, const int (&sl)[NDMA], int ln) {
-    const int t0 = tile * kT;
     const int st = C::NS > 0 ? tile % (FMT == 1 ? C::NS : C::NK) : 0;
     uint16_t* K = sK + (FMT == 1 ? 0 : st) * kTile;
     uint8_t* raw = sRaw + (FMT == 1 ? st : 0) * (20 * 1024);
@@ -272,14 +282,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         size_t off;
         uint8_t* dst;
         if (FMT == 1) {
-          off = fp8_page(slot) + fp8_row(slot) * 512u + 16u * (ln & 31);
+          off = fp8_off(slot, fp8_row(slot) * 512u + 16u * (ln & 31));
           dst = raw + ins * 1024;
         } else {
           // lane = physical chunk of the destination row; it copies logical chunk lane ^ swz
           off = (size_t)slot * kBf16Entry + 16u * (ln ^ lat_swz(t));
           dst = reinterpret_cast<uint8_t*>(K + t * kLat);
         }
-        dma16(a.kv + (t0 + t < n_valid ? off : (size_t)(16 * ln)), dst);
+        dma16(a.kv + off, dst);
       }
     } else if (j < LP + RP) {
       const int ins = wave + NW * (j - LP);
@@ -289,20 +299,19 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         size_t off;
         uint8_t* dst;
         if (FMT == 1) {
-          off = fp8_page(slot) + ((size_t)512 << a.ps_log2) + fp8_row(slot) * 128u + 16u * (ln & 7);
+          off = fp8_off(slot, (512u << a.ps_log2) + fp8_row(slot) * 128u + 16u * (ln & 7));
           dst = raw + (16 + ins) * 1024;
         } else {
           off = (size_t)slot * kBf16Entry + 1024u + 16u * ((ln & 7) ^ ((t >> 1) & 7));
           dst = reinterpret_cast<uint8_t*>(K + kRopeOff) + ins * 1024;
         }
-        dma16(a.kv + (t0 + t < n_valid ? off : (size_t)(16 * ln)), dst);
+        dma16(a.kv + off, dst);
       }
-    } else if (scale_wave) {
+    } else if (scale_wave()) {
       // scales of tile + 1: lane l copies 4 bytes of token l/2
-      const int t = ln >> 1;
       const uint32_t slot = (uint32_t)sl[LP + RP];
-      const size_t off = fp8_page(slot) + ((size_t)640 << a.ps_log2) + fp8_row(slot) * 8u + 4u * (ln & 1);
-      dma4(a.kv + (t0 + kT + t < n_valid ? off : (size_t)(4 * (ln & 1))), sScl + ((tile + 1) % (C::NS + 1)) * 256);
+      const size_t off = fp8_off(slot, (640u << a.ps_log2) + fp8_row(slot) * 8u + 4u * (ln & 1));
+      dma4(a.kv + off, sScl + ((tile + 1) % (C::NS + 1)) * 256);
     }
   };
   auto issue_dma = [&](int tile, const int (&sl)[NDMA]) {
@@ -313,77 +322,95 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   };
   // The scales of tile 0 (FP8), copied by the scale wave before anything else.
   auto issue_first_scales = [&]() {
-    if (!scale_wave) return;
+    if (!scale_wave()) return;
     int ln = lane_id;
     asm volatile("" : "+v"(ln));
-    const int t = ln >> 1;
-    const uint32_t slot = (uint32_t)sSlots[t];
-    const size_t off = fp8_page(slot) + ((size_t)640 << a.ps_log2) + fp8_row(slot) * 8u + 4u * (ln & 1);
-    dma4(a.kv + (t < n_valid ? off : (size_t)(4 * (ln & 1))), sScl);
+    const uint32_t slot = (uint32_t)sSlots[ln >> 1];
+    const size_t off = fp8_off(slot, (640u << a.ps_log2) + fp8_row(slot) * 8u + 4u * (ln & 1));
+    dma4(a.kv + off, sScl);
   };
   // Wait for the oldest tile in flight; the NS - 1 younger ones may stay pending.
   auto wait_oldest = [&]() {
     if (C::NS <= 1) {
       wait_vm();
-    } else if (scale_wave) {
+    } else if (scale_wave()) {
       wait_vm_le<(C::NS > 1 ? (C::NS - 1) * (C::NMIN + 1) : 0)>();
     } else {
       wait_vm_le<(C::NS > 1 ? (C::NS - 1) * C::NMIN : 0)>();
     }
   };
 
+  auto kbuf_of = [&](int tile) { return C::NK > 1 ? tile % C::NK : 0; };
+  // FP8 dequantization of one part is split into a load step (the lane's raw unit and its
+  // scale byte from LDS) and a write step, so the parts can be spread over the PV MFMAs of
+  // the previous tile with each load a few MFMAs ahead of its write.
+  struct RawUnit {
+    u32x4 rv;
+    uint32_t e;
+  };
+  auto finish_load = [&](int tile, int j, int ln) {
+    RawUnit u;
+    const int st = C::NS > 0 ? tile % C::NS : 0;
+    const uint8_t* raw = sRaw + st * (20 * 1024);
+    if (j < LP) {
+      const int ins = min(wave + NW * j, C::NL - 1);
+      u.rv = *reinterpret_cast<const u32x4*>(raw + ins * 1024 + 16 * ln);
+      u.e = sScl[(tile % (C::NS + 1)) * 256 + 8 * lat_token(ins, ln) + ((ln & 31) >> 2)];
+    } else {
+      u.rv = *reinterpret_cast<const u32x4*>(raw + (16 + min(wave + NW * (j - LP), 3)) * 1024 + 16 * ln);
+      u.e = 0u;
+    }
+    return u;
+  };
+  auto finish_part = [&](int tile, int j, const RawUnit& u, int ln) {
+    const int t0 = tile * kT;
+    uint16_t* K = sK + kbuf_of(tile) * kTile;
+    if (j < LP) {
+      const int ins = wave + NW * j;
+      if (ins < C::NL) {
+        const int c = ln & 31;
+        const int t = lat_token(ins, ln);
+        u32x4 rv = u.rv;
+        uint32_t e = u.e;
+        if (t0 + kT > n_valid) {   // last tile (wave uniform): rows past the end become zero
+          const uint32_t m = t0 + t < n_valid ? 0xffffffffu : 0u;
+          rv &= m;
+          e &= m;
+        }
+        const float sc = ue8m0_scale(e);
+        *reinterpret_cast<u32x4*>(K + lat_at(t, 2 * c)) = dequant8_fp8(u32x2{rv[0], rv[1]}, sc);
+        *reinterpret_cast<u32x4*>(K + lat_at(t, 2 * c + 1)) = dequant8_fp8(u32x2{rv[2], rv[3]}, sc);
+      }
+    } else {
+      const int ins = wave + NW * (j - LP);
+      if (ins < 4) {
+        // rope of rows past the end only meets masked scores; it is copied as it is
+        const int t = rope_token(ins, ln);
+        *reinterpret_cast<u32x4*>(K + rope_at(t, ln & 7)) = u.rv;
+      }
+    }
+  };
   // After this lane's copies of `tile` have landed: FP8 dequantizes the units it copied
   // into the tile's K buffer (rows past the valid count become zero), BF16 zeroes the
-  // units of tokens past the valid count.  All LDS reads come before the first write.
-  auto kbuf_of = [&](int tile) { return C::NK > 1 ? tile % C::NK : 0; };
+  // units of tokens past the valid count.
   auto finish_tile = [&](int tile) {
     int ln = lane_id;
     asm volatile("" : "+v"(ln));
-    const int t0 = tile * kT;
-    uint16_t* K = sK + kbuf_of(tile) * kTile;
-    const int st = C::NS > 0 ? tile % (FMT == 1 ? C::NS : C::NK) : 0;
-    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
     if (FMT == 1) {
-      const uint8_t* raw = sRaw + st * (20 * 1024);
-      const uint8_t* scl = sScl + (tile % (C::NS + 1)) * 256;
-      const int c = ln & 31;
-      u32x4 rv[LP + RP];
-      uint32_t e[LP];
+      RawUnit u[LP + RP];
 #pragma unroll
-      for (int j = 0; j < LP; ++j) {
-        const int ins = min(wave + NW * j, C::NL - 1);
-        rv[j] = *reinterpret_cast<const u32x4*>(raw + ins * 1024 + 16 * ln);
-        e[j] = scl[8 * lat_token(ins, ln) + (c >> 2)];
-      }
+      for (int j = 0; j < LP + RP; ++j) u[j] = finish_load(tile, j, ln);
 #pragma unroll
-      for (int j = 0; j < RP; ++j)
-        rv[LP + j] = *reinterpret_cast<const u32x4*>(raw + (16 + min(wave + NW * j, 3)) * 1024 + 16 * ln);
-#pragma unroll
-      for (int j = 0; j < LP; ++j) {
-        const int ins = wave + NW * j;
-        if (ins < C::NL) {
-          const int t = lat_token(ins, ln);
-          const uint32_t m = t0 + t < n_valid ? 0xffffffffu : 0u;   // rows past the end: zero
-          const float sc = ue8m0_scale(e[j] & m);
-          *reinterpret_cast<u32x4*>(K + lat_at(t, 2 * c)) = dequant8_fp8(u32x2{rv[j][0] & m, rv[j][1] & m}, sc);
-          *reinterpret_cast<u32x4*>(K + lat_at(t, 2 * c + 1)) = dequant8_fp8(u32x2{rv[j][2] & m, rv[j][3] & m}, sc);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < RP; ++j) {
-        const int ins = wave + NW * j;
-        if (ins < 4) {
-          // rope of rows past the end only meets masked scores; it is copied as it is
-          const int t = rope_token(ins, ln);
-          *reinterpret_cast<u32x4*>(K + rope_at(t, ln & 7)) = rv[LP + j];
-        }
-      }
+      for (int j = 0; j < LP + RP; ++j) finish_part(tile, j, u[j], ln);
     } else {
       // latent rows past the end must be finite (they meet P = 0 in PV); rope need not be
+      const int t0 = tile * kT;
+      uint16_t* K = sK + kbuf_of(tile) * kTile;
 #pragma unroll
       for (int j = 0; j < LP; ++j) {
         const int ins = wave + NW * j;
-        if (ins < C::NL && t0 + ins >= n_valid) *reinterpret_cast<u32x4*>(K + ins * kLat + 8 * ln) = z;
+        if (ins < C::NL && t0 + ins >= n_valid)
+          *reinterpret_cast<u32x4*>(K + ins * kLat + 8 * ln) = u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
@@ -443,10 +470,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     const int t0 = tile * kT;
     const int nt = min(kT, n_valid - t0);
     const bool has_next = tile + 1 < ntiles;
-    // slots of the tile copied during this one (issued after QK, landed by then)
+    // With two K buffers and FP8, the dequantization of tile + 1 into the other buffer is
+    // spread over the QK MFMAs of this tile (QK leaves LDS bandwidth to spare, PV does
+    // not); its copies have landed after wait_oldest.
+    constexpr bool kWeave = FMT == 1 && C::NK > 1;
+    if (kWeave && has_next) wait_oldest();
+    // slots of the tile copied during this one
     int sl[NDMA];
     if (C::NS > 0) load_slots(tile + C::NS, sl);
-    const uint16_t* K = sK + kbuf_of(tile) * kTile;
 
     // ---- 3. QK: S^T[token][head]; lane holds head hl, tokens acc_row(r, G) -------------
     // The A operand (K rows) is software pipelined kDepth loads ahead; scheduling fences
@@ -455,13 +486,25 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     {
       int ln = lane_id;
       asm volatile("" : "+v"(ln));
-      const int qk_base = qk_base_of(ln);
-      const int rope_base = rope_base_of(ln);
+      // byte offsets into sK of the eight latent (ks % 8) and four rope lane bases of this
+      // tile's buffer, opaque to the compiler so each load is one LDS instruction with a
+      // constant offset
+      const int kbytes = 2 * kbuf_of(tile) * kTile;
+      int qoff[8], roff[4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qoff[i] = kbytes + 2 * (qk_base_of(ln) ^ (16 * i));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) roff[i] = kbytes + 2 * (rope_base_of(ln) ^ (16 * i));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(qoff[i]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(roff[i]));
       auto kload = [&](int ks) {
-        const int off = ks < 32 ? (qk_base ^ (16 * (ks & 7))) + 128 * (ks >> 3) : rope_base ^ (16 * (ks - 32));
-        return *reinterpret_cast<const u32x4*>(K + off);
+        const int off = ks < 32 ? qoff[ks & 7] + 256 * (ks >> 3) : roff[ks - 32];
+        return *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(sK) + off);
       };
       u32x4 kq[kDepth];
+      RawUnit un;
 #pragma unroll
       for (int i = 0; i < kDepth; ++i) kq[i] = kload(i);
 #pragma unroll
@@ -476,6 +519,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
           for (int j = 0; j < NDMA; ++j)
             if (ks == 2 + (j * 33) / NDMA) issue_part(tile + C::NS, j, sl, ln);
         }
+        // dequantization part j of tile + 1: loaded two MFMAs before it is written
+        if (kWeave && has_next) {
+#pragma unroll
+          for (int j = 0; j < LP + RP; ++j) {
+            if (ks == 3 + (j * 30) / (LP + RP)) un = finish_load(tile + 1, j, ln);
+            if (ks == 5 + (j * 30) / (LP + RP)) finish_part(tile + 1, j, un, ln);
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -486,14 +537,27 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     // 32b + 16*(gamma%2) + 4*(j%4) .. +3, i.e. logical chunk 4b + 2*(gamma%2) + (j%4)/2.
     int pln = lane_id;
     asm volatile("" : "+v"(pln));
-    const int pv_base = pv_base_of(pln);
+    // byte offsets into sK of the eight lane bases (b % 4, hh), opaque as for QK
+    int poff[8];
+    {
+      const int kbytes = 2 * kbuf_of(tile) * kTile;
+      const int pv_base = pv_base_of(pln);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int bb = i >> 1, hh = i & 1;
+        poff[i] = kbytes + 2 * ((pv_base ^ (8 * (4 * bb + 2 * hh))) + 4096 * hh);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(poff[i]));
+    }
     auto vaddr = [&](int step, int hh) {
       const int b = step >> 1, s2 = step & 1;
-      return K + ((pv_base ^ (8 * (4 * (b & 3) + 2 * hh))) + 8192 * s2 + 4096 * hh + 128 * (b >> 2));
+      return reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(sK) + poff[(b & 3) * 2 + hh] +
+                                               2 * (8192 * s2 + 128 * (b >> 2)));
     };
-    u32x2 vq[kDepth][2];
+    u32x2 vq[kDepthV][2];
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) {
+    for (int i = 0; i < kDepthV; ++i) {
       vq[i][0] = lds_read_tr16(vaddr(i, 0));
       vq[i][1] = lds_read_tr16(vaddr(i, 1));
     }
@@ -528,11 +592,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     // ---- 5. PV: O[head][dv] += P[head][token] V[token][dv] ---------------------------
 #pragma unroll
     for (int step = 0; step < 32; ++step) {
-      const u32x2 v0 = vq[step % kDepth][0];
-      const u32x2 v1 = vq[step % kDepth][1];
-      if (step + kDepth < 32) {
-        vq[step % kDepth][0] = lds_read_tr16(vaddr(step + kDepth, 0));
-        vq[step % kDepth][1] = lds_read_tr16(vaddr(step + kDepth, 1));
+      const u32x2 v0 = vq[step % kDepthV][0];
+      const u32x2 v1 = vq[step % kDepthV][1];
+      if (step + kDepthV < 32) {
+        vq[step % kDepthV][0] = lds_read_tr16(vaddr(step + kDepthV, 0));
+        vq[step % kDepthV][1] = lds_read_tr16(vaddr(step + kDepthV, 1));
       }
       O[step >> 1] = mfma32x32x16(pa[step & 1], u32x4{v0[0], v0[1], v1[0], v1[1]}, O[step >> 1]);
       __builtin_amdgcn_sched_barrier(0);
@@ -541,8 +605,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     // ---- next tile: finish its gather -------------------------------------------------
     if (has_next) {
       if (C::NK > 1) {
-        wait_oldest();
-        finish_tile(tile + 1);
+        if (!kWeave) {
+          wait_oldest();
+          finish_tile(tile + 1);
+        }
       } else {
         __syncthreads();                 // everyone is done reading the single K tile
         if (C::NS == 0) {
