@@ -54,6 +54,17 @@ __device__ __forceinline__ int rope_at(int row, int chunk) {
   return kRopeOff + row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
+// Cross-half reductions: lanes l and l ^ 32 hold the same head (other tokens); one
+// permlane32 swap gives every lane both values.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Token position (0..31) held in accumulator register r (0..15) of lane group G (lane/32)
 // by a 32x32 MFMA whose rows are tokens.
 __device__ __forceinline__ int acc_row(int r, int G) { return 8 * (r >> 2) + 4 * G + (r & 3); }
@@ -563,25 +574,43 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     }
 
     // ---- 4. softmax (exp2 domain) against a per-head reference max m_used ------------
-    float mx = -INFINITY;
+    // Full tiles with a positive scale (the usual case) need no masking, and the scale
+    // is folded into one multiply of the max and one FMA per score.
+    const bool fast = nt == kT && a.scale_log2 > 0.f;   // wave uniform
+    float mx;
+    if (fast) {
+      float m8[8];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = (acc_row(r, G) < nt) ? s[r] * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, s[r]);
+      for (int r = 0; r < 8; ++r) m8[r] = fmaxf(s[2 * r], s[2 * r + 1]);
+      mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])), fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+      mx *= a.scale_log2;
+    } else {
+      mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = (acc_row(r, G) < nt) ? s[r] * a.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, s[r]);
+      }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_halves(mx);
     if (m_used == -INFINITY) m_used = mx;       // first tile: O and l are still zero
     if (mx > m_used + kRestartLog2) {           // rare: raise the reference and restart
       m_used = mx;
       sRestart = 1;
     }
-    float ls = 0.f;
+    if (fast) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = (s[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[r] - m_used);
-      ls += s[r];
+      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, -m_used));
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = (s[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[r] - m_used);
     }
-    l_part += ls;
+    {
+      float p8[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) p8[r] = s[2 * r] + s[2 * r + 1];
+      l_part += ((p8[0] + p8[1]) + (p8[2] + p8[3])) + ((p8[4] + p8[5]) + (p8[6] + p8[7]));
+    }
     // P as the PV A operand: k-step s2 uses the lane's tokens acc_row(8*s2 + kk, G)
     u32x4 pa[2];
 #pragma unroll
@@ -635,7 +664,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   }
 
   // ---- 6. epilogue ----------------------------------------------------------------------
-  const float l_tot = l_part + __shfl_xor(l_part, 32);
+  const float l_tot = sum_halves(l_part);
   float factor, lse_v;
   if (a.write_partials) {
     if (l_tot > 0.f) {
