@@ -206,6 +206,8 @@ def main() -> int:
             "mfma_tflop_s": mfma_tflops,
             "launch_ms_mean": mean_launch_s * 1e3,
             "launch_ms_min": min(launch_ms),
+            "launch_ms_p50": sorted(launch_ms)[len(launch_ms) // 2],
+            "launch_ms_p90": sorted(launch_ms)[min(len(launch_ms) - 1, (9 * len(launch_ms)) // 10)],
             "input_generation_s": round(t_gen, 2),
         },
         "roofline": {
