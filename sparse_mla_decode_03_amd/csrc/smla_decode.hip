@@ -47,12 +47,8 @@ constexpr float kRestartLog2 = 32.0f;
 //   QK A operand: 16 consecutive rows at one chunk -> 16 different chunk slots;
 //   PV transpose reads: 4 consecutive rows x 4 consecutive chunks -> 16 different slots.
 // Rope rows are 128 bytes (two per bank row) with the chunk XORed with (row/2)%8.
-// Offsets are in bf16 elements; `chunk` is the logical 16-byte chunk (dims 8c..8c+7).
+// A chunk is 16 bytes (8 bf16 dims).
 __device__ __forceinline__ int lat_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
-__device__ __forceinline__ int lat_at(int row, int chunk) { return row * kLat + ((chunk ^ lat_swz(row)) << 3); }
-__device__ __forceinline__ int rope_at(int row, int chunk) {
-  return kRopeOff + row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
-}
 
 // Cross-half reductions: lanes l and l ^ 32 hold the same head (other tokens); one
 // permlane32 swap gives every lane both values.
@@ -221,11 +217,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     n_valid = off;
     __syncthreads();
   }
-  // Slots past the valid count read as slot 0 (a real cache slot), so the copies of the
-  // last tile and of the tiles past the end need no per-lane selection; what they copy
-  // is masked when the tile is finished.
-  for (int i = n_valid + tid; i < kCMax; i += NT) sSlots[i] = 0;
-  __syncthreads();
+  // Positions past the valid count repeat the split's first valid slot, so the copies of
+  // the last tile and of the tiles past the end need no per-lane selection and bring in
+  // finite data (a valid entry of this very split) that meets a masked score, P = 0.
+  {
+    const int first = n_valid > 0 ? sSlots[0] : 0;
+    __syncthreads();
+    for (int i = n_valid + tid; i < kCMax; i += NT) sSlots[i] = first;
+    __syncthreads();
+  }
 
   // ---- q fragments: lane holds head 32*wave + lane%32, dims 16*ks + 8*(lane/32) + 0..7
   // (padded heads read a real head's q; their results are never written)
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     int ln = lane_id;
     asm volatile("" : "+v"(ln));
     const int t0 = tile * kT;
-    // positions past the valid count read slot 0
+    // positions past the valid count read the split's first valid slot
 #pragma unroll
     for (int j = 0; j < LP; ++j) sl[j] = sSlots[min(t0 + lat_token(min(wave + NW * j, C::NL - 1), ln), kCMax - 1)];
 #pragma unroll
@@ -353,76 +353,71 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 
   auto kbuf_of = [&](int tile) { return C::NK > 1 ? tile % C::NK : 0; };
   // FP8 dequantization of one part is split into a load step (the lane's raw unit and its
-  // scale byte from LDS) and a write step, so the parts can be spread over the PV MFMAs of
-  // the previous tile with each load a few MFMAs ahead of its write.
+  // scale byte from LDS) and a write step, so the parts can be spread over the MFMAs with
+  // each load a few MFMAs ahead of its write.  All addresses are a per-tile lane base plus
+  // wave-uniform terms: for latent instruction i the unit of token t = 2i + G, dims
+  // 16c..16c+15 (c = lane % 32) goes to swizzled chunks 2c and 2c + 1 of row t, and
+  // (2c ^ swz(t)) = (2c ^ 4G) ^ U(i) with U(i) = 8(i % 2) + (i / 2) % 4; rope instruction r
+  // puts token 8r + lane / 8, chunk lane % 8, at chunk (lane % 8) ^ (lane / 16) ^ 4(r % 2).
+  struct DqBase {
+    int raw;    // byte offset into sRaw of this lane's unit of instruction `wave`
+    int scl;    // byte offset into sScl of this lane's scale byte for instruction `wave`
+    int lat;    // lane part of the latent write offset (bits 4..10)
+    int rope;   // lane part of the rope write offset (bits 4..9)
+    int kb;     // byte offset of the destination K buffer
+  };
+  auto dq_base = [&](int tile, int ln) {
+    DqBase d;
+    const int G_ = ln >> 5, c = ln & 31;
+    d.raw = (C::NS > 0 ? tile % C::NS : 0) * (20 * 1024) + wave * 1024 + 16 * ln;
+    d.scl = (tile % (C::NS + 1)) * 256 + 16 * wave + 8 * G_ + (c >> 2);
+    d.lat = 1024 * G_ + ((32 * c) ^ (64 * G_));
+    d.rope = 128 * (ln >> 3) + 16 * ((ln & 7) ^ (ln >> 4));
+    d.kb = 2 * kbuf_of(tile) * kTile;
+    return d;
+  };
   struct RawUnit {
     u32x4 rv;
     uint32_t e;
   };
-  auto finish_load = [&](int tile, int j, int ln) {
+  auto finish_load = [&](int j, const DqBase& d) {
     RawUnit u;
-    const int st = C::NS > 0 ? tile % C::NS : 0;
-    const uint8_t* raw = sRaw + st * (20 * 1024);
     if (j < LP) {
-      const int ins = min(wave + NW * j, C::NL - 1);
-      u.rv = *reinterpret_cast<const u32x4*>(raw + ins * 1024 + 16 * ln);
-      u.e = sScl[(tile % (C::NS + 1)) * 256 + 8 * lat_token(ins, ln) + ((ln & 31) >> 2)];
+      u.rv = *reinterpret_cast<const u32x4*>(sRaw + d.raw + NW * j * 1024);
+      u.e = sScl[d.scl + 16 * NW * j];
     } else {
-      u.rv = *reinterpret_cast<const u32x4*>(raw + (16 + min(wave + NW * (j - LP), 3)) * 1024 + 16 * ln);
+      u.rv = *reinterpret_cast<const u32x4*>(sRaw + d.raw + (16 + NW * (j - LP)) * 1024);
       u.e = 0u;
     }
     return u;
   };
-  auto finish_part = [&](int tile, int j, const RawUnit& u, int ln) {
-    const int t0 = tile * kT;
-    uint16_t* K = sK + kbuf_of(tile) * kTile;
+  auto finish_part = [&](int j, const RawUnit& u, const DqBase& d) {
+    uint8_t* Kb = reinterpret_cast<uint8_t*>(sK) + d.kb;
     if (j < LP) {
       const int ins = wave + NW * j;
       if (ins < C::NL) {
-        const int c = ln & 31;
-        const int t = lat_token(ins, ln);
-        u32x4 rv = u.rv;
-        uint32_t e = u.e;
-        if (t0 + kT > n_valid) {   // last tile (wave uniform): rows past the end become zero
-          const uint32_t m = t0 + t < n_valid ? 0xffffffffu : 0u;
-          rv &= m;
-          e &= m;
-        }
-        const float sc = ue8m0_scale(e);
-        *reinterpret_cast<u32x4*>(K + lat_at(t, 2 * c)) = dequant8_fp8(u32x2{rv[0], rv[1]}, sc);
-        *reinterpret_cast<u32x4*>(K + lat_at(t, 2 * c + 1)) = dequant8_fp8(u32x2{rv[2], rv[3]}, sc);
+        const int U16 = 16 * (((ins & 1) << 3) | ((ins >> 1) & 3));
+        const float sc = ue8m0_scale(u.e);
+        *reinterpret_cast<u32x4*>(Kb + 2048 * ins + (d.lat ^ U16)) = dequant8_fp8(u32x2{u.rv[0], u.rv[1]}, sc);
+        *reinterpret_cast<u32x4*>(Kb + 2048 * ins + (d.lat ^ U16 ^ 16)) = dequant8_fp8(u32x2{u.rv[2], u.rv[3]}, sc);
       }
     } else {
-      const int ins = wave + NW * (j - LP);
-      if (ins < 4) {
-        // rope of rows past the end only meets masked scores; it is copied as it is
-        const int t = rope_token(ins, ln);
-        *reinterpret_cast<u32x4*>(K + rope_at(t, ln & 7)) = u.rv;
-      }
+      const int r = wave + NW * (j - LP);
+      if (r < 4) *reinterpret_cast<u32x4*>(Kb + 2 * kRopeOff + 1024 * r + (d.rope ^ (64 * (r & 1)))) = u.rv;
     }
   };
   // After this lane's copies of `tile` have landed: FP8 dequantizes the units it copied
-  // into the tile's K buffer (rows past the valid count become zero), BF16 zeroes the
-  // units of tokens past the valid count.
+  // into the tile's K buffer.  (BF16 copies land in the K buffer directly.)
   auto finish_tile = [&](int tile) {
-    int ln = lane_id;
-    asm volatile("" : "+v"(ln));
     if (FMT == 1) {
+      int ln = lane_id;
+      asm volatile("" : "+v"(ln));
+      const DqBase d = dq_base(tile, ln);
       RawUnit u[LP + RP];
 #pragma unroll
-      for (int j = 0; j < LP + RP; ++j) u[j] = finish_load(tile, j, ln);
+      for (int j = 0; j < LP + RP; ++j) u[j] = finish_load(j, d);
 #pragma unroll
-      for (int j = 0; j < LP + RP; ++j) finish_part(tile, j, u[j], ln);
-    } else {
-      // latent rows past the end must be finite (they meet P = 0 in PV); rope need not be
-      const int t0 = tile * kT;
-      uint16_t* K = sK + kbuf_of(tile) * kTile;
-#pragma unroll
-      for (int j = 0; j < LP; ++j) {
-        const int ins = wave + NW * j;
-        if (ins < C::NL && t0 + ins >= n_valid)
-          *reinterpret_cast<u32x4*>(K + ins * kLat + 8 * ln) = u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int j = 0; j < LP + RP; ++j) finish_part(j, u[j], d);
     }
   };
 
@@ -483,9 +478,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     const bool has_next = tile + 1 < ntiles;
     // With two K buffers and FP8, the dequantization of tile + 1 into the other buffer is
     // spread over the QK MFMAs of this tile (QK leaves LDS bandwidth to spare, PV does
-    // not); its copies have landed after wait_oldest.
+    // not); its copies have landed after wait_oldest.  Past the last tile this converts
+    // the copies of positions past the end into a buffer nobody reads.
     constexpr bool kWeave = FMT == 1 && C::NK > 1;
-    if (kWeave && has_next) wait_oldest();
+    if (kWeave) wait_oldest();
     // slots of the tile copied during this one
     int sl[NDMA];
     if (C::NS > 0) load_slots(tile + C::NS, sl);
@@ -516,6 +512,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       };
       u32x4 kq[kDepth];
       RawUnit un;
+      const DqBase dq = dq_base(tile + 1, ln);
 #pragma unroll
       for (int i = 0; i < kDepth; ++i) kq[i] = kload(i);
 #pragma unroll
@@ -531,11 +528,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
             if (ks == 2 + (j * 33) / NDMA) issue_part(tile + C::NS, j, sl, ln);
         }
         // dequantization part j of tile + 1: loaded two MFMAs before it is written
-        if (kWeave && has_next) {
+        if (kWeave) {
 #pragma unroll
           for (int j = 0; j < LP + RP; ++j) {
-            if (ks == 3 + (j * 30) / (LP + RP)) un = finish_load(tile + 1, j, ln);
-            if (ks == 5 + (j * 30) / (LP + RP)) finish_part(tile + 1, j, un, ln);
+            if (ks == 3 + (j * 30) / (LP + RP)) un = finish_load(j, dq);
+            if (ks == 5 + (j * 30) / (LP + RP)) finish_part(j, un, dq);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
