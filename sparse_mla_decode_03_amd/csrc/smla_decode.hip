@@ -20,6 +20,8 @@
 //      the QK accumulator registers and V read from the same K tile with LDS transpose
 //      reads (no separate V^T copy);
 //   6. epilogue: final output with the sink folded in, or the sink-free split partial.
+#include <type_traits>
+
 #include "smla_device.h"
 #include "smla_kernels.h"
 
@@ -115,7 +117,7 @@ struct Cfg {
   // into NK bf16 K tiles; BF16 copies into a ring of NS + 1 K tiles, or synchronously
   // (NS = 0) when the workgroup must stay small enough for two per CU.
   static constexpr bool BIG = NW >= 3;                  // one workgroup per CU
-  static constexpr int NS = FMT == 1 ? (BIG ? 2 : 1) : (BIG ? 2 : 0);
+  static constexpr int NS = FMT == 1 ? (BIG ? 3 : 1) : (BIG ? 2 : 0);
   static constexpr int NK = FMT == 1 ? (BIG ? 2 : 1) : (BIG ? NS + 1 : 1);
   static constexpr int RAW_BYTES = FMT == 1 ? NS * 20 * 1024 : 16;
   static constexpr int SCL_BYTES = FMT == 1 ? (NS + 1) * 256 : 16;
@@ -341,15 +343,26 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     dma4(a.kv + off, sScl);
   };
   // Wait for the oldest tile in flight; the NS - 1 younger ones may stay pending.
-  auto wait_oldest = [&]() {
-    if (C::NS <= 1) {
+  // A wave issues one group of copies per tile (its parts of tile + NS, in issue order).
+  // Counting from the newest, at most `keep` groups may stay pending; vmcnt completes in
+  // issue order, so everything older has landed.  The scale wave's groups are one copy
+  // longer (the scales); waves issuing more than NMIN copies per group wait for a few of
+  // their newest copies as well, which is harmless.
+  auto wait_groups = [&](auto keep) {
+    constexpr int kKeep = decltype(keep)::value;
+    if constexpr (kKeep <= 0) {
       wait_vm();
-    } else if (scale_wave()) {
-      wait_vm_le<(C::NS > 1 ? (C::NS - 1) * (C::NMIN + 1) : 0)>();
     } else {
-      wait_vm_le<(C::NS > 1 ? (C::NS - 1) * C::NMIN : 0)>();
+      if (scale_wave())
+        wait_vm_le<kKeep * (C::NMIN + 1)>();
+      else
+        wait_vm_le<kKeep * C::NMIN>();
     }
   };
+  // After this wave's group for tile + NS is issued: tile + 1 has landed.
+  auto wait_oldest = [&]() { wait_groups(std::integral_constant<int, C::NS - 1>{}); };
+  // Before this wave's group for tile + NS is issued: tile + 1 has landed.
+  auto wait_next = [&]() { wait_groups(std::integral_constant<int, C::NS - 2>{}); };
 
   auto kbuf_of = [&](int tile) { return C::NK > 1 ? tile % C::NK : 0; };
   // FP8 dequantization of one part is split into a load step (the lane's raw unit and its
@@ -478,10 +491,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     const bool has_next = tile + 1 < ntiles;
     // With two K buffers and FP8, the dequantization of tile + 1 into the other buffer is
     // spread over the QK MFMAs of this tile (QK leaves LDS bandwidth to spare, PV does
-    // not); its copies have landed after wait_oldest.  Past the last tile this converts
-    // the copies of positions past the end into a buffer nobody reads.
+    // not); its copies have landed after wait_next (this tile's own group of copies is
+    // issued inside QK, after the wait).  Past the last tile this converts the copies of
+    // positions past the end into a buffer nobody reads.
     constexpr bool kWeave = FMT == 1 && C::NK > 1;
-    if (kWeave) wait_oldest();
+    if (kWeave) wait_next();
     // slots of the tile copied during this one
     int sl[NDMA];
     if (C::NS > 0) load_slots(tile + C::NS, sl);
