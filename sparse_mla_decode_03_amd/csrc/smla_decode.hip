@@ -638,7 +638,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         vq[step % kDepthV][0] = lds_read_tr16(vaddr(step + kDepthV, 0));
         vq[step % kDepthV][1] = lds_read_tr16(vaddr(step + kDepthV, 1));
       }
-      O[step >> 1] = mfma32x32x16(pa[step & 1], u32x4{v0[0], v0[1], v1[0], v1[1]}, O[step >> 1]);
+      // O^T[dv][head] += V^T[dv][token] P^T[token][head]: the V registers are the A operand
+      // (rows = dv) and P the B operand (columns = heads), so each lane's accumulator holds
+      // one head and runs of four consecutive dv.
+      O[step >> 1] = mfma32x32x16(u32x4{v0[0], v0[1], v1[0], v1[1]}, pa[step & 1], O[step >> 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -701,38 +704,39 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     }
   }
 
-  // Accumulator register r of lane l holds head 32*wave + acc_row(r, G), dv 32b + hl.
-  float fr[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) fr[r] = __shfl(factor, acc_row(r, G));
-  const int hbase = 32 * wave + 4 * G;
+  // Accumulator register r of block b holds head h (this lane's) at dv 32b + acc_row(r, G):
+  // registers 4k..4k+3 are four consecutive dv, stored as one 8-byte (bf16) or 16-byte
+  // (fp32 partial) piece.
   if (a.write_partials) {
     const size_t rs = (size_t)row * a.S + split;
-    float* po = a.part_o + (rs * a.H) * kV + hl;
+    if (h_ok) {
+      float* po = a.part_o + (rs * a.H + h) * kV + 4 * G;
 #pragma unroll
-    for (int b = 0; b < 16; ++b) {
-      const f32x16 ob = O[b];
+      for (int b = 0; b < 16; ++b) {
+        const f32x16 ob = O[b];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int hr = hbase + 8 * (r >> 2) + (r & 3);
-        if (hr < a.H) po[(size_t)hr * kV + 32 * b] = ob[r] * fr[r];
+        for (int k = 0; k < 4; ++k)
+          *reinterpret_cast<f32x4*>(po + 32 * b + 8 * k) =
+              f32x4{ob[4 * k] * factor, ob[4 * k + 1] * factor, ob[4 * k + 2] * factor, ob[4 * k + 3] * factor};
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      if (G == 0) a.part_lse[rs * a.H + h] = lse_v;
     }
-    if (G == 0 && h_ok) a.part_lse[rs * a.H + h] = lse_v;
   } else {
-    __bf16* ob_ptr = reinterpret_cast<__bf16*>(a.out) + ((size_t)row * a.H) * kV + hl;
+    if (h_ok) {
+      uint16_t* op = a.out + ((size_t)row * a.H + h) * kV + 4 * G;
 #pragma unroll
-    for (int b = 0; b < 16; ++b) {
-      const f32x16 ob = O[b];
+      for (int b = 0; b < 16; ++b) {
+        const f32x16 ob = O[b];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int hr = hbase + 8 * (r >> 2) + (r & 3);
-        if (hr < a.H) ob_ptr[(size_t)hr * kV + 32 * b] = (__bf16)(ob[r] * fr[r]);
+        for (int k = 0; k < 4; ++k)
+          *reinterpret_cast<u32x2*>(op + 32 * b + 8 * k) =
+              u32x2{pack_bf16x2(ob[4 * k] * factor, ob[4 * k + 1] * factor),
+                    pack_bf16x2(ob[4 * k + 2] * factor, ob[4 * k + 3] * factor)};
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      if (a.lse != nullptr && G == 0) a.lse[(size_t)row * a.H + h] = lse_v;
     }
-    if (a.lse != nullptr && G == 0 && h_ok) a.lse[(size_t)row * a.H + h] = lse_v;
   }
 }
 
