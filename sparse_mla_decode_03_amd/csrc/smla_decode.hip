@@ -149,6 +149,20 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int ps_mask = (1 << a.ps_log2) - 1;
   if (tid == 0) sRestart = 0;
 
+  // ---- q fragments: lane holds head 32*wave + lane%32, dims 16*ks + 8*(lane/32) + 0..7
+  // (padded heads read a real head's q; their results are never written).  Loaded first,
+  // so their latency overlaps the index translation.
+  const int hl = lane & 31;
+  const int G = lane >> 5;
+  const int h = wave * 32 + hl;
+  const bool h_ok = h < a.H;
+  u32x4 qf[36];
+  {
+    const uint16_t* qp = a.q + ((size_t)row * a.H + min(h, a.H - 1)) * kQK + 8 * G;
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+  }
+
   // ---- 1. translate and compact the split's indices --------------------------------
   // Positions are taken in batches of kCB per thread; all index loads of a batch, then all
   // its page-table loads, are in flight together.
@@ -228,22 +242,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     for (int i = n_valid + tid; i < kCMax; i += NT) sSlots[i] = first;
     __syncthreads();
   }
-
-  // ---- q fragments: lane holds head 32*wave + lane%32, dims 16*ks + 8*(lane/32) + 0..7
-  // (padded heads read a real head's q; their results are never written)
-  const int hl = lane & 31;
-  const int G = lane >> 5;
-  const int h = wave * 32 + hl;
-  const bool h_ok = h < a.H;
-  u32x4 qf[36];
-  {
-    const uint16_t* qp = a.q + ((size_t)row * a.H + min(h, a.H - 1)) * kQK + 8 * G;
-#pragma unroll
-    for (int ks = 0; ks < 36; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
-    // land q before the tile loop, so no wait on the in-flight tile copies is placed at
-    // its first use inside the loop
-    wait_vm();
-  }
+  // land q before the tile copies start, so no wait on them is placed at its first use
+  // inside the loop
+  wait_vm();
 
   float m_used = -INFINITY;
 
@@ -723,20 +724,40 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       if (G == 0) a.part_lse[rs * a.H + h] = lse_v;
     }
   } else {
-    if (h_ok) {
-      uint16_t* op = a.out + ((size_t)row * a.H + h) * kV + 4 * G;
+    // bf16 output through a per-wave LDS stage (the K buffers are free now), in two halves
+    // of 256 dv: each lane writes its 8-byte runs into rows of 520 bytes (one per head;
+    // the 8-byte pad keeps the 32 rows' writes on different banks), then reads back
+    // 16-byte chunks along dv, so every global store writes two whole 512-byte row halves.
+    constexpr int kPitch = 520;
+    static_assert(NW * 32 * kPitch <= (int)sizeof(sK), "output stage exceeds the K buffers");
+    __syncthreads();   // every wave is past its last read of sK (and its copies drained)
+    uint8_t* stage = reinterpret_cast<uint8_t*>(sK) + wave * (32 * kPitch);
+    int ln = lane_id;
+    asm volatile("" : "+v"(ln));
+    const int w_off = (ln & 31) * kPitch + 8 * (ln >> 5);          // row = head, +4 dv for G
+    const int r_off = (ln >> 5) * kPitch + 16 * (ln & 31);         // row (ln / 32) + 2i, chunk
 #pragma unroll
-      for (int b = 0; b < 16; ++b) {
-        const f32x16 ob = O[b];
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb) {
+        const f32x16 ob = O[8 * half + bb];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          *reinterpret_cast<u32x2*>(op + 32 * b + 8 * k) =
+          *reinterpret_cast<u32x2*>(stage + w_off + 64 * bb + 16 * k) =
               u32x2{pack_bf16x2(ob[4 * k] * factor, ob[4 * k + 1] * factor),
                     pack_bf16x2(ob[4 * k + 2] * factor, ob[4 * k + 3] * factor)};
-        __builtin_amdgcn_sched_barrier(0);
       }
-      if (a.lse != nullptr && G == 0) a.lse[(size_t)row * a.H + h] = lse_v;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int hr = 32 * wave + 2 * i + (ln >> 5);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r_off + 2 * i * kPitch);
+        if (hr < a.H)
+          *reinterpret_cast<u32x4*>(a.out + ((size_t)row * a.H + hr) * kV + 256 * half + 8 * (ln & 31)) = v;
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if (a.lse != nullptr && G == 0 && h_ok) a.lse[(size_t)row * a.H + h] = lse_v;
   }
 }
 
