@@ -109,6 +109,9 @@ def main() -> int:
     ap.add_argument("--num-splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="extra launches, each after a 1 GiB scratch write that evicts the "
+                         "caches (L2 and the 256 MB MALL); reported beside the warm figure")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run only a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -171,6 +174,21 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     launch_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+
+    # Cold-cache launches: the scratch write sits outside each event pair.
+    cold_ms = []
+    if args.cold_steps > 0:
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.cold_steps)]
+        for e0, e1 in cevs:
+            scratch.fill_(1)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        cold_ms = sorted(e0.elapsed_time(e1) for e0, e1 in cevs)
+        del scratch
     mean_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
 
     n_valid = inp.num_valid()
@@ -208,6 +226,10 @@ def main() -> int:
             "launch_ms_min": min(launch_ms),
             "launch_ms_p50": sorted(launch_ms)[len(launch_ms) // 2],
             "launch_ms_p90": sorted(launch_ms)[min(len(launch_ms) - 1, (9 * len(launch_ms)) // 10)],
+            "launch_ms_p10": sorted(launch_ms)[len(launch_ms) // 10],
+            "cold_cache_launch_ms_p50": cold_ms[len(cold_ms) // 2] if cold_ms else None,
+            "cold_cache_launch_ms_p10": cold_ms[len(cold_ms) // 10] if cold_ms else None,
+            "cold_cache_launch_ms_p90": cold_ms[min(len(cold_ms) - 1, (9 * len(cold_ms)) // 10)] if cold_ms else None,
             "input_generation_s": round(t_gen, 2),
         },
         "roofline": {

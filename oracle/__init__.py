@@ -1,4 +1,4 @@
-"""Float64 CPU oracle for the sparse MLA decode path.
+"""Float64 CPU oracle for the sparse MLA decode path and the cache store before it.
 
 TEST INFRASTRUCTURE: only tests/, the smoke check in __graft_entry__ and the
 cpu_baseline leg of bench.py may import it.  The library never does; it shares no
@@ -25,4 +25,10 @@ from .sparse_mla_oracle import (  # noqa: F401
     sparse_mla_decode_partials,
     translate,
     ue8m0_to_f64,
+)
+from .cache_store_oracle import (  # noqa: F401,E402
+    cache_store,
+    e4m3fn_nearest,
+    quantize_fp8_ue8m0,
+    ue8m0_for_amax,
 )
