@@ -185,6 +185,26 @@ smla_status sparse_mla_merge_partials(const float* partial_o, const float* parti
                                       int32_t num_rows, int32_t num_splits, int32_t num_heads,
                                       const float* sinks, void* out, float* lse, void* stream);
 
+/* Write new tokens into the paged cache (the step before the decode path: the FP8 paged
+ * cache with UE8M0 scales per 64 latent elements and a bf16 rope part of prhub vllm#43827,
+ * motivation and key code excerpts; in-page addressing as on prhub sglang#24692,
+ * implementation breakdown 2).
+ *   latent    bf16 [num_tokens][512], rope bf16 [num_tokens][64]   (device, 16-byte aligned)
+ *   slots     int32 [num_tokens]: the global slot (page * page_size + row) of each token;
+ *             negative or >= num_pages * page_size: the token is skipped.  Slots must be
+ *             distinct: for a repeated slot it is unspecified which token's bytes remain.
+ *   kv_cache  the cache of the layout above, updated in place (caller-owned)
+ * FP8: each 64-element group gets the scale byte e (value 2^(e-127)) of the smallest power
+ * of two with 448 * 2^(e-127) >= the group's largest magnitude (e = 127 for an all-zero
+ * group; clamped to [0, 254]) and codes = e4m3fn(x / 2^(e-127)) rounded to nearest, ties to
+ * even; the rope is copied.  BF16: the 576 values are copied.  Non-finite inputs give
+ * unspecified codes.  num_tokens == 0 returns SMLA_OK without launching.  No allocation;
+ * asynchronous on `stream`.
+ * Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED (format; FP8 with page_size < 2), MISALIGNED, HIP. */
+smla_status sparse_mla_cache_store(const void* latent, const void* rope, const int32_t* slots,
+                                   int32_t num_tokens, int32_t kv_format, int32_t page_size,
+                                   int32_t num_pages, void* kv_cache, void* stream);
+
 /* Test helper: decode n cache slots (global slot numbers, device int32 [n]) into bf16
  * rows out[n][576] with the same device code the decode kernel uses for its gather and
  * dequantisation.  Slots outside [0, num_pages*page_size) give a zero row.

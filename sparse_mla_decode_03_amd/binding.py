@@ -38,6 +38,7 @@ F_CHECK_INDICES = 2
 EXPORTED = [
     "sparse_mla_decode_plan", "sparse_mla_plan_num_splits", "sparse_mla_decode_run",
     "sparse_mla_merge_partials", "sparse_mla_gather_debug", "sparse_mla_read_index_error",
+    "sparse_mla_cache_store",
     "sparse_mla_status_string", "sparse_mla_version",
 ]
 
@@ -86,6 +87,8 @@ def load_library(path: str = LIB_PATH):
     lib.sparse_mla_merge_partials.restype = ctypes.c_int
     lib.sparse_mla_gather_debug.argtypes = [vp, i32, i32, i32, i32p, i32, vp, vp]
     lib.sparse_mla_gather_debug.restype = ctypes.c_int
+    lib.sparse_mla_cache_store.argtypes = [vp, vp, i32p, i32, i32, i32, i32, vp, vp]
+    lib.sparse_mla_cache_store.restype = ctypes.c_int
     lib.sparse_mla_read_index_error.argtypes = [ctypes.POINTER(Plan), vp, ctypes.POINTER(i32 * 2), vp]
     lib.sparse_mla_read_index_error.restype = ctypes.c_int
     lib.sparse_mla_status_string.argtypes = [ctypes.c_int]
@@ -267,6 +270,29 @@ def gather_debug(kv_cache: torch.Tensor, kv_format, page_size: int, slots: torch
                                            int(kv_cache.shape[0]), _ptr(slots), int(n), _ptr(out),
                                            _stream(stream)))
     return out
+
+
+def cache_store(kv_cache: torch.Tensor, kv_format, page_size: int, latent: torch.Tensor,
+                rope: torch.Tensor, slots: torch.Tensor, stream=None) -> None:
+    """Write tokens (bf16 latent [n, 512], bf16 rope [n, 64], int32 slots [n]) into the
+    paged cache in place: FP8 e4m3fn + UE8M0 per 64 elements, or plain bf16."""
+    lib = load_library()
+    dev = kv_cache.device
+    _require(kv_cache, "kv_cache", torch.uint8, dev)
+    _require(latent, "latent", torch.bfloat16, dev)
+    _require(rope, "rope", torch.bfloat16, dev)
+    _require(slots, "slots", torch.int32, dev)
+    kvf = _kv_format_of(kv_format)
+    if kv_cache.dim() != 2 or kv_cache.shape[1] != (648 if kvf == KV_FP8_UE8M0 else 1152) * page_size:
+        raise ValueError("kv_cache must be [num_pages, page_bytes] for this format and page size")
+    n = slots.numel()
+    if tuple(latent.shape) != (n, 512) or tuple(rope.shape) != (n, 64):
+        raise ValueError("latent must be [n, 512] and rope [n, 64]")
+    with torch.cuda.device(dev):
+        _check("sparse_mla_cache_store",
+               lib.sparse_mla_cache_store(_ptr(latent), _ptr(rope), _ptr(slots), int(n), kvf,
+                                          int(page_size), int(kv_cache.shape[0]), _ptr(kv_cache),
+                                          _stream(stream)))
 
 
 def read_index_error(info: PlanInfo, workspace: torch.Tensor, stream=None):

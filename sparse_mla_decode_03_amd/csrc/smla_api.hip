@@ -259,6 +259,27 @@ smla_status sparse_mla_gather_debug(const void* kv_cache, int32_t kv_format, int
   return SMLA_OK;
 }
 
+smla_status sparse_mla_cache_store(const void* latent, const void* rope, const int32_t* slots,
+                                   int32_t num_tokens, int32_t kv_format, int32_t page_size,
+                                   int32_t num_pages, void* kv_cache, void* stream) {
+  if (kv_format != SMLA_KV_BF16 && kv_format != SMLA_KV_FP8_UE8M0) return SMLA_ERR_UNSUPPORTED;
+  const int l = log2_exact(page_size);
+  if (num_tokens < 0 || num_pages < 1 || page_size < 1 || page_size > 1024 || l < 0 ||
+      (int64_t)num_pages * page_size > INT32_MAX)
+    return SMLA_ERR_BAD_SHAPE;
+  if (kv_format == SMLA_KV_FP8_UE8M0 && page_size < 2) return SMLA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return SMLA_OK;
+  if (latent == nullptr || rope == nullptr || slots == nullptr || kv_cache == nullptr)
+    return SMLA_ERR_NULL_ARG;
+  if (!aligned(latent, 16) || !aligned(rope, 16) || !aligned(kv_cache, 16) || !aligned(slots, 4))
+    return SMLA_ERR_MISALIGNED;
+  if (smla::launch_store(reinterpret_cast<const uint16_t*>(latent), reinterpret_cast<const uint16_t*>(rope),
+                         slots, num_tokens, kv_format, l, num_pages * page_size,
+                         reinterpret_cast<uint8_t*>(kv_cache), reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return SMLA_ERR_HIP;
+  return SMLA_OK;
+}
+
 smla_status sparse_mla_read_index_error(const smla_plan* plan, const void* workspace,
                                         int32_t* row_pos, void* stream) {
   const PlanImpl* pi = as_impl(plan);

@@ -31,5 +31,7 @@ hipError_t launch_merge(const float* part_o, const float* part_lse, int R, int S
 hipError_t launch_gather_debug(const uint8_t* kv, int kv_format, int ps_log2, int num_slots,
                                const int* slots, int n, uint16_t* out, hipStream_t st);
 hipError_t launch_fill_u64(unsigned long long* p, unsigned long long v, hipStream_t st);
+hipError_t launch_store(const uint16_t* latent, const uint16_t* rope, const int32_t* slots, int n,
+                        int kv_format, int ps_log2, int num_slots, uint8_t* kv, hipStream_t st);
 
 }  // namespace smla

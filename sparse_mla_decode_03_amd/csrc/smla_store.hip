@@ -1,0 +1,105 @@
+// Cache store for gfx950: new tokens' latent and rope rows into the paged cache.
+//
+// The FP8 format is e4m3fn codes with one UE8M0 scale byte per 64 latent elements and
+// the 64 rope values kept in bf16 (the UE8M0 paged cache named on prhub vllm#43827,
+// motivation and key code excerpts), laid out in region-split pages (latent | rope |
+// scales) addressed inside the page (prhub sglang#24692, implementation breakdown 2).
+// The scale of a group is the smallest power of two 2^(e-127) with 448 * 2^(e-127) >= the
+// group's largest magnitude, so every code is finite; codes are rounded to nearest, ties
+// to even.  One 64-lane wave stores one token: lane l converts latent dims 8l..8l+7, the
+// eight lanes of a 64-element group reduce its maximum, lanes 0..7 copy the rope.
+#include "smla_device.h"
+#include "smla_kernels.h"
+
+namespace smla {
+
+namespace {
+
+// UE8M0 byte for a group maximum `amax` (a non-negative float holding a bf16 value):
+// amax = f * 2^(E - 127) with f in [1, 2) needs 448 * 2^k >= amax, i.e. k = E - 135 when
+// f <= 1.75 (448 = 1.75 * 2^8) and one more otherwise; e = k + 127, clamped to [0, 254].
+// amax = 0 gives 127.
+__device__ __forceinline__ uint32_t ue8m0_for_amax(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  if (b == 0u) return 127u;
+  const int e = (int)(b >> 23) - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return (uint32_t)min(max(e, 0), 254);
+}
+
+// e4m3fn code of a finite v with |v| <= 448, rounded to nearest, ties to even.  Normal
+// range (|v| >= 2^-6): the fp32 mantissa is rounded to 3 bits at bit 20 (a carry moves into
+// the exponent) and the exponent rebiased from 127 to 7.  Below 2^-6 the code is the
+// subnormal step count m = v / 2^-9 (0..8; 8 is the smallest normal, code 0x08).
+__device__ __forceinline__ uint32_t e4m3fn_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x3C800000u) {
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
+  } else {
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  }
+  return ((u >> 24) & 0x80u) | code;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <int FMT>
+__global__ __launch_bounds__(256) void store_kernel(const uint16_t* __restrict__ latent,
+                                                    const uint16_t* __restrict__ rope,
+                                                    const int32_t* __restrict__ slots, int n,
+                                                    int ps_log2, int num_slots, uint8_t* __restrict__ kv) {
+  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (tok >= n) return;                       // the whole wave
+  const int slot = slots[tok];
+  if (slot < 0 || slot >= num_slots) return;  // the whole wave: skipped
+  const SlotAddr sa = slot_addr<FMT>(slot, ps_log2);
+  const u32x4 w = *reinterpret_cast<const u32x4*>(latent + (size_t)tok * 512 + 8 * lane);
+  if (lane < 8)
+    *reinterpret_cast<u32x4*>(kv + sa.rope + 16 * lane) =
+        *reinterpret_cast<const u32x4*>(rope + (size_t)tok * 64 + 8 * lane);
+  if (FMT == 1) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_lo(w[i]);
+      x[2 * i + 1] = bf16_hi(w[i]);
+    }
+    float am = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(x[i]));
+    // the group's eight lanes are lanes 8g .. 8g+7
+    am = fmaxf(am, __shfl_xor(am, 1));
+    am = fmaxf(am, __shfl_xor(am, 2));
+    am = fmaxf(am, __shfl_xor(am, 4));
+    const uint32_t e = ue8m0_for_amax(am);
+    const int sh = 127 - (int)e;              // x * 2^sh is exact
+    uint32_t c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = e4m3fn_rne(__builtin_amdgcn_ldexpf(x[i], sh));
+    *reinterpret_cast<u32x2*>(kv + sa.latent + 8 * lane) =
+        u32x2{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
+    if ((lane & 7) == 0) kv[sa.scales + (lane >> 3)] = (uint8_t)e;
+  } else {
+    *reinterpret_cast<u32x4*>(kv + sa.latent + 16 * lane) = w;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_store(const uint16_t* latent, const uint16_t* rope, const int32_t* slots, int n,
+                        int kv_format, int ps_log2, int num_slots, uint8_t* kv, hipStream_t st) {
+  const unsigned blocks = (unsigned)((n + 3) / 4);
+  if (kv_format == 1)
+    hipLaunchKernelGGL(store_kernel<1>, dim3(blocks), dim3(256), 0, st, latent, rope, slots, n, ps_log2,
+                       num_slots, kv);
+  else
+    hipLaunchKernelGGL(store_kernel<0>, dim3(blocks), dim3(256), 0, st, latent, rope, slots, n, ps_log2,
+                       num_slots, kv);
+  return hipGetLastError();
+}
+
+}  // namespace smla

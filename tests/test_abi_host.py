@@ -190,3 +190,20 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         B.sparse_mla_decode(q, torch.zeros(1, 1, dtype=torch.uint8), torch.zeros(1, 4, dtype=torch.int32),
                             None, None, None, "bf16", 64, 1.0)
+
+
+def test_cache_store_validation(lib):
+    v = ctypes.c_void_p
+    cs = lib.sparse_mla_cache_store
+    # (latent, rope, slots, n, kv_format, page_size, num_pages, kv_cache, stream)
+    assert cs(v(FAKE), v(FAKE), v(FAKE), 4, 7, 64, 10, v(FAKE), None) == B.ERR_UNSUPPORTED
+    assert cs(v(FAKE), v(FAKE), v(FAKE), 4, B.KV_FP8_UE8M0, 1, 10, v(FAKE), None) == B.ERR_UNSUPPORTED
+    assert cs(v(FAKE), v(FAKE), v(FAKE), -1, B.KV_BF16, 64, 10, v(FAKE), None) == B.ERR_BAD_SHAPE
+    assert cs(v(FAKE), v(FAKE), v(FAKE), 4, B.KV_BF16, 48, 10, v(FAKE), None) == B.ERR_BAD_SHAPE
+    assert cs(v(FAKE), v(FAKE), v(FAKE), 4, B.KV_BF16, 64, 0, v(FAKE), None) == B.ERR_BAD_SHAPE
+    assert cs(None, v(FAKE), v(FAKE), 4, B.KV_BF16, 64, 10, v(FAKE), None) == B.ERR_NULL_ARG
+    assert cs(v(FAKE), v(FAKE), v(FAKE), 4, B.KV_BF16, 64, 10, None, None) == B.ERR_NULL_ARG
+    assert cs(v(FAKE + 8), v(FAKE), v(FAKE), 4, B.KV_BF16, 64, 10, v(FAKE), None) == B.ERR_MISALIGNED
+    assert cs(v(FAKE), v(FAKE), v(FAKE + 2), 4, B.KV_BF16, 64, 10, v(FAKE), None) == B.ERR_MISALIGNED
+    # zero tokens: nothing launched, pointers not checked
+    assert cs(None, None, None, 0, B.KV_FP8_UE8M0, 64, 10, None, None) == B.OK
