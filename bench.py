@@ -59,6 +59,39 @@ def pmc_traffic(launch_units: int):
     return fetch + write
 
 
+def cache_store_measure(B, torch, dev, n_tokens: int, reps: int):
+    """Time sparse_mla_cache_store (FP8 + UE8M0, page size 64) writing n_tokens new tokens
+    to distinct random slots of a pool twice their size.  Algorithmic bytes per token:
+    1024 (bf16 latent) + 128 (bf16 rope) + 4 (slot) read, 512 + 128 + 8 written."""
+    ps = 64
+    npages = max(2, 2 * n_tokens // ps)
+    g = torch.Generator(device=dev).manual_seed(17)
+    cache = torch.zeros((npages, 648 * ps), dtype=torch.uint8, device=dev)
+    lat = torch.randn((n_tokens, 512), generator=g, device=dev).to(torch.bfloat16)
+    rope = torch.randn((n_tokens, 64), generator=g, device=dev).to(torch.bfloat16)
+    slots = torch.randperm(npages * ps, generator=g, device=dev)[:n_tokens].to(torch.int32)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        B.cache_store(cache, "fp8", ps, lat, rope, slots, stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        B.cache_store(cache, "fp8", ps, lat, rope, slots, stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    mean_s = sum(ms) / len(ms) / 1e3
+    nbytes = n_tokens * (1024 + 128 + 4 + 512 + 128 + 8)
+    return {"tokens": n_tokens, "page_size": ps, "pages": npages,
+            "launch_ms_mean": mean_s * 1e3, "launch_ms_p50": ms[len(ms) // 2],
+            "tokens_per_s": n_tokens / mean_s,
+            "roofline": {"bound": "hbm", "achieved": nbytes / mean_s / 1e9,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": nbytes / mean_s / 1e9 / PEAK_HBM_GBS,
+                         "bytes_per_launch": nbytes}}
+
+
 def cpu_baseline(inp, budget_s: float):
     """Time the float64 oracle on whole rows of the same workload until about budget_s
     of CPU work has been done."""
@@ -112,6 +145,8 @@ def main() -> int:
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra launches, each after a 1 GiB scratch write that evicts the "
                          "caches (L2 and the 256 MB MALL); reported beside the warm figure")
+    ap.add_argument("--store-tokens", type=int, default=65536,
+                    help="tokens per timed cache-store launch (0: skip that measurement)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run only a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -243,6 +278,8 @@ def main() -> int:
             "flops_per_launch": flops,
         },
     }
+    if args.store_tokens > 0:
+        res["cache_store"] = cache_store_measure(B, torch, dev, args.store_tokens, 20)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
     print(json.dumps(res), flush=True)

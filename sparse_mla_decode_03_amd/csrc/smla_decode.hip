@@ -41,6 +41,7 @@ constexpr int kDepthV = 3;              // LDS operand load pairs kept in flight
 // workgroup repeats the pass over the row with the larger reference; fp32 and bf16 hold
 // P <= 2^32 without overflow.
 constexpr float kRestartLog2 = 32.0f;
+constexpr unsigned kRestartBits = 0x4F800000u;   // bit pattern of 2^kRestartLog2
 
 // K tile layout.  LDS serves 64 banks of 4 bytes: 16 lanes per cycle for 16-byte reads
 // and 32 lanes per cycle for 8-byte (and transpose) reads.  Latent rows are 1024 bytes of
@@ -247,6 +248,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   wait_vm();
 
   float m_used = -INFINITY;
+  bool have_ref = false;   // some tile has set m_used (block uniform)
+  bool careful = false;    // a repeated pass: every tile checks its max before the exps
 
   // ---- 2. gather (see Cfg for the DMA instruction map).  Every DMA instruction of a
   // tile is issued, also for tokens past the valid count (they read a dummy address in
@@ -573,8 +576,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(poff[i]));
     }
+    // PV steps run k-step major: step = 16 * s2 + b
     auto vaddr = [&](int step, int hh) {
-      const int b = step >> 1, s2 = step & 1;
+      const int b = step & 15, s2 = step >> 4;
       return reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(sK) + poff[(b & 3) * 2 + hh] +
                                                2 * (8192 * s2 + 128 * (b >> 2)));
     };
@@ -584,67 +588,99 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       vq[i][0] = lds_read_tr16(vaddr(i, 0));
       vq[i][1] = lds_read_tr16(vaddr(i, 1));
     }
-
-    // ---- 4. softmax (exp2 domain) against a per-head reference max m_used ------------
-    // Full tiles with a positive scale (the usual case) need no masking, and the scale
-    // is folded into one multiply of the max and one FMA per score.
-    const bool fast = nt == kT && a.scale_log2 > 0.f;   // wave uniform
-    float mx;
-    if (fast) {
-      float m8[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) m8[r] = fmaxf(s[2 * r], s[2 * r + 1]);
-      mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])), fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
-      mx *= a.scale_log2;
-    } else {
-      mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = (acc_row(r, G) < nt) ? s[r] * a.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, s[r]);
-      }
-    }
-    mx = max_halves(mx);
-    if (m_used == -INFINITY) m_used = mx;       // first tile: O and l are still zero
-    if (mx > m_used + kRestartLog2) {           // rare: raise the reference and restart
-      m_used = mx;
-      sRestart = 1;
-    }
-    if (fast) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, -m_used));
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = (s[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[r] - m_used);
-    }
-    {
-      float p8[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) p8[r] = s[2 * r] + s[2 * r + 1];
-      l_part += ((p8[0] + p8[1]) + (p8[2] + p8[3])) + ((p8[4] + p8[5]) + (p8[6] + p8[7]));
-    }
-    // P as the PV A operand: k-step s2 uses the lane's tokens acc_row(8*s2 + kk, G)
-    u32x4 pa[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-      pa[s2] = u32x4{pack_bf16x2(s[8 * s2 + 0], s[8 * s2 + 1]), pack_bf16x2(s[8 * s2 + 2], s[8 * s2 + 3]),
-                     pack_bf16x2(s[8 * s2 + 4], s[8 * s2 + 5]), pack_bf16x2(s[8 * s2 + 6], s[8 * s2 + 7])};
-
-    // ---- 5. PV: O[head][dv] += P[head][token] V[token][dv] ---------------------------
-#pragma unroll
-    for (int step = 0; step < 32; ++step) {
+    // O^T[dv][head] += V^T[dv][token] P^T[token][head]: the V registers are the A operand
+    // (rows = dv) and P the B operand (columns = heads), so each lane's accumulator holds
+    // one head and runs of four consecutive dv.
+    auto pv_step = [&](int step, const u32x4& p) {
       const u32x2 v0 = vq[step % kDepthV][0];
       const u32x2 v1 = vq[step % kDepthV][1];
       if (step + kDepthV < 32) {
         vq[step % kDepthV][0] = lds_read_tr16(vaddr(step + kDepthV, 0));
         vq[step % kDepthV][1] = lds_read_tr16(vaddr(step + kDepthV, 1));
       }
-      // O^T[dv][head] += V^T[dv][token] P^T[token][head]: the V registers are the A operand
-      // (rows = dv) and P the B operand (columns = heads), so each lane's accumulator holds
-      // one head and runs of four consecutive dv.
-      O[step >> 1] = mfma32x32x16(u32x4{v0[0], v0[1], v1[0], v1[1]}, pa[step & 1], O[step >> 1]);
+      O[step & 15] = mfma32x32x16(u32x4{v0[0], v0[1], v1[0], v1[1]}, p, O[step & 15]);
+    };
+    auto pack8 = [&](int s2) {
+      return u32x4{pack_bf16x2(s[8 * s2 + 0], s[8 * s2 + 1]), pack_bf16x2(s[8 * s2 + 2], s[8 * s2 + 3]),
+                   pack_bf16x2(s[8 * s2 + 4], s[8 * s2 + 5]), pack_bf16x2(s[8 * s2 + 6], s[8 * s2 + 7])};
+    };
+
+    // ---- 4./5. softmax (exp2 domain) against a per-head reference max m_used, and PV ---
+    // P as the PV B operand: k-step s2 uses the lane's tokens acc_row(8*s2 + kk, G).
+    // Each probability is exp2(fma(x, ce, -me)).  In the steady state (a full tile, a
+    // reference from earlier tiles, a positive scale) x is the raw score, ce the scale
+    // and me the reference, and nothing precedes the exps: k-step 0's probabilities come
+    // first and the rest of the softmax (k-step 1's probabilities, the row sum, the
+    // overflow check) runs inside k-step 0's MFMAs.  A probability above 2^kRestartLog2
+    // means a score beyond the reference: the pass is repeated on the careful path.
+    // Otherwise (the first tile, a partial tile, a repeated pass) the tile's max is taken
+    // first and may raise the reference; x is then the scaled, masked score minus the
+    // reference, with ce = 1 and me = 0.
+    const bool steady = have_ref && !careful && nt == kT && a.scale_log2 > 0.f;   // uniform
+    float ce = a.scale_log2, me = m_used;
+    if (!steady) {
+      float mx;
+      const bool full = nt == kT && a.scale_log2 > 0.f;   // wave uniform
+      if (full) {
+        float m8[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) m8[r] = fmaxf(s[2 * r], s[2 * r + 1]);
+        mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])), fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+        mx *= a.scale_log2;
+      } else {
+        mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[r] = (acc_row(r, G) < nt) ? s[r] * a.scale_log2 : -INFINITY;
+          mx = fmaxf(mx, s[r]);
+        }
+      }
+      mx = max_halves(mx);
+      if (m_used == -INFINITY) m_used = mx;       // first tile: O and l are still zero
+      if (mx > m_used + kRestartLog2) {           // rare: raise the reference and restart
+        m_used = mx;
+        sRestart = 1;
+      }
+      if (full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = __builtin_fmaf(s[r], a.scale_log2, -m_used);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = s[r] - m_used;    // -inf stays -inf
+      }
+      ce = 1.f;
+      me = 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], ce, -me));
+    const u32x4 p0 = pack8(0);
+    u32x4 p1;
+    unsigned pbits = 0;
+#pragma unroll
+    for (int step = 0; step < 16; ++step) {
+      pv_step(step, p0);
+      if (step < 8) s[8 + step] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 + step], ce, -me));
+      if (step == 8) p1 = pack8(1);
+      if (step == 10) {
+        float p8[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) p8[r] = s[2 * r] + s[2 * r + 1];
+        l_part += ((p8[0] + p8[1]) + (p8[2] + p8[3])) + ((p8[4] + p8[5]) + (p8[6] + p8[7]));
+      }
+      if (step == 12) {
+        // probabilities are >= 0, so their bit patterns order like their values
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pbits = max(pbits, __float_as_uint(s[r]));
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int step = 16; step < 32; ++step) {
+      pv_step(step, p1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (pbits > kRestartBits) sRestart = 1;
+    have_ref = true;
 
     // ---- next tile: finish its gather -------------------------------------------------
     if (has_next) {
@@ -669,6 +705,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     __syncthreads();
     if (sRestart) {  // the same value in every thread: it was written before the barrier
       restart = true;
+      careful = true;
       break;
     }
   }

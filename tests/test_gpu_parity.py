@@ -295,3 +295,37 @@ def test_small_topk_with_strong_sinks(topk, sink):
         idx[0, 0] = -1
         od, _ = oracle_decode(inp, sinks=sinks, indices=idx)
         assert np.abs(od[0] - o[0]).max() > 2e-2
+
+
+@pytest.mark.parametrize("fmt,alpha", [("fp8", 20.0), ("fp8", 40.0), ("bf16", 40.0)])
+def test_score_far_above_the_first_tiles(fmt, alpha):
+    """One entry in a later tile whose rope part is alpha times head j's rope query: its
+    score lies far above everything the kernel saw in the first tile, so the reference
+    max must be raised and the pass repeated.  alpha = 40 puts the excess past the fp32
+    range of exp2 (the probability computed against the old reference is +inf)."""
+    from oracle import cache_store_oracle as cso
+    inp = _small(fmt=fmt, heads=32, topk=256, nreq=2, rows=(1, 1), ctx=(700, 900), seed=91)
+    ps, j, t = inp.spec.page_size, 5, 5 * 32 + 3
+    pos = int(inp.indices[0, t])
+    page = int(inp.page_table[int(inp.row_req[0]), pos // ps])
+    slot = page * ps + pos % ps
+    qb = inp.q[0, j].float()
+    rope = (alpha * qb[512:]).to(torch.bfloat16)
+    lat = torch.randn((1, 512), generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    bits = lambda x: x.contiguous().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+    cache = cso.cache_store(inp.kv_cache.cpu().numpy(), KV[fmt], ps, bits(lat), bits(rope[None]),
+                            np.array([slot]))
+    inp.kv_cache = torch.from_numpy(cache)
+    # precondition: in log2 units the spike exceeds every score of row 0's first tile
+    c = inp.spec.softmax_scale / np.log(2.0)
+    rows = orc.decode_entries(cache, KV[fmt], ps, np.array([
+        int(inp.page_table[int(inp.row_req[0]), int(p) // ps]) * ps + int(p) % ps
+        for p in inp.indices[0, :32].tolist()] + [slot]))
+    qd = inp.q[0, j].double().numpy()
+    first = (rows[:32] @ qd).max() * c
+    spike = float(rows[32] @ qd) * c
+    assert spike - first > (120.0 if alpha >= 40 else 40.0), (spike, first)
+    announce(f"restart {fmt} alpha={alpha} excess={spike - first:.1f}")
+    out, lse = gpu_decode(inp)
+    o, l = oracle_decode(inp)
+    compare(out, lse, o, l, what=f"restart {fmt} alpha={alpha}")
