@@ -64,6 +64,9 @@
  *     or page ids outside [0, num_pages)) are never dereferenced: the kernel treats
  *     them as -1.  With SMLA_F_CHECK_INDICES the first such (row, position) is also
  *     recorded in the workspace and can be read with sparse_mla_read_index_error.
+ *   - Non-finite q or cache values give unspecified output and LSE for the (row, head)
+ *     pairs whose scores or values they reach; every call still completes, and the other
+ *     pairs are unaffected.
  *   - The plan is plain host memory, independent of any data, and may be reused across
  *     calls and graph replays.  The library keeps no mutable global state beyond a
  *     per-device attribute cache filled once.

@@ -42,6 +42,7 @@ constexpr int kDepthV = 3;              // LDS operand load pairs kept in flight
 // P <= 2^32 without overflow.
 constexpr float kRestartLog2 = 32.0f;
 constexpr unsigned kRestartBits = 0x4F800000u;   // bit pattern of 2^kRestartLog2
+constexpr unsigned kInfBits = 0x7F800000u;       // bit pattern of +inf
 
 // K tile layout.  LDS serves 64 banks of 4 bytes: 16 lanes per cycle for 16-byte reads
 // and 32 lanes per cycle for 8-byte (and transpose) reads.  Latent rows are 1024 bytes of
@@ -679,7 +680,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       pv_step(step, p1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (pbits > kRestartBits) sRestart = 1;
+    // +inf counts (a score past the fp32 range of exp2 against this reference); NaN,
+    // whose patterns lie above +inf's, does not: a NaN score must not repeat the pass.
+    if (steady && pbits > kRestartBits && pbits <= kInfBits) sRestart = 1;
     have_ref = true;
 
     // ---- next tile: finish its gather -------------------------------------------------

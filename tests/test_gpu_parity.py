@@ -329,3 +329,38 @@ def test_score_far_above_the_first_tiles(fmt, alpha):
     out, lse = gpu_decode(inp)
     o, l = oracle_decode(inp)
     compare(out, lse, o, l, what=f"restart {fmt} alpha={alpha}")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "bf16"])
+def test_non_finite_inputs_complete_and_stay_local(fmt):
+    """A NaN query element and a cache entry with +inf rope values: the call completes
+    (neither can make the row's pass repeat forever) and every (row, head) whose result
+    the oracle finds finite matches it."""
+    from oracle import cache_store_oracle as cso
+    inp = _small(fmt=fmt, heads=32, topk=256, nreq=3, rows=(1, 2), ctx=(700, 900), seed=93)
+    ps = inp.spec.page_size
+    q = inp.q.clone()
+    q[0, 3, 100] = float("nan")
+    inp.q = q
+    r = inp.num_rows - 1                         # a row of another request than row 0's
+    assert int(inp.row_req[r]) != int(inp.row_req[0])
+    pos = int(inp.indices[r, 6 * 32 + 1])
+    page = int(inp.page_table[int(inp.row_req[r]), pos // ps])
+    lat = torch.randn((1, 512), generator=torch.Generator().manual_seed(6)).to(torch.bfloat16)
+    rope = torch.full((1, 64), float("inf")).to(torch.bfloat16)
+    bits = lambda x: x.contiguous().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+    inp.kv_cache = torch.from_numpy(cso.cache_store(inp.kv_cache.cpu().numpy(), KV[fmt], ps, bits(lat),
+                                                    bits(rope), np.array([page * ps + pos % ps])))
+    announce(f"non-finite inputs {fmt}")
+    out, lse = gpu_decode(inp)
+    torch.cuda.synchronize()
+    with np.errstate(invalid="ignore", over="ignore"):
+        o, l = oracle_decode(inp)
+    ok = np.isfinite(o).all(axis=-1) & np.isfinite(l)
+    # row 0 loses only head 3; the rows that select the +inf entry lose every head
+    assert not ok[0, 3] and ok[0].sum() == 31 and ok.sum() >= 31 + 32
+    got = out.float().cpu().double().numpy()
+    d = np.abs(got[ok] - o[ok])
+    assert d.max() <= 2e-2 and d.mean() <= 2e-3
+    lg = lse.cpu().double().numpy()
+    assert np.all(np.abs(lg[ok] - l[ok]) <= 1e-3 * np.maximum(1.0, np.abs(l[ok])))
