@@ -377,8 +377,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // 16c..16c+15 (c = lane % 32) goes to swizzled chunks 2c and 2c + 1 of row t, and
   // (2c ^ swz(t)) = (2c ^ 4G) ^ U(i) with U(i) = 8(i % 2) + (i / 2) % 4; rope instruction r
   // puts token 8r + lane / 8, chunk lane % 8, at chunk (lane % 8) ^ (lane / 16) ^ 4(r % 2).
+  // The lanes with bit 3 of c set convert and write the second 16-byte half of their
+  // unit first (they load the two 8-byte halves of the raw unit swapped): each 16-byte
+  // write then covers 16 different chunk slots per 16 lanes instead of every other one.
   struct DqBase {
-    int raw;    // byte offset into sRaw of this lane's unit of instruction `wave`
+    int raw;    // byte offset into sRaw of the half of this lane's unit written first
     int scl;    // byte offset into sScl of this lane's scale byte for instruction `wave`
     int lat;    // lane part of the latent write offset (bits 4..10)
     int rope;   // lane part of the rope write offset (bits 4..9)
@@ -387,9 +390,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   auto dq_base = [&](int tile, int ln) {
     DqBase d;
     const int G_ = ln >> 5, c = ln & 31;
-    d.raw = (C::NS > 0 ? tile % C::NS : 0) * (20 * 1024) + wave * 1024 + 16 * ln;
+    d.raw = (C::NS > 0 ? tile % C::NS : 0) * (20 * 1024) + wave * 1024 + 16 * ln + 8 * ((c >> 3) & 1);
     d.scl = (tile % (C::NS + 1)) * 256 + 16 * wave + 8 * G_ + (c >> 2);
-    d.lat = 1024 * G_ + ((32 * c) ^ (64 * G_));
+    d.lat = 1024 * G_ + ((32 * c) ^ (64 * G_) ^ (16 * ((c >> 3) & 1)));
     d.rope = 128 * (ln >> 3) + 16 * ((ln & 7) ^ (ln >> 4));
     d.kb = 2 * kbuf_of(tile) * kTile;
     return d;
@@ -401,10 +404,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   auto finish_load = [&](int j, const DqBase& d) {
     RawUnit u;
     if (j < LP) {
-      u.rv = *reinterpret_cast<const u32x4*>(sRaw + d.raw + NW * j * 1024);
+      const u32x2 first = *reinterpret_cast<const u32x2*>(sRaw + d.raw + NW * j * 1024);
+      const u32x2 second = *reinterpret_cast<const u32x2*>(sRaw + (d.raw ^ 8) + NW * j * 1024);
+      u.rv = u32x4{first[0], first[1], second[0], second[1]};
       u.e = sScl[d.scl + 16 * NW * j];
     } else {
-      u.rv = *reinterpret_cast<const u32x4*>(sRaw + d.raw + (16 + NW * (j - LP)) * 1024);
+      u.rv = *reinterpret_cast<const u32x4*>(sRaw + (d.raw & ~15) + (16 + NW * (j - LP)) * 1024);
       u.e = 0u;
     }
     return u;
@@ -422,6 +427,21 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     } else {
       const int r = wave + NW * (j - LP);
       if (r < 4) *reinterpret_cast<u32x4*>(Kb + 2 * kRopeOff + 1024 * r + (d.rope ^ (64 * (r & 1)))) = u.rv;
+    }
+  };
+  // One quarter q of latent part j: the bf16 pairs of raw dword q go to `half`; after the
+  // odd quarters a 16-byte half of the unit is written.
+  auto finish_quarter = [&](int j, int q, const RawUnit& u, u32x4& half, const DqBase& d) {
+    const int ins = wave + NW * j;
+    if (ins < C::NL) {
+      const float sc = ue8m0_scale(u.e);
+      half[2 * (q & 1)] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.rv[q], sc, false));
+      half[2 * (q & 1) + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.rv[q], sc, true));
+      if (q & 1) {
+        uint8_t* Kb = reinterpret_cast<uint8_t*>(sK) + d.kb;
+        const int U16 = 16 * (((ins & 1) << 3) | ((ins >> 1) & 3));
+        *reinterpret_cast<u32x4*>(Kb + 2048 * ins + (d.lat ^ U16 ^ (q == 3 ? 16 : 0))) = half;
+      }
     }
   };
   // After this lane's copies of `tile` have landed: FP8 dequantizes the units it copied
@@ -500,6 +520,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     // issued inside QK, after the wait).  Past the last tile this converts the copies of
     // positions past the end into a buffer nobody reads.
     constexpr bool kWeave = FMT == 1 && C::NK > 1;
+    constexpr bool kFine = (LP + RP) * 6 <= 36 && (C::NS == 0 || 1 + 6 * (NDMA - 1) < 36);
     if (kWeave) wait_next();
     // slots of the tile copied during this one
     int sl[NDMA];
@@ -531,6 +552,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       };
       u32x4 kq[kDepth];
       RawUnit un;
+      u32x4 half;
       const DqBase dq = dq_base(tile + 1, ln);
 #pragma unroll
       for (int i = 0; i < kDepth; ++i) kq[i] = kload(i);
@@ -544,14 +566,28 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         if (C::NS > 0) {
 #pragma unroll
           for (int j = 0; j < NDMA; ++j)
-            if (ks == 2 + (j * 33) / NDMA) issue_part(tile + C::NS, j, sl, ln);
+            if (ks == (kFine ? 1 + 6 * j : 2 + (j * 33) / NDMA)) issue_part(tile + C::NS, j, sl, ln);
         }
-        // dequantization part j of tile + 1: loaded two MFMAs before it is written
+        // dequantization part j of tile + 1.  With few parts per wave (kFine) each latent
+        // part is loaded at step 6j and converted a quarter per step at 6j+2 .. 6j+5, so
+        // no step carries more than two conversions beside its MFMA; the copies sit on the
+        // steps between.  Otherwise a part is loaded two MFMAs before it is written.
         if (kWeave) {
 #pragma unroll
           for (int j = 0; j < LP + RP; ++j) {
-            if (ks == 3 + (j * 30) / (LP + RP)) un = finish_load(j, dq);
-            if (ks == 5 + (j * 30) / (LP + RP)) finish_part(j, un, dq);
+            if constexpr (kFine) {
+              if (ks == 6 * j) un = finish_load(j, dq);
+              if (j < LP) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                  if (ks == 6 * j + 2 + q) finish_quarter(j, q, un, half, dq);
+              } else if (ks == 6 * j + 2) {
+                finish_part(j, un, dq);
+              }
+            } else {
+              if (ks == 3 + (j * 30) / (LP + RP)) un = finish_load(j, dq);
+              if (ks == 5 + (j * 30) / (LP + RP)) finish_part(j, un, dq);
+            }
           }
         }
         __builtin_amdgcn_sched_barrier(0);
