@@ -1,4 +1,5 @@
-"""Float64 CPU oracle for the sparse MLA decode path and the cache store before it.
+"""Float64 CPU oracle for the sparse MLA decode path, the cache store before it and the
+indexer that produces its index lists.
 
 TEST INFRASTRUCTURE: only tests/, the smoke check in __graft_entry__ and the
 cpu_baseline leg of bench.py may import it.  The library never does; it shares no
@@ -31,4 +32,13 @@ from .cache_store_oracle import (  # noqa: F401,E402
     e4m3fn_nearest,
     quantize_fp8_ue8m0,
     ue8m0_for_amax,
+)
+from .indexer_oracle import (  # noqa: F401,E402
+    INDEX_DIM,
+    KEY_BYTES,
+    decode_keys,
+    indexer_logits,
+    indexer_topk,
+    key_page_bytes,
+    row_slots,
 )

@@ -258,3 +258,134 @@ def compulsory_bytes(inp: Inputs) -> int:
 def algorithmic_flops(inp: Inputs) -> int:
     """2*H*(576+512) per attended entry: the QK and PV contractions."""
     return 2 * inp.num_heads * (WIDTH + LATENT) * inp.num_valid()
+
+
+# ---------------------------------------------------------------------------------------
+# Indexer inputs: FP8 index keys (128 e4m3fn codes + an fp32 scale per token, paged like
+# the latent cache), FP8 index queries and fp32 per-head weights, next_n rows per request.
+# ---------------------------------------------------------------------------------------
+
+INDEX_DIM = 128
+
+
+@dataclass(frozen=True)
+class IndexerSpec:
+    name: str
+    num_requests: int
+    next_n: int
+    num_heads: int
+    topk: int
+    ctx_lo: int
+    ctx_hi: int
+    page_size: int = 64
+    permute_pages: bool = True
+
+    def scaled(self, **kw) -> "IndexerSpec":
+        return dataclasses.replace(self, **kw)
+
+
+INDEXER_WORKLOADS = {
+    # the index lists of the headline decode workload: 128 requests x 4 MTP rows
+    "idx_b128_mtp4_h64": IndexerSpec("idx_b128_mtp4_h64", 128, 4, 64, 2048, 8192, 131072),
+    "idx_b32_n1_h64": IndexerSpec("idx_b32_n1_h64", 32, 1, 64, 2048, 4096, 32768),
+    "idx_small": IndexerSpec("idx_small", 3, 2, 64, 256, 200, 1500),
+}
+
+
+@dataclass
+class IndexerInputs:
+    spec: IndexerSpec
+    q_codes: torch.Tensor            # uint8 [R, H, 128] e4m3fn
+    weights: torch.Tensor            # fp32 [R, H]
+    key_cache: torch.Tensor          # uint8 [num_pages, 132 * page_size]
+    row_req: torch.Tensor            # int32 [R]
+    row_len: torch.Tensor            # int32 [R]: positions 0 .. len-1 are visible
+    page_table: torch.Tensor         # int32 [B, max_pages]
+    context_lens: torch.Tensor       # int32 [B]
+    width: int                       # logits row stride (>= max row_len, multiple of 64)
+
+    @property
+    def num_rows(self) -> int:
+        return int(self.q_codes.shape[0])
+
+
+def encode_keys(x: torch.Tensor):
+    """float32 keys [n, 128] -> e4m3fn codes [n, 128] and fp32 scales [n] (amax / 448,
+    1 for an all-zero key)."""
+    amax = x.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    codes = (x / scale[:, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, scale.to(torch.float32)
+
+
+def pack_key_pages(codes: torch.Tensor, scales: torch.Tensor, page_size: int) -> torch.Tensor:
+    """Region-split key pages: codes [ps][128] | scales fp32 [ps]."""
+    n = codes.shape[0]
+    assert n % page_size == 0
+    npg = n // page_size
+    out = torch.empty((npg, (INDEX_DIM + 4) * page_size), dtype=torch.uint8, device=codes.device)
+    out[:, : INDEX_DIM * page_size] = codes.reshape(npg, INDEX_DIM * page_size)
+    out[:, INDEX_DIM * page_size:] = scales.contiguous().view(torch.uint8).reshape(npg, 4 * page_size)
+    return out
+
+
+def make_key_cache(num_pages: int, page_size: int, seed: int, device="cpu",
+                   chunk_pages: int = 4096) -> torch.Tensor:
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) + 7919)
+    cache = torch.empty((num_pages, (INDEX_DIM + 4) * page_size), dtype=torch.uint8, device=device)
+    for p0 in range(0, num_pages, chunk_pages):
+        p1 = min(num_pages, p0 + chunk_pages)
+        x = torch.randn(((p1 - p0) * page_size, INDEX_DIM), generator=gen, device=device,
+                        dtype=torch.float32)
+        codes, scales = encode_keys(x)
+        cache[p0:p1] = pack_key_pages(codes, scales, page_size)
+    return cache
+
+
+def make_indexer_inputs(spec: IndexerSpec, seed: int, device="cpu", cache_device=None) -> IndexerInputs:
+    """Requests with contexts U[ctx_lo, ctx_hi]; row i of a request's next_n rows sees
+    positions 0 .. ctx - next_n + i (the MTP rows are the request's last next_n tokens).
+    Queries N(0,1) cast to e4m3fn, weights N(0,1)/sqrt(H), keys N(0,1) quantized per token."""
+    cache_device = device if cache_device is None else cache_device
+    rng = np.random.default_rng(seed)
+    B, ps, nn, H = spec.num_requests, spec.page_size, spec.next_n, spec.num_heads
+    ctx = rng.integers(spec.ctx_lo, spec.ctx_hi + 1, size=B)
+    pages_per_req = -(-ctx // ps)
+    num_pages = int(pages_per_req.sum())
+    perm = rng.permutation(num_pages) if spec.permute_pages else np.arange(num_pages)
+    page_table = np.full((B, int(pages_per_req.max())), -1, dtype=np.int32)
+    start = 0
+    for b in range(B):
+        page_table[b, : pages_per_req[b]] = perm[start: start + pages_per_req[b]]
+        start += pages_per_req[b]
+    R = B * nn
+    row_req = np.repeat(np.arange(B, dtype=np.int32), nn)
+    row_len = np.array([ctx[b] - (nn - 1 - i) for b in range(B) for i in range(nn)], dtype=np.int32)
+    q = torch.from_numpy(rng.standard_normal(size=(R, H, INDEX_DIM), dtype=np.float32))
+    q_codes = q.to(torch.float8_e4m3fn).view(torch.uint8)
+    weights = torch.from_numpy((rng.standard_normal(size=(R, H)) / math.sqrt(H)).astype(np.float32))
+    width = int(-(-int(row_len.max()) // 64) * 64)
+    cache = make_key_cache(num_pages, ps, seed, device=cache_device)
+    mv = lambda t: t.to(device)  # noqa: E731
+    return IndexerInputs(spec, mv(q_codes), mv(weights), cache, mv(torch.from_numpy(row_req)),
+                         mv(torch.from_numpy(row_len)), mv(torch.from_numpy(page_table)),
+                         mv(torch.from_numpy(ctx.astype(np.int32))), width)
+
+
+def indexer_algorithmic_bytes(inp: IndexerInputs) -> int:
+    """Each request's keys read once (132 B per position up to its longest row), the
+    queries (128 B per head) and weights (4 B per head) of every row, the page-table rows,
+    and the logits written (4 B per visible position)."""
+    lens = inp.row_len.cpu().numpy().astype(np.int64)
+    rr = inp.row_req.cpu().numpy()
+    per_req = np.zeros(inp.spec.num_requests, dtype=np.int64)
+    np.maximum.at(per_req, rr, lens)
+    H = inp.spec.num_heads
+    return int(per_req.sum() * 132 + inp.num_rows * H * 132
+               + (-(-per_req // inp.spec.page_size)).sum() * 4 + lens.sum() * 4)
+
+
+def indexer_algorithmic_flops(inp: IndexerInputs) -> int:
+    """2 * H * 128 per (row, visible position)."""
+    return int(2 * inp.spec.num_heads * INDEX_DIM * inp.row_len.cpu().numpy().astype(np.int64).sum())
