@@ -208,6 +208,41 @@ smla_status sparse_mla_cache_store(const void* latent, const void* rope, const i
                                    int32_t num_tokens, int32_t kv_format, int32_t page_size,
                                    int32_t num_pages, void* kv_cache, void* stream);
 
+/* Indexer, the step that produces the index lists: FP8 paged MQA logits of every query
+ * row over its context (the indexer's fp8_paged_mqa_logits on prhub sglang#24692,
+ * implementation breakdown item 5; next_n rows of a request served natively, so each key
+ * page is read once for all of them, per-row context lengths: prhub vllm#52164,
+ * implementation breakdown items 1-5).  With e = e4m3fn decode:
+ *   logits[r][t] = sum_h weights[r][h] * max(0, scale_t * sum_d e(q[r][h][d]) * e(code_t[d]))
+ * for 0 <= t < min(row_len[r], width); positions t >= min(row_len[r], width) are not
+ * written.  Positions are request-local and translated through page_table as on the decode
+ * path; a position whose page id is outside [0, num_pages) gets -inf.
+ *   q_codes   e4m3fn [R][64][128], R = num_requests * next_n rows, request-major (row
+ *             b*next_n + i is row i of request b)                    (device, 16 B aligned)
+ *   weights   fp32 [R][64] (any query scale folded in)                (device, 16 B aligned)
+ *   key_cache num_pages pages of 132*page_size bytes: codes e4m3fn [page_size][128], then
+ *             fp32 scales [page_size]; scales must be >= 0 (quantization scales)
+ *   row_len   int32 [R]; page_table int32 [num_requests][max_pages]
+ *   logits    fp32 [R][width] (caller-owned, 16 B aligned); width a multiple of 64 and
+ *             max_pages * 64 >= width
+ * Supported: num_heads = 64, page_size = 64, next_n 1..4.  No allocation; asynchronous.
+ * Errors: UNSUPPORTED, BAD_SHAPE, NULL_ARG, MISALIGNED, HIP. */
+smla_status sparse_mla_indexer_logits(const void* q_codes, const float* weights, const void* key_cache,
+                                      const int32_t* row_len, const int32_t* page_table,
+                                      int32_t num_requests, int32_t next_n, int32_t num_heads,
+                                      int32_t page_size, int32_t num_pages, int32_t max_pages,
+                                      int32_t width, float* logits, void* stream);
+
+/* Top-k of the indexer logits (the selection that yields the decode path's index lists,
+ * same passages as above): for each row r, with n = min(row_len[r], width), the topk
+ * positions t < n of largest logits[r][t], a tie at the boundary going to the smaller
+ * position, written to indices[r][0..topk) in ascending position order; with n <= topk,
+ * positions 0..n-1 and then -1.  NaN logits give an unspecified selection.
+ *   logits fp32 [rows][width]; row_len int32 [rows]; indices int32 [rows][topk]
+ * No allocation; asynchronous.  Errors: BAD_SHAPE, NULL_ARG, MISALIGNED, HIP. */
+smla_status sparse_mla_indexer_topk(const float* logits, const int32_t* row_len, int32_t rows,
+                                    int32_t width, int32_t topk, int32_t* indices, void* stream);
+
 /* Test helper: decode n cache slots (global slot numbers, device int32 [n]) into bf16
  * rows out[n][576] with the same device code the decode kernel uses for its gather and
  * dequantisation.  Slots outside [0, num_pages*page_size) give a zero row.

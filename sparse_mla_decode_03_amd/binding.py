@@ -40,6 +40,8 @@ EXPORTED = [
     "sparse_mla_merge_partials", "sparse_mla_gather_debug", "sparse_mla_read_index_error",
     "sparse_mla_cache_store",
     "sparse_mla_status_string", "sparse_mla_version",
+    "sparse_mla_indexer_logits",
+    "sparse_mla_indexer_topk",
 ]
 
 
@@ -88,6 +90,9 @@ def load_library(path: str = LIB_PATH):
     lib.sparse_mla_gather_debug.argtypes = [vp, i32, i32, i32, i32p, i32, vp, vp]
     lib.sparse_mla_gather_debug.restype = ctypes.c_int
     lib.sparse_mla_cache_store.argtypes = [vp, vp, i32p, i32, i32, i32, i32, vp, vp]
+    lib.sparse_mla_indexer_logits.argtypes = [vp, f32p, vp, i32p, i32p, i32, i32, i32, i32, i32, i32,
+                                              i32, f32p, vp]
+    lib.sparse_mla_indexer_topk.argtypes = [f32p, i32p, i32, i32, i32, i32p, vp]
     lib.sparse_mla_cache_store.restype = ctypes.c_int
     lib.sparse_mla_read_index_error.argtypes = [ctypes.POINTER(Plan), vp, ctypes.POINTER(i32 * 2), vp]
     lib.sparse_mla_read_index_error.restype = ctypes.c_int
@@ -293,6 +298,64 @@ def cache_store(kv_cache: torch.Tensor, kv_format, page_size: int, latent: torch
                lib.sparse_mla_cache_store(_ptr(latent), _ptr(rope), _ptr(slots), int(n), kvf,
                                           int(page_size), int(kv_cache.shape[0]), _ptr(kv_cache),
                                           _stream(stream)))
+
+
+def indexer_logits(q_codes: torch.Tensor, weights: torch.Tensor, key_cache: torch.Tensor,
+                   row_len: torch.Tensor, page_table: torch.Tensor, next_n: int, width: int,
+                   page_size: int = 64, logits: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """FP8 paged MQA logits: q_codes uint8 [R, 64, 128] (e4m3fn), weights fp32 [R, 64],
+    key_cache uint8 [num_pages, 132 * page_size], row_len int32 [R], page_table int32
+    [B, max_pages] with R = B * next_n.  Returns fp32 logits [R, width]; positions at or
+    past a row's length are left as they were in `logits` (allocated empty if None)."""
+    lib = load_library()
+    dev = q_codes.device
+    _require(q_codes, "q_codes", torch.uint8, dev)
+    _require(weights, "weights", torch.float32, dev)
+    _require(key_cache, "key_cache", torch.uint8, dev)
+    _require(row_len, "row_len", torch.int32, dev)
+    _require(page_table, "page_table", torch.int32, dev)
+    R = int(q_codes.shape[0])
+    B = int(page_table.shape[0])
+    if q_codes.dim() != 3 or tuple(q_codes.shape[1:]) != (64, 128) or tuple(weights.shape) != (R, 64):
+        raise ValueError("q_codes must be [R, 64, 128] and weights [R, 64]")
+    if R != B * next_n or tuple(row_len.shape) != (R,):
+        raise ValueError("rows must be num_requests * next_n, request-major, with one length each")
+    if key_cache.dim() != 2 or key_cache.shape[1] != 132 * page_size:
+        raise ValueError("key_cache must be [num_pages, 132 * page_size]")
+    if logits is None:
+        logits = torch.empty((R, width), dtype=torch.float32, device=dev)
+    _require(logits, "logits", torch.float32, dev)
+    if tuple(logits.shape) != (R, width):
+        raise ValueError("logits must be [R, width]")
+    with torch.cuda.device(dev):
+        _check("sparse_mla_indexer_logits",
+               lib.sparse_mla_indexer_logits(_ptr(q_codes), _ptr(weights), _ptr(key_cache), _ptr(row_len),
+                                             _ptr(page_table), B, int(next_n), 64, int(page_size),
+                                             int(key_cache.shape[0]), int(page_table.shape[1]), int(width),
+                                             _ptr(logits), _stream(stream)))
+    return logits
+
+
+def indexer_topk(logits: torch.Tensor, row_len: torch.Tensor, topk: int, out: torch.Tensor = None,
+                 stream=None) -> torch.Tensor:
+    """Top-k positions of each row's logits (ascending positions, -1 padded): int32 [R, topk]."""
+    lib = load_library()
+    dev = logits.device
+    _require(logits, "logits", torch.float32, dev)
+    _require(row_len, "row_len", torch.int32, dev)
+    R, width = int(logits.shape[0]), int(logits.shape[1])
+    if tuple(row_len.shape) != (R,):
+        raise ValueError("row_len must be [R]")
+    if out is None:
+        out = torch.empty((R, topk), dtype=torch.int32, device=dev)
+    _require(out, "out", torch.int32, dev)
+    if tuple(out.shape) != (R, topk):
+        raise ValueError("out must be [R, topk]")
+    with torch.cuda.device(dev):
+        _check("sparse_mla_indexer_topk",
+               lib.sparse_mla_indexer_topk(_ptr(logits), _ptr(row_len), R, width, int(topk), _ptr(out),
+                                           _stream(stream)))
+    return out
 
 
 def read_index_error(info: PlanInfo, workspace: torch.Tensor, stream=None):

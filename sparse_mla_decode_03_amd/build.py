@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libsparse_mla.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["smla_api.hip", "smla_decode.hip", "smla_merge.hip", "smla_store.hip"]
+SOURCES = ["smla_api.hip", "smla_decode.hip", "smla_merge.hip", "smla_store.hip", "smla_indexer.hip"]
 ARCH = "gfx950"
 
 

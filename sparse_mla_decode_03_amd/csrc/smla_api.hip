@@ -280,6 +280,54 @@ smla_status sparse_mla_cache_store(const void* latent, const void* rope, const i
   return SMLA_OK;
 }
 
+smla_status sparse_mla_indexer_logits(const void* q_codes, const float* weights, const void* key_cache,
+                                      const int32_t* row_len, const int32_t* page_table,
+                                      int32_t num_requests, int32_t next_n, int32_t num_heads,
+                                      int32_t page_size, int32_t num_pages, int32_t max_pages,
+                                      int32_t width, float* logits, void* stream) {
+  if (num_heads != 64 || page_size != 64 || next_n < 1 || next_n > 4) return SMLA_ERR_UNSUPPORTED;
+  if (num_requests < 0 || num_pages < 1 || width < 64 || width % 64 != 0 || max_pages < width / 64 ||
+      (int64_t)num_requests * next_n > INT32_MAX / 64 || (int64_t)num_pages * page_size > INT32_MAX)
+    return SMLA_ERR_BAD_SHAPE;
+  if (num_requests == 0) return SMLA_OK;
+  if (q_codes == nullptr || weights == nullptr || key_cache == nullptr || row_len == nullptr ||
+      page_table == nullptr || logits == nullptr)
+    return SMLA_ERR_NULL_ARG;
+  if (!aligned(q_codes, 16) || !aligned(weights, 16) || !aligned(key_cache, 16) || !aligned(logits, 16) ||
+      !aligned(row_len, 4) || !aligned(page_table, 4))
+    return SMLA_ERR_MISALIGNED;
+  smla::IndexerLogitsArgs a;
+  a.q = reinterpret_cast<const uint8_t*>(q_codes);
+  a.weights = weights;
+  a.keys = reinterpret_cast<const uint8_t*>(key_cache);
+  a.row_len = row_len;
+  a.page_table = page_table;
+  a.logits = logits;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.width = width;
+  if (smla::launch_indexer_logits(a, next_n, num_requests, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return SMLA_ERR_HIP;
+  return SMLA_OK;
+}
+
+smla_status sparse_mla_indexer_topk(const float* logits, const int32_t* row_len, int32_t rows,
+                                    int32_t width, int32_t topk, int32_t* indices, void* stream) {
+  if (rows < 0 || width < 1 || topk < 1 || topk > (1 << 20)) return SMLA_ERR_BAD_SHAPE;
+  if (rows == 0) return SMLA_OK;
+  if (logits == nullptr || row_len == nullptr || indices == nullptr) return SMLA_ERR_NULL_ARG;
+  if (!aligned(logits, 4) || !aligned(row_len, 4) || !aligned(indices, 4)) return SMLA_ERR_MISALIGNED;
+  smla::IndexerTopkArgs a;
+  a.logits = logits;
+  a.row_len = row_len;
+  a.out = indices;
+  a.width = width;
+  a.topk = topk;
+  if (smla::launch_indexer_topk(a, rows, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return SMLA_ERR_HIP;
+  return SMLA_OK;
+}
+
 smla_status sparse_mla_read_index_error(const smla_plan* plan, const void* workspace,
                                         int32_t* row_pos, void* stream) {
   const PlanImpl* pi = as_impl(plan);

@@ -69,34 +69,6 @@ __device__ __forceinline__ float sum_halves(float x) {
 // by a 32x32 MFMA whose rows are tokens.
 __device__ __forceinline__ int acc_row(int r, int G) { return 8 * (r >> 2) + 4 * G + (r & 3); }
 
-// Copy 16 (or 4) bytes per lane from global memory into LDS at dst + lane*size
-// (global_load_lds; dst is the same for the whole wave).  Written as inline asm so that
-// the compiler does not track these LDS writes: it would otherwise wait for every copy in
-// flight (vmcnt(0)) before any read of the staging area, exposing the full memory latency
-// once per tile.  The kernel orders the copies itself with explicit vmcnt waits (wait_vm,
-// wait_vm_le) before reading what they wrote.
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)(p));
-}
-__device__ __forceinline__ void dma16(const void* src, const void* lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds_offset(lds_wave_base)) : "memory");
-}
-__device__ __forceinline__ void dma4(const void* src, const void* lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(src), "s"(lds_offset(lds_wave_base)) : "memory");
-}
-// Wait until at most N of this wave's global loads (LDS copies included) are pending.
-// The builtin lets the compiler's own wait insertion see the wait; the empty asm with a
-// memory clobber keeps LDS reads of the copied data below it.
-template <int N>
-__device__ __forceinline__ void wait_vm_le() {
-  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
-  // vmcnt is split over bits 3:0 and 15:14; expcnt and lgkmcnt stay at their maxima
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
-  asm volatile("" ::: "memory");
-}
-__device__ __forceinline__ void wait_vm() { wait_vm_le<0>(); }
 
 // Per-configuration LDS and work split.  A tile is gathered by 64-lane DMA instructions
 // that each fill 1 KB of LDS, of two kinds:

@@ -1,0 +1,341 @@
+// Indexer for gfx950: FP8 paged MQA logits over each query row's context, and the top-k
+// selection that turns them into the index lists the decode path reads.
+//
+// The indexer's FP8 paged MQA logits are named on prhub sglang#24692 (implementation
+// breakdown item 5, key files); prhub vllm#52164 (implementation breakdown items 1-5,
+// key code excerpts) has the kernel take a request's next_n query rows natively, so that
+// every key page is read once for all of them, with per-row context lengths.  The logit
+// of row r at position t is sum_h w[r][h] * max(0, scale_t * <q[r][h], codes_t>) with
+// 128-dimensional e4m3fn queries and keys; top-k keeps the K largest logits, a tie at the
+// boundary going to the smaller position.
+//
+// Logits: one workgroup per (request, chunk of 32 key pages), four waves.  The chunk's
+// pages stream through a three-page LDS ring by global_load_lds; wave w serves row
+// w % next_n of the request on its share of each page's two 32-token blocks, so a page is
+// read from HBM once for all rows.  Scores come from the FP8 MFMA 32x32x64 (rows = 32
+// heads, columns = 32 tokens); each lane then holds one token and 16 heads of a block, so
+// the weighted ReLU sum over heads is 32 FMAs and one swap between lane halves.  The key
+// scale multiplies the head sum (the ReLU is positively homogeneous; scales are >= 0).
+// Logits are staged in LDS and stored after the chunk, so the loop's vmcnt waits count
+// only the page copies.
+//
+// Top-k: one workgroup per row.  Logits map to order-preserving 32-bit keys; three
+// histogram passes (11 + 11 + 10 bits) over the row find the K-th largest key T and how
+// many positions holding T are taken; a last pass writes every position with a key above
+// T and the first such ties in position order, compacted in ascending position order.
+#include "smla_device.h"
+#include "smla_kernels.h"
+
+namespace smla {
+
+namespace {
+
+typedef int __attribute__((ext_vector_type(8))) i32x8;
+
+constexpr int kIdxDim = 128;
+constexpr int kIdxHeads = 64;
+constexpr int kKeyPage = 64;                       // tokens per key page
+constexpr int kKeyPageCodes = kIdxDim * kKeyPage;  // 8192 bytes of codes, then 64 fp32 scales
+constexpr int kKeyPageBytes = kKeyPageCodes + 4 * kKeyPage;
+constexpr int kChunkPages = 32;
+constexpr int kRing = 3;
+constexpr int kSlotBytes = kKeyPageBytes;          // one LDS ring slot
+
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// LDS key page: token t's codes at t*128, its logical 16-byte chunk c stored at chunk
+// c ^ ((t >> 1) & 7), so the 16 lanes of a B-operand read (16 tokens, one chunk) hit 16
+// different chunk slots; the scales follow at byte 8192.
+__device__ __forceinline__ int key_swz(int t) { return (t >> 1) & 7; }
+
+template <int NN>
+__global__ __launch_bounds__(256, 2) void indexer_logits_kernel(IndexerLogitsArgs a) {
+  // G groups of next_n waves split each page's two 32-token blocks
+  constexpr int G = NN <= 2 ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t sRing[kRing * kSlotBytes];
+  __shared__ __attribute__((aligned(16))) float sStage[NN][kChunkPages * kKeyPage];
+  __shared__ int sPage[kChunkPages];
+  __shared__ int sOk[kChunkPages];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = blockIdx.y;
+  const int p0 = blockIdx.x * kChunkPages;
+  const int row0 = b * NN;
+  int len_max = 0;
+#pragma unroll
+  for (int i = 0; i < NN; ++i) len_max = max(len_max, min(a.row_len[row0 + i], a.width));
+  const int npages_b = (len_max + kKeyPage - 1) / kKeyPage;
+  if (p0 >= npages_b) return;                       // the whole workgroup
+  const int np = min(kChunkPages, npages_b - p0);
+
+  const bool active = wave < NN * G;
+  const int ri = wave % NN, grp = wave / NN;
+  const int row = row0 + ri;
+  const int row_len = min(a.row_len[row], a.width);
+
+  // A operands (queries) and weights of this wave's row: head block mb holds heads
+  // 32mb + lane%32; k-step ks covers dims 64ks .. 64ks+63, lane half lane/32 its bytes
+  // 32*(lane/32) .. +31.  The accumulator register j of a block holds head
+  // 8(j/4) + 4(lane/32) + j%4, whose weight is wj[mb][j].
+  i32x8 qa[2][2];
+  float wj[2][16];
+  if (active) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const uint8_t* qh = a.q + ((size_t)row * kIdxHeads + 32 * mb + (lane & 31)) * kIdxDim + 32 * (lane >> 5);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(qh + 64 * ks);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(qh + 64 * ks + 16);
+        qa[mb][ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+      const float* wr = a.weights + (size_t)row * kIdxHeads + 32 * mb + 4 * (lane >> 5);
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 w4 = *reinterpret_cast<const f32x4*>(wr + 8 * g4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wj[mb][4 * g4 + e] = w4[e];
+      }
+    }
+  }
+  if (tid < kChunkPages) {
+    const int p = p0 + tid;
+    const int pid = p < npages_b ? a.page_table[(size_t)b * a.max_pages + p] : 0;
+    const bool ok = p < npages_b && pid >= 0 && pid < a.num_pages;
+    sPage[tid] = ok ? pid : 0;                      // invalid pages are read from page 0
+    sOk[tid] = ok;
+  }
+  wait_vm();
+  __syncthreads();
+
+  // Page copies: wave w's instruction j fills 1 KB of codes (tokens 8(4j + w) .. +7, lane
+  // = physical chunk); wave 0 also copies the 64 scales.
+  auto issue_page = [&](int it) {
+    uint8_t* slot = sRing + (it % kRing) * kSlotBytes;
+    const uint8_t* src = a.keys + (size_t)sPage[it] * kKeyPageBytes;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int t = 8 * (4 * j + wave) + (lane >> 3);
+      const int lc = (lane & 7) ^ key_swz(t);
+      dma16(src + t * kIdxDim + 16 * lc, slot + 1024 * (4 * j + wave));
+    }
+    if (wave == 0) dma4(src + kKeyPageCodes + 4 * lane, slot + kKeyPageCodes);
+  };
+  // this wave's copies per page: 3 (wave 0) or 2
+  auto wait_page = [&](int it) {
+    const int later = min(np - 1, it + kRing - 1) - it;    // pages issued after `it`
+    if (wave == 0) {
+      if (later >= 2) wait_vm_le<6>(); else if (later == 1) wait_vm_le<3>(); else wait_vm();
+    } else {
+      if (later >= 2) wait_vm_le<4>(); else if (later == 1) wait_vm_le<2>(); else wait_vm();
+    }
+  };
+
+  for (int it = 0; it < min(np, kRing); ++it) issue_page(it);
+  for (int it = 0; it < np; ++it) {
+    wait_page(it);
+    __syncthreads();
+    if (active) {
+      const uint8_t* slot = sRing + (it % kRing) * kSlotBytes;
+      const float* scl = reinterpret_cast<const float*>(slot + kKeyPageCodes);
+      const bool page_ok = sOk[it] != 0;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        if (nb % G != grp) continue;
+        const int tn = 32 * nb + (lane & 31);      // this lane's token in the page
+        f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int lc = 4 * ks + 2 * (lane >> 5);
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(slot + tn * kIdxDim + 16 * (lc ^ key_swz(tn)));
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(slot + tn * kIdxDim + 16 * ((lc + 1) ^ key_swz(tn)));
+          const i32x8 kb = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+            acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mb][ks], kb, acc[mb], 0, 0, 0, 127, 0, 127);
+        }
+        float part = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) part = __builtin_fmaf(wj[mb][j], fmaxf(acc[mb][j], 0.f), part);
+        const float logit = halves_sum(part) * scl[tn];
+        const int t_abs = (p0 + it) * kKeyPage + tn;
+        if (lane < 32) sStage[ri][it * kKeyPage + tn] = (page_ok && t_abs < row_len) ? logit : -INFINITY;
+      }
+    }
+    __syncthreads();
+    if (it + kRing < np) issue_page(it + kRing);
+  }
+  __syncthreads();
+  // store the chunk's logits of every row, positions below the row's length only
+  for (int i = 0; i < NN; ++i) {
+    const int rl = min(a.row_len[row0 + i], a.width);
+    const int base = p0 * kKeyPage;
+    const int n = min(np * kKeyPage, rl - base);
+    float* dst = a.logits + (size_t)(row0 + i) * a.width + base;
+    for (int t = tid; t < n; t += 256) dst[t] = sStage[i][t];
+  }
+}
+
+// ---- top-k ------------------------------------------------------------------------------
+
+// Order-preserving key of a float: larger floats give larger unsigned keys (-inf lowest
+// among non-NaN values); -0 and +0 get the same key, as they are equal.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int kTopkThreads = 256;
+
+// Block-wide exclusive prefix sum of one value per thread; returns the prefix and the
+// total.  Uses `scratch` (kTopkThreads / 64 ints).
+__device__ __forceinline__ int block_excl_scan(int v, int* scratch, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkThreads / 64; ++w) {
+    const int s = scratch[w];
+    if (w < wave) before += s;
+    total += s;
+  }
+  __syncthreads();
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void indexer_topk_kernel(IndexerTopkArgs a) {
+  __shared__ int sHist[2048];
+  __shared__ int sScan[kTopkThreads / 64];
+  __shared__ int sSel[2];                      // chosen bin, count still needed from it
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n = max(0, min(a.row_len[r], a.width));
+  const int K = a.topk;
+  const float* lg = a.logits + (size_t)r * a.width;
+  int32_t* out = a.out + (size_t)r * K;
+
+  if (n <= K) {
+    // every position, then -1
+    for (int j = tid; j < K; j += kTopkThreads) out[j] = j < n ? j : -1;
+    return;
+  }
+  if (tid == 0) {
+    sSel[0] = 0;
+    sSel[1] = K;
+  }
+  // Radix select of the K-th largest key: digit widths 11, 11, 10 from the top.
+  uint32_t prefix = 0, prefix_mask = 0;
+  int need = K;                                 // how many still to take at or below the prefix
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nbins = pass == 2 ? 1024 : 2048;
+    for (int i = tid; i < nbins; i += kTopkThreads) sHist[i] = 0;
+    __syncthreads();
+    for (int t = tid; t < n; t += kTopkThreads) {
+      const uint32_t k = order_key(lg[t]);
+      if ((k & prefix_mask) == prefix) atomicAdd(&sHist[(k >> shift) & (nbins - 1)], 1);
+    }
+    __syncthreads();
+    // find the bin holding the need-th largest: count from the top bin down.  Thread i
+    // owns bins nbins-1-8i .. nbins-8-8i (descending).
+    const int per = nbins / kTopkThreads;      // 8 or 4
+    int local = 0;
+    for (int j = 0; j < per; ++j) local += sHist[nbins - 1 - (per * tid + j)];
+    int total;
+    const int before = block_excl_scan(local, sScan, total);
+    if (before < need && before + local >= need) {
+      int acc = before;
+      for (int j = 0; j < per; ++j) {
+        const int bin = nbins - 1 - (per * tid + j);
+        const int c = sHist[bin];
+        if (acc + c >= need) {
+          sSel[0] = bin;
+          sSel[1] = need - acc;
+          break;
+        }
+        acc += c;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sSel[0] << shift;
+    prefix_mask |= (uint32_t)(nbins - 1) << shift;
+    need = sSel[1];
+    __syncthreads();
+  }
+  // prefix = T, the K-th largest key; `need` positions holding T are taken, the smallest
+  // positions first.  Positions in ascending order, four per thread per round.
+  const uint32_t T = prefix;
+  int ties_before = 0, out_before = 0;
+#pragma unroll 1
+  for (int base = 0; base < n; base += 4 * kTopkThreads) {
+    uint32_t k4[4];
+    int tie = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = base + 4 * tid + e;
+      k4[e] = t < n ? order_key(lg[t]) : 0u;
+      tie += (t < n && k4[e] == T) ? 1 : 0;
+    }
+    int tie_total;
+    int tie_rank = ties_before + block_excl_scan(tie, sScan, tie_total);
+    int sel[4], cnt = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = base + 4 * tid + e;
+      bool s = false;
+      if (t < n) {
+        if (k4[e] > T) s = true;
+        else if (k4[e] == T) { s = tie_rank < need; ++tie_rank; }
+      }
+      sel[e] = s;
+      cnt += s;
+    }
+    int out_total;
+    int pos = out_before + block_excl_scan(cnt, sScan, out_total);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (sel[e] && pos < K) out[pos] = base + 4 * tid + e;
+      pos += sel[e];
+    }
+    ties_before += tie_total;
+    out_before += out_total;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_indexer_logits(const IndexerLogitsArgs& a, int next_n, int num_requests, hipStream_t st) {
+  const int chunks = (a.width / kKeyPage + kChunkPages - 1) / kChunkPages;
+  const dim3 grid(chunks, num_requests);
+  switch (next_n) {
+    case 1: hipLaunchKernelGGL(indexer_logits_kernel<1>, grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL(indexer_logits_kernel<2>, grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL(indexer_logits_kernel<3>, grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL(indexer_logits_kernel<4>, grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_topk(const IndexerTopkArgs& a, int rows, hipStream_t st) {
+  hipLaunchKernelGGL(indexer_topk_kernel, dim3(rows), dim3(kTopkThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace smla

@@ -24,6 +24,23 @@ struct DecodeArgs {
   float scale_log2;             // softmax_scale * log2(e)
 };
 
+struct IndexerLogitsArgs {
+  const uint8_t* q;             // e4m3fn [R][64][128]
+  const float* weights;         // [R][64]
+  const uint8_t* keys;          // key pages: codes [64][128] | fp32 scales [64]
+  const int32_t* row_len;       // [R]
+  const int32_t* page_table;    // [B][max_pages]
+  float* logits;                // [R][width]
+  int32_t max_pages, num_pages, width;
+};
+
+struct IndexerTopkArgs {
+  const float* logits;          // [R][width]
+  const int32_t* row_len;       // [R]
+  int32_t* out;                 // [R][topk]
+  int32_t width, topk;
+};
+
 int max_chunk_positions();
 hipError_t launch_decode(const DecodeArgs& a, int kv_format, hipStream_t st);
 hipError_t launch_merge(const float* part_o, const float* part_lse, int R, int S, int H,
@@ -33,5 +50,8 @@ hipError_t launch_gather_debug(const uint8_t* kv, int kv_format, int ps_log2, in
 hipError_t launch_fill_u64(unsigned long long* p, unsigned long long v, hipStream_t st);
 hipError_t launch_store(const uint16_t* latent, const uint16_t* rope, const int32_t* slots, int n,
                         int kv_format, int ps_log2, int num_slots, uint8_t* kv, hipStream_t st);
+
+hipError_t launch_indexer_logits(const IndexerLogitsArgs& a, int next_n, int num_requests, hipStream_t st);
+hipError_t launch_indexer_topk(const IndexerTopkArgs& a, int rows, hipStream_t st);
 
 }  // namespace smla

@@ -207,3 +207,36 @@ def test_cache_store_validation(lib):
     assert cs(v(FAKE), v(FAKE), v(FAKE + 2), 4, B.KV_BF16, 64, 10, v(FAKE), None) == B.ERR_MISALIGNED
     # zero tokens: nothing launched, pointers not checked
     assert cs(None, None, None, 0, B.KV_FP8_UE8M0, 64, 10, None, None) == B.OK
+
+
+def test_indexer_validation(lib):
+    v = ctypes.c_void_p
+    il = lib.sparse_mla_indexer_logits
+    # (q, weights, keys, row_len, page_table, B, next_n, heads, page_size, num_pages,
+    #  max_pages, width, logits, stream)
+    args = [v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), 4, 2, 64, 64, 100, 8, 512, v(FAKE), None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["q", "w", "k", "len", "pt", "B", "nn", "H", "ps", "np", "mp", "width", "out", "st"]
+        for key, val in kw.items():
+            a[names.index(key)] = val
+        return il(*a)
+
+    assert call(H=32) == B.ERR_UNSUPPORTED
+    assert call(ps=16) == B.ERR_UNSUPPORTED
+    assert call(nn=5) == B.ERR_UNSUPPORTED and call(nn=0) == B.ERR_UNSUPPORTED
+    assert call(width=500) == B.ERR_BAD_SHAPE and call(width=0) == B.ERR_BAD_SHAPE
+    assert call(mp=7) == B.ERR_BAD_SHAPE            # the table must cover the width
+    assert call(np=0) == B.ERR_BAD_SHAPE and call(B=-1) == B.ERR_BAD_SHAPE
+    assert call(q=None) == B.ERR_NULL_ARG and call(out=None) == B.ERR_NULL_ARG
+    assert call(w=v(FAKE + 4)) == B.ERR_MISALIGNED and call(len=v(FAKE + 2)) == B.ERR_MISALIGNED
+    assert call(B=0, q=None, out=None) == B.OK      # nothing to do
+    tk = lib.sparse_mla_indexer_topk
+    # (logits, row_len, rows, width, topk, indices, stream)
+    assert tk(v(FAKE), v(FAKE), 3, 0, 16, v(FAKE), None) == B.ERR_BAD_SHAPE
+    assert tk(v(FAKE), v(FAKE), 3, 64, 0, v(FAKE), None) == B.ERR_BAD_SHAPE
+    assert tk(v(FAKE), v(FAKE), -1, 64, 16, v(FAKE), None) == B.ERR_BAD_SHAPE
+    assert tk(None, v(FAKE), 3, 64, 16, v(FAKE), None) == B.ERR_NULL_ARG
+    assert tk(v(FAKE), v(FAKE), 3, 64, 16, v(FAKE + 1), None) == B.ERR_MISALIGNED
+    assert tk(None, None, 0, 64, 16, None, None) == B.OK
