@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PMC_FILE = os.path.join(ROOT, "profiles", "decode_b128_mtp4_h128_fp8_pmc.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "sparse_mla_decode_03_amd", "csrc", f)
                   for f in ("smla_decode.hip", "smla_device.h")]
@@ -92,6 +93,56 @@ def cache_store_measure(B, torch, dev, n_tokens: int, reps: int):
                          "bytes_per_launch": nbytes}}
 
 
+def indexer_measure(B, W, torch, dev, name: str, reps: int):
+    """Time the indexer on one workload: the logits kernel and the top-k kernel, each
+    launched `reps` times after warm-up, HIP events on the launch stream."""
+    spec = W.INDEXER_WORKLOADS[name]
+    inp = W.make_indexer_inputs(spec, 5, device=dev, cache_device=dev)
+    stream = torch.cuda.current_stream()
+    logits = torch.empty((inp.num_rows, inp.width), dtype=torch.float32, device=dev)
+    out = torch.empty((inp.num_rows, spec.topk), dtype=torch.int32, device=dev)
+
+    def logits_call():
+        B.indexer_logits(inp.q_codes, inp.weights, inp.key_cache, inp.row_len, inp.page_table,
+                         spec.next_n, inp.width, logits=logits, stream=stream)
+
+    def topk_call():
+        B.indexer_topk(logits, inp.row_len, spec.topk, out=out, stream=stream)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+        return sum(ms) / len(ms), ms[len(ms) // 2]
+
+    lg_mean, lg_p50 = timed(logits_call)
+    tk_mean, tk_p50 = timed(topk_call)
+    nbytes = W.indexer_algorithmic_bytes(inp)
+    flops = W.indexer_algorithmic_flops(inp)
+    positions = int(inp.row_len.sum().item())
+    tk_bytes = positions * 4 + inp.num_rows * spec.topk * 4 + inp.num_rows * 4
+    gbs = nbytes / (lg_mean / 1e3) / 1e9
+    return {"workload": name, "rows": inp.num_rows, "next_n": spec.next_n, "heads": spec.num_heads,
+            "topk": spec.topk, "visible_positions": positions,
+            "logits_ms_mean": lg_mean, "logits_ms_p50": lg_p50,
+            "topk_ms_mean": tk_mean, "topk_ms_p50": tk_p50,
+            "logits_roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": gbs / PEAK_HBM_GBS, "bytes_per_launch": nbytes,
+                                "fp8_tflop_s": flops / (lg_mean / 1e3) / 1e12,
+                                "fp8_frac": flops / (lg_mean / 1e3) / 1e12 / PEAK_FP8_TFLOPS},
+            "topk_roofline": {"bound": "hbm", "achieved": tk_bytes / (tk_mean / 1e3) / 1e9,
+                              "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                              "frac": tk_bytes / (tk_mean / 1e3) / 1e9 / PEAK_HBM_GBS,
+                              "bytes_per_launch": tk_bytes}}
+
+
 def cpu_baseline(inp, budget_s: float):
     """Time the float64 oracle on whole rows of the same workload until about budget_s
     of CPU work has been done."""
@@ -147,6 +198,8 @@ def main() -> int:
                          "caches (L2 and the 256 MB MALL); reported beside the warm figure")
     ap.add_argument("--store-tokens", type=int, default=65536,
                     help="tokens per timed cache-store launch (0: skip that measurement)")
+    ap.add_argument("--indexer", default="idx_b128_mtp4_h64",
+                    help="indexer workload measured beside the decode ('' to skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run only a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -280,6 +333,8 @@ def main() -> int:
     }
     if args.store_tokens > 0:
         res["cache_store"] = cache_store_measure(B, torch, dev, args.store_tokens, 20)
+    if args.indexer:
+        res["indexer"] = indexer_measure(B, W, torch, dev, args.indexer, 20)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
     print(json.dumps(res), flush=True)

@@ -238,7 +238,8 @@ smla_status sparse_mla_indexer_logits(const void* q_codes, const float* weights,
  * positions t < n of largest logits[r][t], a tie at the boundary going to the smaller
  * position, written to indices[r][0..topk) in ascending position order; with n <= topk,
  * positions 0..n-1 and then -1.  NaN logits give an unspecified selection.
- *   logits fp32 [rows][width]; row_len int32 [rows]; indices int32 [rows][topk]
+ *   logits fp32 [rows][width] (16 B aligned, width a multiple of 4); row_len int32 [rows];
+ *   indices int32 [rows][topk]
  * No allocation; asynchronous.  Errors: BAD_SHAPE, NULL_ARG, MISALIGNED, HIP. */
 smla_status sparse_mla_indexer_topk(const float* logits, const int32_t* row_len, int32_t rows,
                                     int32_t width, int32_t topk, int32_t* indices, void* stream);

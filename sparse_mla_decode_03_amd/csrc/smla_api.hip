@@ -313,10 +313,10 @@ smla_status sparse_mla_indexer_logits(const void* q_codes, const float* weights,
 
 smla_status sparse_mla_indexer_topk(const float* logits, const int32_t* row_len, int32_t rows,
                                     int32_t width, int32_t topk, int32_t* indices, void* stream) {
-  if (rows < 0 || width < 1 || topk < 1 || topk > (1 << 20)) return SMLA_ERR_BAD_SHAPE;
+  if (rows < 0 || width < 4 || width % 4 != 0 || topk < 1 || topk > (1 << 20)) return SMLA_ERR_BAD_SHAPE;
   if (rows == 0) return SMLA_OK;
   if (logits == nullptr || row_len == nullptr || indices == nullptr) return SMLA_ERR_NULL_ARG;
-  if (!aligned(logits, 4) || !aligned(row_len, 4) || !aligned(indices, 4)) return SMLA_ERR_MISALIGNED;
+  if (!aligned(logits, 16) || !aligned(row_len, 4) || !aligned(indices, 4)) return SMLA_ERR_MISALIGNED;
   smla::IndexerTopkArgs a;
   a.logits = logits;
   a.row_len = row_len;

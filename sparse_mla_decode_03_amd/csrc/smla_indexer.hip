@@ -192,10 +192,12 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-constexpr int kTopkThreads = 256;
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kCandCap = 6144;                 // candidates of the first bin kept in LDS
 
 // Block-wide exclusive prefix sum of one value per thread; returns the prefix and the
-// total.  Uses `scratch` (kTopkThreads / 64 ints).
+// total.  Uses `scratch` (kTopkWaves ints).
 __device__ __forceinline__ int block_excl_scan(int v, int* scratch, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
@@ -209,7 +211,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* scratch, int& total) 
   int before = 0;
   total = 0;
 #pragma unroll
-  for (int w = 0; w < kTopkThreads / 64; ++w) {
+  for (int w = 0; w < kTopkWaves; ++w) {
     const int s = scratch[w];
     if (w < wave) before += s;
     total += s;
@@ -218,10 +220,52 @@ __device__ __forceinline__ int block_excl_scan(int v, int* scratch, int& total) 
   return before + x - v;
 }
 
+// Keys of positions 4i .. 4i+3 of the row (positions >= n give key 0, below every
+// real key but never counted: callers check the position).
+__device__ __forceinline__ void load_keys4(const float* lg, int i4, int n, uint32_t (&k)[4]) {
+  if (i4 + 3 < n) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(lg + i4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) k[e] = order_key(v[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) k[e] = i4 + e < n ? order_key(lg[i4 + e]) : 0u;
+  }
+}
+
+// The bin holding the need-th largest of a histogram counted from the top: thread i owns
+// bins nbins-1-per*i .. nbins-per*(i+1) (descending).  Writes (bin, count still needed
+// from it) to sel.  All threads call it.
+__device__ __forceinline__ void find_bin(const int* hist, int nbins, int need, int* scratch, int* sel) {
+  const int tid = threadIdx.x;
+  const int per = nbins / kTopkThreads;
+  int local = 0;
+  for (int j = 0; j < per; ++j) local += hist[nbins - 1 - (per * tid + j)];
+  int total;
+  const int before = block_excl_scan(local, scratch, total);
+  if (before < need && before + local >= need) {
+    int acc = before;
+    for (int j = 0; j < per; ++j) {
+      const int bin = nbins - 1 - (per * tid + j);
+      const int c = hist[bin];
+      if (acc + c >= need) {
+        sel[0] = bin;
+        sel[1] = need - acc;
+        break;
+      }
+      acc += c;
+    }
+  }
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(kTopkThreads) void indexer_topk_kernel(IndexerTopkArgs a) {
   __shared__ int sHist[2048];
-  __shared__ int sScan[kTopkThreads / 64];
-  __shared__ int sSel[2];                      // chosen bin, count still needed from it
+  __shared__ uint32_t sCandKey[kCandCap];
+  __shared__ int sCandPos[kCandCap];
+  __shared__ int sScan[kTopkWaves];
+  __shared__ int sSel[2];
+  __shared__ int sCount;
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int n = max(0, min(a.row_len[r], a.width));
@@ -230,90 +274,132 @@ __global__ __launch_bounds__(kTopkThreads) void indexer_topk_kernel(IndexerTopkA
   int32_t* out = a.out + (size_t)r * K;
 
   if (n <= K) {
-    // every position, then -1
     for (int j = tid; j < K; j += kTopkThreads) out[j] = j < n ? j : -1;
     return;
   }
+  // ---- pass 1: histogram of the top 11 bits ----
+  for (int i = tid; i < 2048; i += kTopkThreads) sHist[i] = 0;
   if (tid == 0) {
     sSel[0] = 0;
     sSel[1] = K;
+    sCount = 0;
   }
-  // Radix select of the K-th largest key: digit widths 11, 11, 10 from the top.
-  uint32_t prefix = 0, prefix_mask = 0;
-  int need = K;                                 // how many still to take at or below the prefix
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int nbins = pass == 2 ? 1024 : 2048;
-    for (int i = tid; i < nbins; i += kTopkThreads) sHist[i] = 0;
-    __syncthreads();
-    for (int t = tid; t < n; t += kTopkThreads) {
-      const uint32_t k = order_key(lg[t]);
-      if ((k & prefix_mask) == prefix) atomicAdd(&sHist[(k >> shift) & (nbins - 1)], 1);
-    }
-    __syncthreads();
-    // find the bin holding the need-th largest: count from the top bin down.  Thread i
-    // owns bins nbins-1-8i .. nbins-8-8i (descending).
-    const int per = nbins / kTopkThreads;      // 8 or 4
-    int local = 0;
-    for (int j = 0; j < per; ++j) local += sHist[nbins - 1 - (per * tid + j)];
-    int total;
-    const int before = block_excl_scan(local, sScan, total);
-    if (before < need && before + local >= need) {
-      int acc = before;
-      for (int j = 0; j < per; ++j) {
-        const int bin = nbins - 1 - (per * tid + j);
-        const int c = sHist[bin];
-        if (acc + c >= need) {
-          sSel[0] = bin;
-          sSel[1] = need - acc;
-          break;
+  __syncthreads();
+  for (int i4 = 4 * tid; i4 < n; i4 += 4 * kTopkThreads) {
+    uint32_t k[4];
+    load_keys4(lg, i4, n, k);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (i4 + e < n) atomicAdd(&sHist[k[e] >> 21], 1);
+  }
+  __syncthreads();
+  find_bin(sHist, 2048, K, sScan, sSel);
+  const uint32_t b1 = (uint32_t)sSel[0];
+  int need = sSel[1];
+  const int c1 = sHist[b1];
+  __syncthreads();
+
+  uint32_t T;
+  int ties_total = -1;                          // known only on the LDS path
+  if (c1 <= kCandCap) {
+    // ---- pass 2: the first bin's keys and positions into LDS, then select there ----
+    for (int i4 = 4 * tid; i4 < n; i4 += 4 * kTopkThreads) {
+      uint32_t k[4];
+      load_keys4(lg, i4, n, k);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (i4 + e < n && (k[e] >> 21) == b1) {
+          const int slot = atomicAdd(&sCount, 1);
+          sCandKey[slot] = k[e];
+          sCandPos[slot] = i4 + e;
         }
-        acc += c;
-      }
     }
-    __syncthreads();
-    prefix |= (uint32_t)sSel[0] << shift;
-    prefix_mask |= (uint32_t)(nbins - 1) << shift;
-    need = sSel[1];
-    __syncthreads();
+    uint32_t prefix = b1 << 21, mask = 0x7FFu << 21;
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+      const int shift = pass == 0 ? 10 : 0;
+      const int nbins = pass == 0 ? 2048 : 1024;
+      __syncthreads();
+      for (int i = tid; i < 2048; i += kTopkThreads) sHist[i] = 0;
+      __syncthreads();
+      for (int c = tid; c < c1; c += kTopkThreads) {
+        const uint32_t k = sCandKey[c];
+        if ((k & mask) == prefix) atomicAdd(&sHist[(k >> shift) & (nbins - 1)], 1);
+      }
+      __syncthreads();
+      find_bin(sHist, nbins, need, sScan, sSel);
+      prefix |= (uint32_t)sSel[0] << shift;
+      mask |= (uint32_t)(nbins - 1) << shift;
+      need = sSel[1];
+      if (pass == 1) ties_total = sHist[sSel[0]];
+    }
+    T = prefix;
+  } else {
+    // ---- passes 2 and 3 over the row (a crowded first bin) ----
+    uint32_t prefix = b1 << 21, mask = 0x7FFu << 21;
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+      const int shift = pass == 0 ? 10 : 0;
+      const int nbins = pass == 0 ? 2048 : 1024;
+      for (int i = tid; i < 2048; i += kTopkThreads) sHist[i] = 0;
+      __syncthreads();
+      for (int i4 = 4 * tid; i4 < n; i4 += 4 * kTopkThreads) {
+        uint32_t k[4];
+        load_keys4(lg, i4, n, k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (i4 + e < n && (k[e] & mask) == prefix) atomicAdd(&sHist[(k[e] >> shift) & (nbins - 1)], 1);
+      }
+      __syncthreads();
+      find_bin(sHist, nbins, need, sScan, sSel);
+      prefix |= (uint32_t)sSel[0] << shift;
+      mask |= (uint32_t)(nbins - 1) << shift;
+      need = sSel[1];
+      __syncthreads();
+    }
+    T = prefix;
   }
-  // prefix = T, the K-th largest key; `need` positions holding T are taken, the smallest
-  // positions first.  Positions in ascending order, four per thread per round.
-  const uint32_t T = prefix;
+  // ---- last pass: every key above T and the first `need` keys equal to T, written in
+  // ascending position order.  When every tie is taken, one scan per round suffices.
+  const bool all_ties = ties_total == need;
   int ties_before = 0, out_before = 0;
 #pragma unroll 1
   for (int base = 0; base < n; base += 4 * kTopkThreads) {
-    uint32_t k4[4];
-    int tie = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = base + 4 * tid + e;
-      k4[e] = t < n ? order_key(lg[t]) : 0u;
-      tie += (t < n && k4[e] == T) ? 1 : 0;
-    }
-    int tie_total;
-    int tie_rank = ties_before + block_excl_scan(tie, sScan, tie_total);
+    const int i4 = base + 4 * tid;
+    uint32_t k[4];
+    load_keys4(lg, i4, n, k);
     int sel[4], cnt = 0;
+    if (all_ties) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = base + 4 * tid + e;
-      bool s = false;
-      if (t < n) {
-        if (k4[e] > T) s = true;
-        else if (k4[e] == T) { s = tie_rank < need; ++tie_rank; }
+      for (int e = 0; e < 4; ++e) {
+        sel[e] = (i4 + e < n && k[e] >= T) ? 1 : 0;
+        cnt += sel[e];
       }
-      sel[e] = s;
-      cnt += s;
+    } else {
+      int tie = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tie += (i4 + e < n && k[e] == T) ? 1 : 0;
+      int tie_total;
+      int tie_rank = ties_before + block_excl_scan(tie, sScan, tie_total);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bool s2 = false;
+        if (i4 + e < n) {
+          if (k[e] > T) s2 = true;
+          else if (k[e] == T) { s2 = tie_rank < need; ++tie_rank; }
+        }
+        sel[e] = s2;
+        cnt += sel[e];
+      }
+      ties_before += tie_total;
     }
     int out_total;
     int pos = out_before + block_excl_scan(cnt, sScan, out_total);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (sel[e] && pos < K) out[pos] = base + 4 * tid + e;
+      if (sel[e] && pos < K) out[pos] = i4 + e;
       pos += sel[e];
     }
-    ties_before += tie_total;
     out_before += out_total;
   }
 }

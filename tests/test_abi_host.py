@@ -239,4 +239,6 @@ def test_indexer_validation(lib):
     assert tk(v(FAKE), v(FAKE), -1, 64, 16, v(FAKE), None) == B.ERR_BAD_SHAPE
     assert tk(None, v(FAKE), 3, 64, 16, v(FAKE), None) == B.ERR_NULL_ARG
     assert tk(v(FAKE), v(FAKE), 3, 64, 16, v(FAKE + 1), None) == B.ERR_MISALIGNED
+    assert tk(v(FAKE + 4), v(FAKE), 3, 64, 16, v(FAKE), None) == B.ERR_MISALIGNED
+    assert tk(v(FAKE), v(FAKE), 3, 66, 16, v(FAKE), None) == B.ERR_BAD_SHAPE
     assert tk(None, None, 0, 64, 16, None, None) == B.OK

@@ -164,6 +164,12 @@ def test_topk_edges():
     neg[1, ::3] = 0.0
     neg[1, 1::3] = -0.0
     _topk_case(neg, torch.tensor([width, width, 100], dtype=torch.int32), 2048, "negative, -inf, +-0")
+    # a first-bin crowd larger than the kernel keeps in LDS (the three-pass route), and one
+    # that fits
+    big = torch.full((3, 20000), 1.5)
+    big[1, ::5] = 2.0
+    big[2] = torch.from_numpy(rng.standard_normal(20000).astype(np.float32))
+    _topk_case(big, torch.tensor([20000, 20000, 19999], dtype=torch.int32), 2048, "crowded first bin")
     _topk_case(lg, lens, 1, "K = 1")
     _topk_case(lg, lens, 3000, "K = 3000")
 
