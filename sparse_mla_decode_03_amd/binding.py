@@ -93,6 +93,8 @@ def load_library(path: str = LIB_PATH):
     lib.sparse_mla_indexer_logits.argtypes = [vp, f32p, vp, i32p, i32p, i32, i32, i32, i32, i32, i32,
                                               i32, f32p, vp]
     lib.sparse_mla_indexer_topk.argtypes = [f32p, i32p, i32, i32, i32, i32p, vp]
+    lib.sparse_mla_indexer_logits.restype = ctypes.c_int
+    lib.sparse_mla_indexer_topk.restype = ctypes.c_int
     lib.sparse_mla_cache_store.restype = ctypes.c_int
     lib.sparse_mla_read_index_error.argtypes = [ctypes.POINTER(Plan), vp, ctypes.POINTER(i32 * 2), vp]
     lib.sparse_mla_read_index_error.restype = ctypes.c_int

@@ -9,10 +9,10 @@
 // 128-dimensional e4m3fn queries and keys; top-k keeps the K largest logits, a tie at the
 // boundary going to the smaller position.
 //
-// Logits: one workgroup per (request, chunk of 32 key pages), four waves.  The chunk's
-// pages stream through a three-page LDS ring by global_load_lds; wave w serves row
-// w % next_n of the request on its share of each page's two 32-token blocks, so a page is
-// read from HBM once for all rows.  Scores come from the FP8 MFMA 32x32x64 (rows = 32
+// Logits: one workgroup per (request, chunk of 16 key pages), four waves, three workgroups
+// per compute unit.  The chunk's pages stream through a four-page LDS ring by
+// global_load_lds; wave w serves row w % next_n of the request on its share of each
+// page's two 32-token blocks, so a page is read from HBM once for all rows.  Scores come from the FP8 MFMA 32x32x64 (rows = 32
 // heads, columns = 32 tokens); each lane then holds one token and 16 heads of a block, so
 // the weighted ReLU sum over heads is 32 FMAs and one swap between lane halves.  The key
 // scale multiplies the head sum (the ReLU is positively homogeneous; scales are >= 0).
@@ -37,8 +37,8 @@ constexpr int kIdxHeads = 64;
 constexpr int kKeyPage = 64;                       // tokens per key page
 constexpr int kKeyPageCodes = kIdxDim * kKeyPage;  // 8192 bytes of codes, then 64 fp32 scales
 constexpr int kKeyPageBytes = kKeyPageCodes + 4 * kKeyPage;
-constexpr int kChunkPages = 32;
-constexpr int kRing = 3;
+constexpr int kChunkPages = 16;
+constexpr int kRing = 4;
 constexpr int kSlotBytes = kKeyPageBytes;          // one LDS ring slot
 
 __device__ __forceinline__ float halves_sum(float x) {
@@ -51,8 +51,22 @@ __device__ __forceinline__ float halves_sum(float x) {
 // different chunk slots; the scales follow at byte 8192.
 __device__ __forceinline__ int key_swz(int t) { return (t >> 1) & 7; }
 
+// Wait until this wave's copies of all but the `later` most recent pages (PER copies
+// each) have landed.
+template <int PER>
+__device__ __forceinline__ void wait_later(int later) {
+  static_assert(kRing <= 5, "wait_later covers up to four later pages");
+  switch (later) {
+    case 0: wait_vm(); break;
+    case 1: wait_vm_le<PER>(); break;
+    case 2: wait_vm_le<2 * PER>(); break;
+    case 3: wait_vm_le<3 * PER>(); break;
+    default: wait_vm_le<4 * PER>(); break;
+  }
+}
+
 template <int NN>
-__global__ __launch_bounds__(256, 2) void indexer_logits_kernel(IndexerLogitsArgs a) {
+__global__ __launch_bounds__(256, 3) void indexer_logits_kernel(IndexerLogitsArgs a) {
   // G groups of next_n waves split each page's two 32-token blocks
   constexpr int G = NN <= 2 ? 2 : 1;
   __shared__ __attribute__((aligned(16))) uint8_t sRing[kRing * kSlotBytes];
@@ -125,14 +139,11 @@ __global__ __launch_bounds__(256, 2) void indexer_logits_kernel(IndexerLogitsArg
     }
     if (wave == 0) dma4(src + kKeyPageCodes + 4 * lane, slot + kKeyPageCodes);
   };
-  // this wave's copies per page: 3 (wave 0) or 2
+  // this wave's copies per page: 3 (wave 0) or 2; the pages issued after `it` may stay
+  // in flight
   auto wait_page = [&](int it) {
-    const int later = min(np - 1, it + kRing - 1) - it;    // pages issued after `it`
-    if (wave == 0) {
-      if (later >= 2) wait_vm_le<6>(); else if (later == 1) wait_vm_le<3>(); else wait_vm();
-    } else {
-      if (later >= 2) wait_vm_le<4>(); else if (later == 1) wait_vm_le<2>(); else wait_vm();
-    }
+    const int later = min(np - 1, it + kRing - 1) - it;
+    if (wave == 0) wait_later<3>(later); else wait_later<2>(later);
   };
 
   for (int it = 0; it < min(np, kRing); ++it) issue_page(it);
