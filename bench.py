@@ -93,6 +93,49 @@ def cache_store_measure(B, torch, dev, n_tokens: int, reps: int):
                          "bytes_per_launch": nbytes}}
 
 
+def mixed_measure(B, W, torch, dev, name: str, reps: int):
+    """One decode launch over a batch that mixes prefill chunks and decode rows."""
+    spec = W.WORKLOADS[name]
+    inp = W.make_inputs(spec, 41, device=dev, cache_device=dev)
+    R, H = inp.num_rows, inp.num_heads
+    prob = B.make_problem(R, spec.num_requests, H, spec.topk, spec.page_size, inp.num_pages,
+                          inp.page_table.shape[1], B.KV_FP8_UE8M0, B.IDX_LOGICAL, 0, 0,
+                          spec.softmax_scale)
+    info = B.plan(prob)
+    out = torch.empty((R, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((R, H), dtype=torch.float32, device=dev)
+    ws = (torch.empty(info.workspace_bytes, dtype=torch.uint8, device=dev)
+          if info.workspace_bytes else None)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.run(info, inp.q, inp.kv_cache, inp.indices, inp.row_req, inp.page_table, inp.sinks,
+              out, lse, None, None, ws, stream)
+
+    for _ in range(3):
+        step()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    mean_s = sum(ms) / len(ms) / 1e3
+    n = inp.num_valid()
+    flops = W.algorithmic_flops(inp)
+    counts = torch.bincount(inp.row_req.long().cpu()).tolist()
+    return {"workload": name, "rows": R, "requests": spec.num_requests,
+            "rows_per_request": {str(k): counts.count(k) for k in sorted(set(counts))},
+            "attended_entries": n, "num_splits": info.num_splits,
+            "launch_ms_mean": mean_s * 1e3, "launch_ms_p50": ms[len(ms) // 2],
+            "entries_per_s": n / mean_s,
+            "roofline": {"bound": "mfma", "achieved": flops / mean_s / 1e12, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": flops / mean_s / 1e12 / PEAK_BF16_TFLOPS,
+                         "flops_per_launch": flops}}
+
+
 def indexer_measure(B, W, torch, dev, name: str, reps: int):
     """Time the indexer on one workload: the logits kernel and the top-k kernel, each
     launched `reps` times after warm-up, HIP events on the launch stream."""
@@ -198,6 +241,8 @@ def main() -> int:
                          "caches (L2 and the 256 MB MALL); reported beside the warm figure")
     ap.add_argument("--store-tokens", type=int, default=65536,
                     help="tokens per timed cache-store launch (0: skip that measurement)")
+    ap.add_argument("--mixed", default="mixed_b24_h128_fp8",
+                    help="prefill+decode batch measured beside the decode ('' to skip)")
     ap.add_argument("--indexer", default="idx_b128_mtp4_h64",
                     help="indexer workload measured beside the decode ('' to skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -333,6 +378,8 @@ def main() -> int:
     }
     if args.store_tokens > 0:
         res["cache_store"] = cache_store_measure(B, torch, dev, args.store_tokens, 20)
+    if args.mixed:
+        res["mixed_prefill_decode"] = mixed_measure(B, W, torch, dev, args.mixed, 10)
     if args.indexer:
         res["indexer"] = indexer_measure(B, W, torch, dev, args.indexer, 20)
     if not args.no_cpu_baseline:

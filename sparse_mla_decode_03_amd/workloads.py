@@ -70,6 +70,7 @@ class WorkloadSpec:
     permute_pages: bool = True
     num_splits: int = 0              # 0 = planner decides
     softmax_scale: float = 1.0 / math.sqrt(576.0)
+    causal: bool = False             # row i of n rows draws from positions < ctx - n + 1 + i
 
     def scaled(self, **kw) -> "WorkloadSpec":
         return dataclasses.replace(self, **kw)
@@ -86,6 +87,10 @@ WORKLOADS = {
     "ragged_b256_h64_fp8": WorkloadSpec("ragged_b256_h64_fp8", 256, (1, 2, 4), 64, 2048, 4096,
                                         4096, KV_FP8, valid="uniform", sinks="half_neg_inf",
                                         shared_frac=0.1),
+    # prefill chunks and decode rows in one launch: requests with 1, 4 or 256 query rows,
+    # each row with its own causal top-k list
+    "mixed_b24_h128_fp8": WorkloadSpec("mixed_b24_h128_fp8", 24, (1, 4, 256), 128, 2048, 8192,
+                                       65536, KV_FP8, causal=True),
 }
 # Order of the workloads as they are numbered in the documentation (1..5).
 WORKLOAD_ORDER = ["tiny_bf16", "b32_h64_fp8", "b128_mtp4_h128_fp8", "b2_h128_bf16_split16",
@@ -218,8 +223,12 @@ def make_inputs(spec: WorkloadSpec, seed: int, device="cpu", cache_device=None) 
     R = int(nrows.sum())
     row_req = np.repeat(np.arange(B, dtype=np.int32), nrows)
     indices = np.full((R, K), -1, dtype=np.int32)
+    first_row = np.concatenate([[0], np.cumsum(nrows)[:-1]])
     for r in range(R):
         c = int(ctx[row_req[r]])
+        if spec.causal:
+            b = int(row_req[r])
+            c -= int(nrows[b]) - 1 - (r - int(first_row[b]))
         if spec.valid == "uniform":
             count = int(rng.integers(1, K + 1))
         else:

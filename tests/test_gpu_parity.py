@@ -364,3 +364,32 @@ def test_non_finite_inputs_complete_and_stay_local(fmt):
     assert d.max() <= 2e-2 and d.mean() <= 2e-3
     lg = lse.cpu().double().numpy()
     assert np.all(np.abs(lg[ok] - l[ok]) <= 1e-3 * np.maximum(1.0, np.abs(l[ok])))
+
+
+@pytest.mark.parametrize("full", [False, True])
+def test_mixed_prefill_and_decode_rows_in_one_launch(full):
+    """Requests with 1, 4 or 256 query rows in one launch, each row with its own causal
+    top-k list: the grid covers exactly the rows, with no padding to the longest request.
+    Sampled rows (the prefill chunks' first, middle and last rows among them)."""
+    spec = W.WORKLOADS["mixed_b24_h128_fp8"]
+    if not full:
+        spec = spec.scaled(num_requests=4, ctx_hi=9000)
+    inp = W.make_inputs(spec, 41, device="cpu", cache_device=DEV if full else None)
+    counts = torch.bincount(inp.row_req.long()).tolist()
+    announce(f"mixed rows={inp.num_rows} per request={counts} full={full}")
+    out, lse = gpu_decode(inp)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    first = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    rng = np.random.default_rng(41)
+    rows = {0, inp.num_rows - 1}
+    for b, n in enumerate(counts):
+        rows |= {int(first[b]), int(first[b] + n // 2), int(first[b] + n - 1)}
+    rows |= set(rng.choice(inp.num_rows, size=8, replace=False).tolist())
+    rows = sorted(rows)
+    if full:
+        sub_cache, sub_pt = page_subset(inp, rows)
+        o, l = oracle_decode(inp, rows=rows, kv_cache=sub_cache, page_table=sub_pt)
+    else:
+        o, l = oracle_decode(inp, rows=rows)
+    compare(out[rows], lse[rows], o, l, what=f"mixed rows={len(rows)}")
