@@ -123,9 +123,40 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int ps_mask = (1 << a.ps_log2) - 1;
   if (tid == 0) sRestart = 0;
 
+  // ---- 1a. the loads of the index translation come first: the split's first batch of
+  // indices and the request's page-table row (into LDS, borrowed from the K buffers, when
+  // it has at most kPtPer * NT entries), so their use below does not wait for q ----
+  int req = 0;
+  bool req_ok = true;
+  if (a.index_mode == 0) {
+    req = a.row_req[row];
+    req_ok = req >= 0 && req < a.B;
+  }
+  constexpr int kCB = 8;
+  constexpr int kPtPer = 8;
+  int* sPt = reinterpret_cast<int*>(sK);
+  // typed LDS view for the lookups, so they stay LDS reads (a pointer that may be LDS or
+  // global would become a flat load, whose wait also covers the q loads)
+  const __attribute__((address_space(3))) int* sPtL = (const __attribute__((address_space(3))) int*)(sPt);
+  const bool pt_lds = a.index_mode == 0 && req_ok && a.max_pages <= kPtPer * NT;   // uniform
+  int tv0[kCB];
+#pragma unroll
+  for (int i = 0; i < kCB; ++i) {
+    const int p = p0 + i * NT + tid;
+    tv0[i] = p < p1 ? a.indices[(size_t)row * a.K + p] : -1;
+  }
+  int ptv[kPtPer];
+  if (pt_lds) {
+#pragma unroll
+    for (int j = 0; j < kPtPer; ++j) {
+      const int e = j * NT + tid;
+      ptv[j] = e < a.max_pages ? a.page_table[(size_t)req * a.max_pages + e] : -1;
+    }
+  }
+
   // ---- q fragments: lane holds head 32*wave + lane%32, dims 16*ks + 8*(lane/32) + 0..7
-  // (padded heads read a real head's q; their results are never written).  Loaded first,
-  // so their latency overlaps the index translation.
+  // (padded heads read a real head's q; their results are never written).  Their latency
+  // overlaps the index translation.
   const int hl = lane & 31;
   const int G = lane >> 5;
   const int h = wave * 32 + hl;
@@ -136,39 +167,52 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
   }
+  if (pt_lds) {
+#pragma unroll
+    for (int j = 0; j < kPtPer; ++j)
+      if (j * NT + tid < a.max_pages) sPt[j * NT + tid] = ptv[j];
+  }
+  __syncthreads();
 
   // ---- 1. translate and compact the split's indices --------------------------------
   // Positions are taken in batches of kCB per thread; all index loads of a batch, then all
-  // its page-table loads, are in flight together.
-  int req = 0;
-  bool req_ok = true;
-  if (a.index_mode == 0) {
-    req = a.row_req[row];
-    req_ok = req >= 0 && req < a.B;
-  }
-  constexpr int kCB = 8;
+  // its page-table loads (LDS reads when the row is staged), are in flight together.
   int n_valid = 0;
   for (int base = p0; base < p1; base += kCB * NT) {
     int tv[kCB];
 #pragma unroll
     for (int i = 0; i < kCB; ++i) {
       const int p = base + i * NT + tid;
-      tv[i] = p < p1 ? a.indices[(size_t)row * a.K + p] : -1;
+      tv[i] = base == p0 ? tv0[i] : (p < p1 ? a.indices[(size_t)row * a.K + p] : -1);
     }
     int slot[kCB];
     bool ok[kCB];
+    if (a.index_mode == 0) {
 #pragma unroll
-    for (int i = 0; i < kCB; ++i) {
-      const int t = tv[i];
-      ok[i] = false;
-      slot[i] = 0;
-      if (a.index_mode == 0) {
-        if (req_ok && t >= 0 && (t >> a.ps_log2) < a.max_pages)
-          slot[i] = a.page_table[(size_t)req * a.max_pages + (t >> a.ps_log2)];   // page for now
-        ok[i] = req_ok && t >= 0 && (t >> a.ps_log2) < a.max_pages;
+      for (int i = 0; i < kCB; ++i) {
+        ok[i] = req_ok && tv[i] >= 0 && (tv[i] >> a.ps_log2) < a.max_pages;
+        slot[i] = 0;
+      }
+      // the page of each position for now; each branch consumes its own loads (the empty
+      // asm), so no wait after the join has to cover both kinds of load
+      if (pt_lds) {
+#pragma unroll
+        for (int i = 0; i < kCB; ++i)
+          if (ok[i]) slot[i] = sPtL[tv[i] >> a.ps_log2];
+#pragma unroll
+        for (int i = 0; i < kCB; ++i) asm volatile("" : "+v"(slot[i]));
       } else {
-        ok[i] = t >= 0 && t < a.num_slots;
-        slot[i] = t;
+#pragma unroll
+        for (int i = 0; i < kCB; ++i)
+          if (ok[i]) slot[i] = a.page_table[(size_t)req * a.max_pages + (tv[i] >> a.ps_log2)];
+#pragma unroll
+        for (int i = 0; i < kCB; ++i) asm volatile("" : "+v"(slot[i]));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kCB; ++i) {
+        ok[i] = tv[i] >= 0 && tv[i] < a.num_slots;
+        slot[i] = tv[i];
       }
     }
     unsigned long long m[kCB];
