@@ -244,6 +244,23 @@ smla_status sparse_mla_indexer_logits(const void* q_codes, const float* weights,
 smla_status sparse_mla_indexer_topk(const float* logits, const int32_t* row_len, int32_t rows,
                                     int32_t width, int32_t topk, int32_t* indices, void* stream);
 
+/* Once-per-step global index build: translate request-local top-k positions into global
+ * cache slots, so that the decode calls of every layer in the step read them in
+ * SMLA_IDX_GLOBAL mode without the block-table lookups (the once-per-step sparse index
+ * build reused across layers: prhub vllm#43827, implementation breakdown 3; the translation
+ * itself is vllm#43477's block-table conversion, key code excerpts: forward_mqa).
+ *   slots[r][j] = page_table[row_req[r]][t / page_size] * page_size + t % page_size,
+ *   t = indices[r][j]; -1 where the decode path would mask the entry (t < 0, the page
+ *   index >= max_pages, a page id outside [0, num_pages), row_req outside [0, num_requests)).
+ *   indices, slots int32 [rows][topk]; row_req int32 [rows];
+ *   page_table int32 [num_requests][max_pages]  (device, caller-owned)
+ * page_size a power of two <= 1024.  No allocation; asynchronous.
+ * Errors: BAD_SHAPE, NULL_ARG, MISALIGNED, HIP. */
+smla_status sparse_mla_translate_indices(const int32_t* indices, const int32_t* row_req,
+                                        const int32_t* page_table, int32_t rows, int32_t topk,
+                                        int32_t num_requests, int32_t max_pages, int32_t page_size,
+                                        int32_t num_pages, int32_t* slots, void* stream);
+
 /* Test helper: decode n cache slots (global slot numbers, device int32 [n]) into bf16
  * rows out[n][576] with the same device code the decode kernel uses for its gather and
  * dequantisation.  Slots outside [0, num_pages*page_size) give a zero row.

@@ -42,6 +42,7 @@ EXPORTED = [
     "sparse_mla_status_string", "sparse_mla_version",
     "sparse_mla_indexer_logits",
     "sparse_mla_indexer_topk",
+    "sparse_mla_translate_indices",
 ]
 
 
@@ -93,6 +94,8 @@ def load_library(path: str = LIB_PATH):
     lib.sparse_mla_indexer_logits.argtypes = [vp, f32p, vp, i32p, i32p, i32, i32, i32, i32, i32, i32,
                                               i32, f32p, vp]
     lib.sparse_mla_indexer_topk.argtypes = [f32p, i32p, i32, i32, i32, i32p, vp]
+    lib.sparse_mla_translate_indices.argtypes = [i32p, i32p, i32p, i32, i32, i32, i32, i32, i32, i32p, vp]
+    lib.sparse_mla_translate_indices.restype = ctypes.c_int
     lib.sparse_mla_indexer_logits.restype = ctypes.c_int
     lib.sparse_mla_indexer_topk.restype = ctypes.c_int
     lib.sparse_mla_cache_store.restype = ctypes.c_int
@@ -357,6 +360,26 @@ def indexer_topk(logits: torch.Tensor, row_len: torch.Tensor, topk: int, out: to
         _check("sparse_mla_indexer_topk",
                lib.sparse_mla_indexer_topk(_ptr(logits), _ptr(row_len), R, width, int(topk), _ptr(out),
                                            _stream(stream)))
+    return out
+
+
+def translate_indices(indices: torch.Tensor, row_req: torch.Tensor, page_table: torch.Tensor,
+                      page_size: int, num_pages: int, out: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """Request-local top-k positions -> global slots (int32 [R, K], -1 where masked)."""
+    lib = load_library()
+    dev = indices.device
+    _require(indices, "indices", torch.int32, dev)
+    _require(row_req, "row_req", torch.int32, dev)
+    _require(page_table, "page_table", torch.int32, dev)
+    R, K = int(indices.shape[0]), int(indices.shape[1])
+    if out is None:
+        out = torch.empty((R, K), dtype=torch.int32, device=dev)
+    _require(out, "out", torch.int32, dev)
+    with torch.cuda.device(dev):
+        _check("sparse_mla_translate_indices",
+               lib.sparse_mla_translate_indices(_ptr(indices), _ptr(row_req), _ptr(page_table), R, K,
+                                                int(page_table.shape[0]), int(page_table.shape[1]),
+                                                int(page_size), int(num_pages), _ptr(out), _stream(stream)))
     return out
 
 

@@ -328,6 +328,25 @@ smla_status sparse_mla_indexer_topk(const float* logits, const int32_t* row_len,
   return SMLA_OK;
 }
 
+smla_status sparse_mla_translate_indices(const int32_t* indices, const int32_t* row_req,
+                                        const int32_t* page_table, int32_t rows, int32_t topk,
+                                        int32_t num_requests, int32_t max_pages, int32_t page_size,
+                                        int32_t num_pages, int32_t* slots, void* stream) {
+  const int l = log2_exact(page_size);
+  if (rows < 0 || topk < 1 || num_requests < 1 || max_pages < 1 || num_pages < 1 || l < 0 ||
+      page_size > 1024 || (int64_t)num_pages * page_size > INT32_MAX || (int64_t)rows * topk > INT32_MAX)
+    return SMLA_ERR_BAD_SHAPE;
+  if (rows == 0) return SMLA_OK;
+  if (indices == nullptr || row_req == nullptr || page_table == nullptr || slots == nullptr)
+    return SMLA_ERR_NULL_ARG;
+  if (!aligned(indices, 4) || !aligned(row_req, 4) || !aligned(page_table, 4) || !aligned(slots, 4))
+    return SMLA_ERR_MISALIGNED;
+  if (smla::launch_translate(indices, row_req, page_table, rows, topk, num_requests, max_pages, l, num_pages,
+                             slots, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return SMLA_ERR_HIP;
+  return SMLA_OK;
+}
+
 smla_status sparse_mla_read_index_error(const smla_plan* plan, const void* workspace,
                                         int32_t* row_pos, void* stream) {
   const PlanImpl* pi = as_impl(plan);

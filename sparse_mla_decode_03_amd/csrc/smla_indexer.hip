@@ -415,7 +415,41 @@ __global__ __launch_bounds__(kTopkThreads) void indexer_topk_kernel(IndexerTopkA
   }
 }
 
+// ---- global index build ----------------------------------------------------------------
+// Request-local top-k positions to global cache slots through the block table, once per
+// step, for the decode calls of every layer to read in GLOBAL mode (the once-per-step
+// sparse index build cached in the step's metadata, prhub vllm#43827 implementation
+// breakdown 3).  Entries the decode path would mask (-1, out of the table, a page id outside
+// the pool, a request out of range) become -1.
+__global__ __launch_bounds__(256) void translate_kernel(const int32_t* __restrict__ idx,
+                                                        const int32_t* __restrict__ row_req,
+                                                        const int32_t* __restrict__ page_table,
+                                                        int rows, int topk, int num_requests,
+                                                        int max_pages, int ps_log2, int num_pages,
+                                                        int32_t* __restrict__ out) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (long long)rows * topk) return;
+  const int r = (int)(e / topk);
+  const int t = idx[e];
+  const int req = row_req[r];
+  int slot = -1;
+  if (t >= 0 && req >= 0 && req < num_requests && (t >> ps_log2) < max_pages) {
+    const int pg = page_table[(size_t)req * max_pages + (t >> ps_log2)];
+    if (pg >= 0 && pg < num_pages) slot = (pg << ps_log2) | (t & ((1 << ps_log2) - 1));
+  }
+  out[e] = slot;
+}
+
 }  // namespace
+
+hipError_t launch_translate(const int32_t* idx, const int32_t* row_req, const int32_t* page_table,
+                            int rows, int topk, int num_requests, int max_pages, int ps_log2,
+                            int num_pages, int32_t* out, hipStream_t st) {
+  const long long n = (long long)rows * topk;
+  hipLaunchKernelGGL(translate_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, idx, row_req,
+                     page_table, rows, topk, num_requests, max_pages, ps_log2, num_pages, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_indexer_logits(const IndexerLogitsArgs& a, int next_n, int num_requests, hipStream_t st) {
   const int chunks = (a.width / kKeyPage + kChunkPages - 1) / kChunkPages;

@@ -53,5 +53,8 @@ hipError_t launch_store(const uint16_t* latent, const uint16_t* rope, const int3
 
 hipError_t launch_indexer_logits(const IndexerLogitsArgs& a, int next_n, int num_requests, hipStream_t st);
 hipError_t launch_indexer_topk(const IndexerTopkArgs& a, int rows, hipStream_t st);
+hipError_t launch_translate(const int32_t* idx, const int32_t* row_req, const int32_t* page_table,
+                            int rows, int topk, int num_requests, int max_pages, int ps_log2,
+                            int num_pages, int32_t* out, hipStream_t st);
 
 }  // namespace smla

@@ -242,3 +242,16 @@ def test_indexer_validation(lib):
     assert tk(v(FAKE + 4), v(FAKE), 3, 64, 16, v(FAKE), None) == B.ERR_MISALIGNED
     assert tk(v(FAKE), v(FAKE), 3, 66, 16, v(FAKE), None) == B.ERR_BAD_SHAPE
     assert tk(None, None, 0, 64, 16, None, None) == B.OK
+
+
+def test_translate_validation(lib):
+    v = ctypes.c_void_p
+    tr = lib.sparse_mla_translate_indices
+    # (indices, row_req, page_table, rows, topk, num_requests, max_pages, page_size, num_pages, slots, stream)
+    assert tr(v(FAKE), v(FAKE), v(FAKE), 4, 16, 2, 8, 48, 100, v(FAKE), None) == B.ERR_BAD_SHAPE
+    assert tr(v(FAKE), v(FAKE), v(FAKE), 4, 0, 2, 8, 64, 100, v(FAKE), None) == B.ERR_BAD_SHAPE
+    assert tr(v(FAKE), v(FAKE), v(FAKE), -1, 16, 2, 8, 64, 100, v(FAKE), None) == B.ERR_BAD_SHAPE
+    assert tr(v(FAKE), v(FAKE), v(FAKE), 4, 16, 2, 8, 64, 0, v(FAKE), None) == B.ERR_BAD_SHAPE
+    assert tr(None, v(FAKE), v(FAKE), 4, 16, 2, 8, 64, 100, v(FAKE), None) == B.ERR_NULL_ARG
+    assert tr(v(FAKE), v(FAKE), v(FAKE), 4, 16, 2, 8, 64, 100, v(FAKE + 2), None) == B.ERR_MISALIGNED
+    assert tr(None, None, None, 0, 16, 2, 8, 64, 100, None, None) == B.OK

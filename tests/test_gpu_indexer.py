@@ -193,3 +193,43 @@ def test_indexer_then_decode():
     out, lse = gpu_decode(dinp)
     o, l = oracle_decode(dinp)
     compare(out, lse, o, l, what="indexer -> decode")
+
+
+@pytest.mark.parametrize("name,full", [("b128_mtp4_h128_fp8", False), ("ragged_b256_h64_fp8", False),
+                                       ("b128_mtp4_h128_fp8", True)])
+def test_global_index_build_then_global_decode(name, full):
+    """sparse_mla_translate_indices against the oracle's block-table translation (exact),
+    masked entries as -1; then the decode in GLOBAL mode over the built slots gives the
+    same bits as the decode in LOGICAL mode over the positions."""
+    spec = W.WORKLOADS[name]
+    if not full:
+        spec = spec.scaled(num_requests=8 if name.startswith("ragged") else 3, ctx_hi=20000)
+    inp = W.make_inputs(spec, 51, device="cpu", cache_device=DEV if full else None)
+    idx = inp.indices.clone()
+    # plant entries the decode path masks: below -1, past the table, a request's page id
+    # outside the pool (a copy of the table is used for that)
+    idx[0, 5] = -7
+    idx[1, 9] = inp.page_table.shape[1] * spec.page_size + 3
+    pt = inp.page_table.clone()
+    b1 = int(inp.row_req[min(2, inp.num_rows - 1)])
+    pt[b1, 0] = inp.num_pages + 11
+    announce(f"index build {name} full={full} R={inp.num_rows}")
+    slots = B.translate_indices(idx.to(DEV), inp.row_req.to(DEV), pt.to(DEV), spec.page_size, inp.num_pages)
+    torch.cuda.synchronize()
+    got = slots.cpu().numpy()
+    ptn, rr = pt.numpy(), inp.row_req.numpy()
+    for r in range(inp.num_rows):
+        row = idx[r].numpy()
+        bad = (row < 0) | (row // spec.page_size >= ptn.shape[1])
+        page = np.where(bad, 0, ptn[rr[r], np.where(bad, 0, row // spec.page_size)])
+        bad |= (page < 0) | (page >= inp.num_pages)
+        keep = np.where(~bad)[0]
+        pos, want = orc.translate(np.where(bad, -1, row), orc.IDX_LOGICAL, int(rr[r]), ptn, spec.page_size)
+        assert np.array_equal(pos, keep)
+        assert np.array_equal(got[r, keep], want) and np.all(got[r, bad] == -1)
+    # the same decode, LOGICAL over positions vs GLOBAL over the built slots
+    out_l, lse_l = gpu_decode(inp, indices=idx, page_table=pt)
+    out_g, lse_g = gpu_decode(inp, indices=slots.cpu(), index_mode=B.IDX_GLOBAL, page_table=pt)
+    torch.cuda.synchronize()
+    assert torch.equal(out_l.view(torch.int16), out_g.view(torch.int16))
+    assert torch.equal(lse_l, lse_g)
