@@ -93,14 +93,19 @@ def cache_store_measure(B, torch, dev, n_tokens: int, reps: int):
                          "bytes_per_launch": nbytes}}
 
 
-def mixed_measure(B, W, torch, dev, name: str, reps: int):
-    """One decode launch over a batch that mixes prefill chunks and decode rows."""
+def kv_code(B, name: str) -> int:
+    return {"bf16": B.KV_BF16, "fp8": B.KV_FP8_UE8M0, "fp8t": B.KV_FP8_TENSOR}[name]
+
+
+def decode_measure(B, W, torch, dev, name: str, reps: int, seed: int):
+    """Time one decode launch of a workload other than the headline one: the batch that
+    mixes prefill chunks and decode rows, or the headline shape over another cache format."""
     spec = W.WORKLOADS[name]
-    inp = W.make_inputs(spec, 41, device=dev, cache_device=dev)
+    inp = W.make_inputs(spec, seed, device=dev, cache_device=dev)
     R, H = inp.num_rows, inp.num_heads
     prob = B.make_problem(R, spec.num_requests, H, spec.topk, spec.page_size, inp.num_pages,
-                          inp.page_table.shape[1], B.KV_FP8_UE8M0, B.IDX_LOGICAL, 0, 0,
-                          spec.softmax_scale)
+                          inp.page_table.shape[1], kv_code(B, spec.kv_format), B.IDX_LOGICAL, 0, 0,
+                          spec.softmax_scale, spec.kv_scale)
     info = B.plan(prob)
     out = torch.empty((R, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((R, H), dtype=torch.float32, device=dev)
@@ -126,7 +131,8 @@ def mixed_measure(B, W, torch, dev, name: str, reps: int):
     n = inp.num_valid()
     flops = W.algorithmic_flops(inp)
     counts = torch.bincount(inp.row_req.long().cpu()).tolist()
-    return {"workload": name, "rows": R, "requests": spec.num_requests,
+    del inp
+    return {"workload": name, "kv_format": spec.kv_format, "rows": R, "requests": spec.num_requests,
             "rows_per_request": {str(k): counts.count(k) for k in sorted(set(counts))},
             "attended_entries": n, "num_splits": info.num_splits,
             "launch_ms_mean": mean_s * 1e3, "launch_ms_p50": ms[len(ms) // 2],
@@ -197,7 +203,7 @@ def cpu_baseline(inp, budget_s: float):
 
     R = inp.num_rows
     rows_done, entries, elapsed = 0, 0, 0.0
-    kvf = orc.KV_FP8_UE8M0 if inp.spec.kv_format == "fp8" else orc.KV_BF16
+    kvf = {"bf16": orc.KV_BF16, "fp8": orc.KV_FP8_UE8M0, "fp8t": orc.KV_FP8_TENSOR}[inp.spec.kv_format]
     qb = inp.q.cpu().view(torch.int16).numpy().view(np.uint16)
     idx = inp.indices.cpu()
     rr = inp.row_req.cpu()
@@ -215,7 +221,7 @@ def cpu_baseline(inp, budget_s: float):
         sinks = None if inp.sinks is None else inp.sinks.cpu().numpy()
         t0 = time.perf_counter()
         orc.sparse_mla_decode(qb, sub, kvf, inp.spec.page_size, idx.numpy(), rr.numpy(), npt,
-                              sinks, inp.spec.softmax_scale, rows=rows)
+                              sinks, inp.spec.softmax_scale, rows=rows, kv_scale=inp.spec.kv_scale)
         elapsed += time.perf_counter() - t0
         entries += int((idx[rows] != -1).sum())
         rows_done += len(rows)
@@ -243,6 +249,9 @@ def main() -> int:
                     help="tokens per timed cache-store launch (0: skip that measurement)")
     ap.add_argument("--mixed", default="mixed_b24_h128_fp8",
                     help="prefill+decode batch measured beside the decode ('' to skip)")
+    ap.add_argument("--fp8-tensor", default="b128_mtp4_h128_fp8t",
+                    help="also time this workload over the contiguous per-tensor FP8 cache "
+                         "(empty: skip)")
     ap.add_argument("--indexer", default="idx_b128_mtp4_h64",
                     help="indexer workload measured beside the decode ('' to skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -278,10 +287,10 @@ def main() -> int:
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
     R, H, K = inp.num_rows, inp.num_heads, spec.topk
-    kvf = B.KV_FP8_UE8M0 if spec.kv_format == "fp8" else B.KV_BF16
+    kvf = kv_code(B, spec.kv_format)
     prob = B.make_problem(R, spec.num_requests, H, K, spec.page_size, inp.num_pages,
                           inp.page_table.shape[1], kvf, B.IDX_LOGICAL, spec.num_splits, 0,
-                          spec.softmax_scale)
+                          spec.softmax_scale, spec.kv_scale)
     info = B.plan(prob)
     out = torch.empty((R, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((R, H), dtype=torch.float32, device=dev)
@@ -347,7 +356,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": spec.name, "requests": spec.num_requests, "rows": R, "heads": H,
-            "topk": K, "kv_format": "fp8_e4m3+ue8m0" if spec.kv_format == "fp8" else "bf16",
+            "topk": K, "kv_format": {"fp8": "fp8_e4m3+ue8m0", "fp8t": "fp8_e4m3_per_tensor",
+                                          "bf16": "bf16"}[spec.kv_format],
             "page_size": spec.page_size, "pages": inp.num_pages, "num_splits": info.num_splits,
             "attended_entries_per_step": n_valid,
             "tokens_per_s": R * K_steps / wall,
@@ -381,7 +391,7 @@ def main() -> int:
                                 stream=stream)
     gprob = B.make_problem(R, spec.num_requests, H, K, spec.page_size, inp.num_pages,
                            inp.page_table.shape[1], kvf, B.IDX_GLOBAL, spec.num_splits, 0,
-                           spec.softmax_scale)
+                           spec.softmax_scale, spec.kv_scale)
     ginfo = B.plan(gprob)
 
     def timed_ms(fn, reps=20):
@@ -422,7 +432,9 @@ def main() -> int:
     if args.store_tokens > 0:
         res["cache_store"] = cache_store_measure(B, torch, dev, args.store_tokens, 20)
     if args.mixed:
-        res["mixed_prefill_decode"] = mixed_measure(B, W, torch, dev, args.mixed, 10)
+        res["mixed_prefill_decode"] = decode_measure(B, W, torch, dev, args.mixed, 10, 41)
+    if args.fp8_tensor:
+        res["per_tensor_fp8"] = decode_measure(B, W, torch, dev, args.fp8_tensor, 20, 43)
     if args.indexer:
         res["indexer"] = indexer_measure(B, W, torch, dev, args.indexer, 20)
     if not args.no_cpu_baseline:

@@ -50,6 +50,12 @@
  *                      S.1111.111 = NaN); a scale byte is UE8M0 (power of two, 255 = NaN).
  *                      The dequantized value is exact in bf16 for scale bytes 10..246;
  *                      outside that range the kernel's bf16 rounding applies.
+ *   SMLA_KV_FP8_TENSOR page = e4m3fn[page_size][576]; bytes per page 576*page_size.  The
+ *                      contiguous per-tensor FP8 cache of prhub vllm#43827 (implementation
+ *                      breakdown 1 and 4: a contiguous bf16 or fp8_e4m3 cache, bmm1 scale =
+ *                      softmax scale * kv scale, bmm2 scale = kv scale): k[d] = e4m3fn(code[d])
+ *                      * kv_scale for all 576 dims.  The kernel applies kv_scale as those
+ *                      two scalar factors (scores and output); q stays bf16.
  * A cache slot s lives in page s / page_size at in-page row s % page_size.
  *
  * Conventions
@@ -102,7 +108,7 @@ typedef enum {
   SMLA_ERR_BAD_PLAN = 7              /* the plan was not produced by sparse_mla_decode_plan */
 } smla_status;
 
-typedef enum { SMLA_KV_BF16 = 0, SMLA_KV_FP8_UE8M0 = 1 } smla_kv_format;
+typedef enum { SMLA_KV_BF16 = 0, SMLA_KV_FP8_UE8M0 = 1, SMLA_KV_FP8_TENSOR = 2 } smla_kv_format;
 
 /* LOGICAL: idx is a request-local position t; slot = page_table[row_req[r]][t / page_size]
  * * page_size + t % page_size (the block-table translation that the vLLM SM120 backend
@@ -133,6 +139,8 @@ typedef struct {
   int32_t num_splits;        /* 0: the planner chooses; > 0: forced S (chunks of ceil(K/S) positions) */
   int32_t flags;             /* SMLA_F_* */
   float softmax_scale;       /* multiplies q.k; the sink lives in the same (scaled) logit domain */
+  float kv_scale;            /* SMLA_KV_FP8_TENSOR: the one scale of every cache value (finite,
+                                > 0); ignored for the other formats */
 } smla_problem;
 
 /* Host-side plan.  Copyable plain bytes; contents are private to the library. */
@@ -263,7 +271,9 @@ smla_status sparse_mla_translate_indices(const int32_t* indices, const int32_t* 
 
 /* Test helper: decode n cache slots (global slot numbers, device int32 [n]) into bf16
  * rows out[n][576] with the same device code the decode kernel uses for its gather and
- * dequantisation.  Slots outside [0, num_pages*page_size) give a zero row.
+ * dequantisation.  Slots outside [0, num_pages*page_size) give a zero row.  For
+ * SMLA_KV_FP8_TENSOR the row holds the code values e4m3fn(code[d]): the decode applies
+ * kv_scale as two scalar factors, not per element.
  * Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED, MISALIGNED, HIP. */
 smla_status sparse_mla_gather_debug(const void* kv_cache, int32_t kv_format, int32_t page_size,
                                     int32_t num_pages, const int32_t* slots, int32_t n, void* out,

@@ -13,6 +13,7 @@ from .sparse_mla_oracle import (  # noqa: F401
     IDX_LOGICAL,
     KV_BF16,
     KV_FP8_UE8M0,
+    KV_FP8_TENSOR,
     QK_DIM,
     V_DIM,
     attend,

@@ -44,6 +44,8 @@ BF16_ENTRY_BYTES = 1152
 
 KV_BF16 = 0
 KV_FP8_UE8M0 = 1
+KV_FP8_TENSOR = 2
+FP8_TENSOR_ENTRY_BYTES = 576
 IDX_LOGICAL = 0
 IDX_GLOBAL = 1
 
@@ -93,10 +95,13 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------------------
 
 def page_bytes(kv_format: int, page_size: int) -> int:
-    return (FP8_ENTRY_BYTES if kv_format == KV_FP8_UE8M0 else BF16_ENTRY_BYTES) * page_size
+    entry = {KV_BF16: BF16_ENTRY_BYTES, KV_FP8_UE8M0: FP8_ENTRY_BYTES,
+             KV_FP8_TENSOR: FP8_TENSOR_ENTRY_BYTES}[kv_format]
+    return entry * page_size
 
 
-def decode_entries(cache: np.ndarray, kv_format: int, page_size: int, slots) -> np.ndarray:
+def decode_entries(cache: np.ndarray, kv_format: int, page_size: int, slots,
+                   kv_scale: float = 1.0) -> np.ndarray:
     """Dequantize cache slots into float64 rows k[n, 576].
 
     `cache` is the whole paged buffer as bytes (any shape; it is flattened).  A slot is
@@ -104,7 +109,9 @@ def decode_entries(cache: np.ndarray, kv_format: int, page_size: int, slots) -> 
     that the kernel of sglang#24692 reads through fp8 / uint8 / bf16 views of the same
     buffer (implementation breakdown item 2): e4m3fn latent [ps][512] at byte 0, bf16
     rope [ps][64] at byte 512*ps, UE8M0 scales [ps][8] at byte 640*ps.  The BF16 page
-    is bf16 [ps][576].
+    is bf16 [ps][576].  The per-tensor FP8 page (the contiguous fp8_e4m3 cache of
+    vllm#43827, implementation breakdown 1 and 4) is e4m3fn [ps][576], every value times
+    the one tensor scale `kv_scale`.
     """
     flat = np.ascontiguousarray(cache).reshape(-1).view(np.uint8)
     slots = np.asarray(slots, dtype=np.int64).reshape(-1)
@@ -120,6 +127,11 @@ def decode_entries(cache: np.ndarray, kv_format: int, page_size: int, slots) -> 
         offs = base + row * BF16_ENTRY_BYTES
         raw = flat[offs[:, None] + np.arange(BF16_ENTRY_BYTES)[None, :]]
         out[:] = bf16_bits_to_f64(raw.view(np.uint16).reshape(n, QK_DIM))
+        return out
+    if kv_format == KV_FP8_TENSOR:
+        offs = base + row * FP8_TENSOR_ENTRY_BYTES
+        codes = flat[offs[:, None] + np.arange(FP8_TENSOR_ENTRY_BYTES)[None, :]]
+        out[:] = e4m3fn_to_f64(codes) * float(kv_scale)
         return out
     if kv_format != KV_FP8_UE8M0:
         raise ValueError(f"unknown kv_format {kv_format}")
@@ -179,16 +191,17 @@ def attend(q: np.ndarray, k: np.ndarray, scale: float, sink) -> tuple[np.ndarray
     return o, lse
 
 
-def _row_inputs(r, q_bits, cache, kv_format, page_size, indices, row_req, page_table, index_mode):
+def _row_inputs(r, q_bits, cache, kv_format, page_size, indices, row_req, page_table, index_mode,
+                kv_scale=1.0):
     req = int(row_req[r]) if index_mode == IDX_LOGICAL else -1
     pos, slots = translate(indices[r], index_mode, req, page_table, page_size)
-    k = decode_entries(cache, kv_format, page_size, slots)
+    k = decode_entries(cache, kv_format, page_size, slots, kv_scale)
     q = bf16_bits_to_f64(q_bits[r])
     return q, pos, k
 
 
 def sparse_mla_decode(q_bits, cache, kv_format, page_size, indices, row_req, page_table,
-                      sinks, softmax_scale, index_mode=IDX_LOGICAL, rows=None):
+                      sinks, softmax_scale, index_mode=IDX_LOGICAL, rows=None, kv_scale=1.0):
     """Final decode output for the given rows.
 
     q_bits: uint16 [R, H, 576] (bf16 bit patterns); cache: uint8 paged buffer;
@@ -204,7 +217,7 @@ def sparse_mla_decode(q_bits, cache, kv_format, page_size, indices, row_req, pag
     lses = np.zeros((len(rows), H))
     for i, r in enumerate(rows):
         q, _, k = _row_inputs(r, q_bits, cache, kv_format, page_size, indices, row_req,
-                              page_table, index_mode)
+                              page_table, index_mode, kv_scale)
         outs[i], lses[i] = attend(q, k, softmax_scale, sink)
     return outs, lses
 
@@ -217,7 +230,7 @@ def chunk_bounds(topk: int, num_splits: int):
 
 def sparse_mla_decode_partials(q_bits, cache, kv_format, page_size, indices, row_req,
                                page_table, softmax_scale, num_splits, index_mode=IDX_LOGICAL,
-                               rows=None):
+                               rows=None, kv_scale=1.0):
     """Sink-free per-chunk partials o_c [n_rows, S, H, 512] and lse_c [n_rows, S, H]."""
     q_bits = np.asarray(q_bits)
     indices = np.asarray(indices)
@@ -228,7 +241,7 @@ def sparse_mla_decode_partials(q_bits, cache, kv_format, page_size, indices, row
     lse_c = np.full((len(rows), num_splits, H), -np.inf)
     for i, r in enumerate(rows):
         q, pos, k = _row_inputs(r, q_bits, cache, kv_format, page_size, indices, row_req,
-                                page_table, index_mode)
+                                page_table, index_mode, kv_scale)
         for c, (lo, hi) in enumerate(bounds):
             sel = (pos >= lo) & (pos < hi)
             o_c[i, c], lse_c[i, c] = attend(q, k[sel], softmax_scale, None)

@@ -30,6 +30,8 @@ ERR_BAD_PLAN = 7
 
 KV_BF16 = 0
 KV_FP8_UE8M0 = 1
+KV_FP8_TENSOR = 2
+ENTRY_BYTES = {0: 1152, 1: 648, 2: 576}    # page bytes = entry bytes * page_size
 IDX_LOGICAL = 0
 IDX_GLOBAL = 1
 F_PARTIALS_ONLY = 1
@@ -54,6 +56,7 @@ class Problem(ctypes.Structure):
         ("max_pages_per_req", ctypes.c_int32), ("kv_format", ctypes.c_int32),
         ("index_mode", ctypes.c_int32), ("num_splits", ctypes.c_int32),
         ("flags", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("kv_scale", ctypes.c_float),
     ]
 
 
@@ -138,10 +141,10 @@ class PlanInfo:
 
 def make_problem(num_rows, num_requests, num_heads, topk, page_size, num_pages,
                  max_pages_per_req, kv_format, index_mode=IDX_LOGICAL, num_splits=0, flags=0,
-                 softmax_scale=1.0 / math.sqrt(576.0)) -> Problem:
+                 softmax_scale=1.0 / math.sqrt(576.0), kv_scale=1.0) -> Problem:
     return Problem(int(num_rows), int(num_requests), int(num_heads), int(topk), int(page_size),
                    int(num_pages), int(max_pages_per_req), int(kv_format), int(index_mode),
-                   int(num_splits), int(flags), float(softmax_scale))
+                   int(num_splits), int(flags), float(softmax_scale), float(kv_scale))
 
 
 def plan(problem: Problem, num_cus: int = 0) -> PlanInfo:
@@ -168,7 +171,7 @@ def run(info: PlanInfo, q, kv_cache, indices, row_req, page_table, sinks, out, l
 
 def _kv_format_of(kv_format) -> int:
     if isinstance(kv_format, str):
-        return KV_FP8_UE8M0 if kv_format == "fp8" else KV_BF16
+        return {"fp8": KV_FP8_UE8M0, "fp8t": KV_FP8_TENSOR, "bf16": KV_BF16}[kv_format]
     return int(kv_format)
 
 
@@ -185,7 +188,8 @@ def sparse_mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, indices: torch.Te
                       row_req: Optional[torch.Tensor], page_table: Optional[torch.Tensor],
                       sinks: Optional[torch.Tensor], kv_format, page_size: int,
                       softmax_scale: float, index_mode: int = IDX_LOGICAL, num_splits: int = 0,
-                      flags: int = 0, num_cus: int = 0, stream=None, return_info: bool = False):
+                      flags: int = 0, num_cus: int = 0, stream=None, return_info: bool = False,
+                      kv_scale: float = 1.0):
     """Convenience wrapper: plan, allocate out/lse/workspace with torch, run.
 
     q bf16 [R,H,576]; kv_cache uint8 [num_pages, page_bytes]; indices int32 [R,K];
@@ -218,10 +222,10 @@ def sparse_mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, indices: torch.Te
         if sinks.numel() != H:
             raise ValueError("sinks must hold one value per head")
     kvf = _kv_format_of(kv_format)
-    if kv_cache.dim() != 2 or kv_cache.shape[1] != (648 if kvf == KV_FP8_UE8M0 else 1152) * page_size:
+    if kv_cache.dim() != 2 or kv_cache.shape[1] != ENTRY_BYTES[kvf] * page_size:
         raise ValueError("kv_cache must be [num_pages, page_bytes] for this format and page size")
-    prob = make_problem(R, B, H, K, page_size, kv_cache.shape[0], P, _kv_format_of(kv_format),
-                        index_mode, num_splits, flags, softmax_scale)
+    prob = make_problem(R, B, H, K, page_size, kv_cache.shape[0], P, kvf,
+                        index_mode, num_splits, flags, softmax_scale, kv_scale)
     with torch.cuda.device(dev):
         info = plan(prob, num_cus)
         ws = (torch.empty(info.workspace_bytes, dtype=torch.uint8, device=dev)
@@ -269,8 +273,7 @@ def gather_debug(kv_cache: torch.Tensor, kv_format, page_size: int, slots: torch
     dev = kv_cache.device
     _require(kv_cache, "kv_cache", torch.uint8, dev)
     _require(slots, "slots", torch.int32, dev)
-    if kv_cache.dim() != 2 or kv_cache.shape[1] != (648 if _kv_format_of(kv_format) == KV_FP8_UE8M0
-                                                    else 1152) * page_size:
+    if kv_cache.dim() != 2 or kv_cache.shape[1] != ENTRY_BYTES[_kv_format_of(kv_format)] * page_size:
         raise ValueError("kv_cache must be [num_pages, page_bytes] for this format and page size")
     n = slots.numel()
     out = torch.empty((n, 576), dtype=torch.bfloat16, device=dev)

@@ -67,7 +67,8 @@ smla_status check_problem(const smla_problem* p) {
   if (p->topk % 4 != 0) return SMLA_ERR_MISALIGNED;
   if (p->num_heads % 16 != 0 || p->num_heads < 16 || p->num_heads > SMLA_MAX_HEADS)
     return SMLA_ERR_UNSUPPORTED;
-  if (p->kv_format != SMLA_KV_BF16 && p->kv_format != SMLA_KV_FP8_UE8M0) return SMLA_ERR_UNSUPPORTED;
+  if (p->kv_format != SMLA_KV_BF16 && p->kv_format != SMLA_KV_FP8_UE8M0 && p->kv_format != SMLA_KV_FP8_TENSOR)
+    return SMLA_ERR_UNSUPPORTED;
   if (p->index_mode != SMLA_IDX_LOGICAL && p->index_mode != SMLA_IDX_GLOBAL) return SMLA_ERR_UNSUPPORTED;
   if (p->flags & ~(SMLA_F_PARTIALS_ONLY | SMLA_F_CHECK_INDICES)) return SMLA_ERR_UNSUPPORTED;
   const int l = log2_exact(p->page_size);
@@ -82,6 +83,8 @@ smla_status check_problem(const smla_problem* p) {
   if (p->num_splits < 0 || p->num_splits > SMLA_MAX_SPLITS || p->num_splits > p->topk)
     return SMLA_ERR_BAD_SHAPE;
   if (!isfinite(p->softmax_scale)) return SMLA_ERR_BAD_SHAPE;
+  if (p->kv_format == SMLA_KV_FP8_TENSOR && !(isfinite(p->kv_scale) && p->kv_scale > 0.f))
+    return SMLA_ERR_BAD_SHAPE;
   return SMLA_OK;
 }
 
@@ -194,7 +197,9 @@ smla_status sparse_mla_decode_run(const smla_plan* plan, const void* q, const vo
   a.num_slots = p.num_pages * p.page_size;
   a.max_pages = logical ? p.max_pages_per_req : 0;
   a.index_mode = p.index_mode;
-  a.scale_log2 = p.softmax_scale * 1.4426950408889634f;
+  const bool tensor_fp8 = p.kv_format == SMLA_KV_FP8_TENSOR;
+  a.scale_log2 = p.softmax_scale * (tensor_fp8 ? p.kv_scale : 1.0f) * 1.4426950408889634f;
+  a.out_scale = tensor_fp8 ? p.kv_scale : 1.0f;
   if (p.flags & SMLA_F_CHECK_INDICES) {
     a.err = reinterpret_cast<unsigned long long*>(ws + pi->off_err);
     if (smla::launch_fill_u64(a.err, ~0ull, st) != hipSuccess) return SMLA_ERR_HIP;
@@ -244,7 +249,8 @@ smla_status sparse_mla_merge_partials(const float* partial_o, const float* parti
 smla_status sparse_mla_gather_debug(const void* kv_cache, int32_t kv_format, int32_t page_size,
                                     int32_t num_pages, const int32_t* slots, int32_t n, void* out,
                                     void* stream) {
-  if (kv_format != SMLA_KV_BF16 && kv_format != SMLA_KV_FP8_UE8M0) return SMLA_ERR_UNSUPPORTED;
+  if (kv_format != SMLA_KV_BF16 && kv_format != SMLA_KV_FP8_UE8M0 && kv_format != SMLA_KV_FP8_TENSOR)
+    return SMLA_ERR_UNSUPPORTED;
   const int l = log2_exact(page_size);
   if (n < 0 || num_pages < 1 || page_size < 1 || page_size > 1024 || l < 0 ||
       (int64_t)num_pages * page_size > INT32_MAX)

@@ -82,21 +82,24 @@ __device__ __forceinline__ int acc_row(int r, int G) { return 8 * (r >> 2) + 4 *
 // ahead of the codes, and the other waves read them after the end-of-tile barrier.
 // With three or more waves (one workgroup per CU) the K tile is double-buffered; with
 // fewer, a single tile keeps the workgroup small enough for two per CU.
+// FMT: 0 = BF16 pages, 1 = FP8 with UE8M0 group scales, 2 = per-tensor FP8 (576 codes per
+// entry, contiguous; the tensor scale is folded into the softmax scale and the output).
 template <int NW, int FMT>
 struct Cfg {
-  static constexpr int NL = FMT == 1 ? 16 : 32;         // latent instructions per tile
+  static constexpr int NL = FMT != 0 ? 16 : 32;         // latent instructions per tile
+  static constexpr int RR = FMT == 2 ? 2 : 4;           // rope instructions per tile
   static constexpr int LP = (NL + NW - 1) / NW;         // latent parts per wave
-  static constexpr int RP = (4 + NW - 1) / NW;          // rope parts per wave
+  static constexpr int RP = (RR + NW - 1) / NW;         // rope parts per wave
   // Tiles in flight and K tile buffers.  FP8 stages raw bytes (NS stages) and dequantizes
   // into NK bf16 K tiles; BF16 copies into a ring of NS + 1 K tiles, or synchronously
   // (NS = 0) when the workgroup must stay small enough for two per CU.
   static constexpr bool BIG = NW >= 3;                  // one workgroup per CU
-  static constexpr int NS = FMT == 1 ? (BIG ? 3 : 1) : (BIG ? 2 : 0);
-  static constexpr int NK = FMT == 1 ? (BIG ? 2 : 1) : (BIG ? NS + 1 : 1);
-  static constexpr int RAW_BYTES = FMT == 1 ? NS * 20 * 1024 : 16;
+  static constexpr int NS = FMT != 0 ? (BIG ? 3 : 1) : (BIG ? 2 : 0);
+  static constexpr int NK = FMT != 0 ? (BIG ? 2 : 1) : (BIG ? NS + 1 : 1);
+  static constexpr int RAW_BYTES = FMT != 0 ? NS * 20 * 1024 : 16;
   static constexpr int SCL_BYTES = FMT == 1 ? (NS + 1) * 256 : 16;
   // copies every wave issues per tile at least (the scale wave one more)
-  static constexpr int NMIN = NL / NW + 4 / NW;
+  static constexpr int NMIN = NL / NW + RR / NW;
 };
 
 template <int NW, int FMT>
@@ -279,8 +282,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   constexpr int NDMA = LP + RP + (FMT == 1 ? 1 : 0);   // slot registers (scales last)
   // recomputed from the wave index where needed (cheaper than keeping the flag live)
   auto scale_wave = [&]() { return FMT == 1 && __builtin_amdgcn_readfirstlane(tid >> 6) == NW - 1; };
-  auto lat_token = [&](int ins, int ln) { return FMT == 1 ? 2 * ins + (ln >> 5) : ins; };
-  auto rope_token = [&](int ins, int ln) { return 8 * ins + (ln >> 3); };
+  auto lat_token = [&](int ins, int ln) { return FMT != 0 ? 2 * ins + (ln >> 5) : ins; };
+  // a rope instruction covers 8 tokens (128 bytes each) or, per-tensor FP8, 16 (64 bytes)
+  auto rope_token = [&](int ins, int ln) { return FMT == 2 ? 16 * ins + (ln >> 2) : 8 * ins + (ln >> 3); };
   auto load_slots = [&](int tile, int (&sl)[NDMA]) {
     int ln = lane_id;
     asm volatile("" : "+v"(ln));
@@ -289,7 +293,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < LP; ++j) sl[j] = sSlots[min(t0 + lat_token(min(wave + NW * j, C::NL - 1), ln), kCMax - 1)];
 #pragma unroll
-    for (int j = 0; j < RP; ++j) sl[LP + j] = sSlots[min(t0 + rope_token(min(wave + NW * j, 3), ln), kCMax - 1)];
+    for (int j = 0; j < RP; ++j) sl[LP + j] = sSlots[min(t0 + rope_token(min(wave + NW * j, C::RR - 1), ln), kCMax - 1)];
     // the scale wave copies the scales of the following tile
     if (FMT == 1) sl[LP + RP] = sSlots[min(t0 + kT + (ln >> 1), kCMax - 1)];
   };
@@ -305,9 +309,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // address terms are recomputed at each part instead of being hoisted out of the tile loop
   // (which costs registers, then spills whose reloads would wait on the copies).
   auto issue_part = [&](int tile, int j, const int (&sl)[NDMA], int ln) {
-    const int st = C::NS > 0 ? tile % (FMT == 1 ? C::NS : C::NK) : 0;
-    uint16_t* K = sK + (FMT == 1 ? 0 : st) * kTile;
-    uint8_t* raw = sRaw + (FMT == 1 ? st : 0) * (20 * 1024);
+    const int st = C::NS > 0 ? tile % (FMT != 0 ? C::NS : C::NK) : 0;
+    uint16_t* K = sK + (FMT != 0 ? 0 : st) * kTile;
+    uint8_t* raw = sRaw + (FMT != 0 ? st : 0) * (20 * 1024);
     if (j < LP) {
       const int ins = wave + NW * j;
       if (ins < C::NL) {
@@ -318,6 +322,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         if (FMT == 1) {
           off = fp8_off(slot, fp8_row(slot) * 512u + 16u * (ln & 31));
           dst = raw + ins * 1024;
+        } else if (FMT == 2) {
+          off = (size_t)slot * kQK + 16u * (ln & 31);
+          dst = raw + ins * 1024;
         } else {
           // lane = physical chunk of the destination row; it copies logical chunk lane ^ swz
           off = (size_t)slot * kBf16Entry + 16u * (ln ^ lat_swz(t));
@@ -327,13 +334,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       }
     } else if (j < LP + RP) {
       const int ins = wave + NW * (j - LP);
-      if (ins < 4) {
+      if (ins < C::RR) {
         const int t = rope_token(ins, ln);
         const uint32_t slot = (uint32_t)sl[j];
         size_t off;
         uint8_t* dst;
         if (FMT == 1) {
           off = fp8_off(slot, (512u << a.ps_log2) + fp8_row(slot) * 128u + 16u * (ln & 7));
+          dst = raw + (16 + ins) * 1024;
+        } else if (FMT == 2) {
+          off = (size_t)slot * kQK + 512u + 16u * (ln & 3);
           dst = raw + (16 + ins) * 1024;
         } else {
           off = (size_t)slot * kBf16Entry + 1024u + 16u * ((ln & 7) ^ ((t >> 1) & 7));
@@ -392,7 +402,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // wave-uniform terms: for latent instruction i the unit of token t = 2i + G, dims
   // 16c..16c+15 (c = lane % 32) goes to swizzled chunks 2c and 2c + 1 of row t, and
   // (2c ^ swz(t)) = (2c ^ 4G) ^ U(i) with U(i) = 8(i % 2) + (i / 2) % 4; rope instruction r
-  // puts token 8r + lane / 8, chunk lane % 8, at chunk (lane % 8) ^ (lane / 16) ^ 4(r % 2).
+  // puts token 8r + lane / 8, chunk lane % 8, at chunk (lane % 8) ^ (lane / 16) ^ 4(r % 2);
+  // per-tensor FP8 rope instruction r holds token 16r + lane / 4, codes 16(lane % 4) .. +15,
+  // converted to logical chunks 2(lane % 4) and 2(lane % 4) + 1 of the token's rope row.
   // The lanes with bit 3 of c set convert and write the second 16-byte half of their
   // unit first (they load the two 8-byte halves of the raw unit swapped): each 16-byte
   // write then covers 16 different chunk slots per 16 lanes instead of every other one.
@@ -409,7 +421,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     d.raw = (C::NS > 0 ? tile % C::NS : 0) * (20 * 1024) + wave * 1024 + 16 * ln + 8 * ((c >> 3) & 1);
     d.scl = (tile % (C::NS + 1)) * 256 + 16 * wave + 8 * G_ + (c >> 2);
     d.lat = 1024 * G_ + ((32 * c) ^ (64 * G_) ^ (16 * ((c >> 3) & 1)));
-    d.rope = 128 * (ln >> 3) + 16 * ((ln & 7) ^ (ln >> 4));
+    d.rope = FMT == 2 ? 128 * (ln >> 2) + 16 * ((2 * (ln & 3)) ^ ((ln >> 3) & 7))
+                      : 128 * (ln >> 3) + 16 * ((ln & 7) ^ (ln >> 4));
     d.kb = 2 * kbuf_of(tile) * kTile;
     return d;
   };
@@ -423,7 +436,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       const u32x2 first = *reinterpret_cast<const u32x2*>(sRaw + d.raw + NW * j * 1024);
       const u32x2 second = *reinterpret_cast<const u32x2*>(sRaw + (d.raw ^ 8) + NW * j * 1024);
       u.rv = u32x4{first[0], first[1], second[0], second[1]};
-      u.e = sScl[d.scl + 16 * NW * j];
+      u.e = FMT == 1 ? (uint32_t)sScl[d.scl + 16 * NW * j] : 127u;   // per-tensor FP8: scale 1
     } else {
       u.rv = *reinterpret_cast<const u32x4*>(sRaw + (d.raw & ~15) + (16 + NW * (j - LP)) * 1024);
       u.e = 0u;
@@ -439,6 +452,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         const float sc = ue8m0_scale(u.e);
         *reinterpret_cast<u32x4*>(Kb + 2048 * ins + (d.lat ^ U16)) = dequant8_fp8(u32x2{u.rv[0], u.rv[1]}, sc);
         *reinterpret_cast<u32x4*>(Kb + 2048 * ins + (d.lat ^ U16 ^ 16)) = dequant8_fp8(u32x2{u.rv[2], u.rv[3]}, sc);
+      }
+    } else if (FMT == 2) {
+      const int r = wave + NW * (j - LP);
+      if (r < C::RR) {
+        uint8_t* dst = Kb + 2 * kRopeOff + 2048 * r;
+        *reinterpret_cast<u32x4*>(dst + d.rope) = dequant8_fp8(u32x2{u.rv[0], u.rv[1]}, 1.0f);
+        *reinterpret_cast<u32x4*>(dst + (d.rope ^ 16)) = dequant8_fp8(u32x2{u.rv[2], u.rv[3]}, 1.0f);
       }
     } else {
       const int r = wave + NW * (j - LP);
@@ -463,7 +483,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // After this lane's copies of `tile` have landed: FP8 dequantizes the units it copied
   // into the tile's K buffer.  (BF16 copies land in the K buffer directly.)
   auto finish_tile = [&](int tile) {
-    if (FMT == 1) {
+    if (FMT != 0) {
       int ln = lane_id;
       asm volatile("" : "+v"(ln));
       const DqBase d = dq_base(tile, ln);
@@ -535,7 +555,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     // not); its copies have landed after wait_next (this tile's own group of copies is
     // issued inside QK, after the wait).  Past the last tile this converts the copies of
     // positions past the end into a buffer nobody reads.
-    constexpr bool kWeave = FMT == 1 && C::NK > 1;
+    constexpr bool kWeave = FMT != 0 && C::NK > 1;
     constexpr bool kFine = (LP + RP) * 6 <= 36 && (C::NS == 0 || 1 + 6 * (NDMA - 1) < 36);
     if (kWeave) wait_next();
     // slots of the tile copied during this one
@@ -796,6 +816,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       lse_v = (M + __log2f(z)) * kLn2;
     }
   }
+  factor *= a.out_scale;   // the per-tensor FP8 value scale (1 otherwise)
 
   // Accumulator register r of block b holds head h (this lane's) at dv 32b + acc_row(r, G):
   // registers 4k..4k+3 are four consecutive dv, stored as one 8-byte (bf16) or 16-byte
@@ -897,7 +918,11 @@ int max_chunk_positions() { return kCMax; }
 
 hipError_t launch_decode(const DecodeArgs& a, int kv_format, hipStream_t st) {
   const int nw = (a.H + 31) / 32;
-  return kv_format == 1 ? launch_fmt<1>(a, nw, st) : launch_fmt<0>(a, nw, st);
+  switch (kv_format) {
+    case 1: return launch_fmt<1>(a, nw, st);
+    case 2: return launch_fmt<2>(a, nw, st);
+    default: return launch_fmt<0>(a, nw, st);
+  }
 }
 
 hipError_t launch_gather_debug(const uint8_t* kv, int kv_format, int ps_log2, int num_slots,
@@ -906,6 +931,9 @@ hipError_t launch_gather_debug(const uint8_t* kv, int kv_format, int ps_log2, in
   const unsigned blocks = (unsigned)((items + 255) / 256);
   if (kv_format == 1)
     hipLaunchKernelGGL(gather_debug_kernel<1>, dim3(blocks), dim3(256), 0, st, kv, ps_log2, num_slots,
+                       slots, n, out);
+  else if (kv_format == 2)
+    hipLaunchKernelGGL(gather_debug_kernel<2>, dim3(blocks), dim3(256), 0, st, kv, ps_log2, num_slots,
                        slots, n, out);
   else
     hipLaunchKernelGGL(gather_debug_kernel<0>, dim3(blocks), dim3(256), 0, st, kv, ps_log2, num_slots,

@@ -67,7 +67,8 @@ __device__ __forceinline__ u32x4 dequant8_fp8(u32x2 raw, float scale) {
 }
 
 // Byte offsets of one cache slot's regions.  FP8 page = latent [ps][512] | rope bf16
-// [ps][64] | scales [ps][8]; BF16 page = bf16 [ps][576].
+// [ps][64] | scales [ps][8]; BF16 page = bf16 [ps][576]; per-tensor FP8 (FMT 2) page =
+// e4m3fn [ps][576], one scale for the whole cache applied outside the gather.
 struct SlotAddr {
   size_t latent;  // FP8: 512 codes; BF16: the 1152-byte row
   size_t rope;    // FP8 only
@@ -84,6 +85,10 @@ __device__ __forceinline__ SlotAddr slot_addr(int slot, int ps_log2) {
     a.latent = base + row * 512;
     a.rope = base + ((size_t)512 << ps_log2) + row * 128;
     a.scales = base + ((size_t)640 << ps_log2) + row * 8;
+  } else if (FMT == 2) {
+    a.latent = ((page << ps_log2) + row) * kQK;
+    a.rope = a.latent + 512;
+    a.scales = 0;
   } else {
     a.latent = (page << ps_log2) * kBf16Entry + row * kBf16Entry;
     a.rope = a.latent + 1024;
@@ -99,6 +104,8 @@ __device__ __forceinline__ u32x4 load_latent8(const uint8_t* __restrict__ kv, co
     const u32x2 raw = *reinterpret_cast<const u32x2*>(kv + a.latent + 8 * c);
     const uint32_t e = kv[a.scales + (c >> 3)];
     return dequant8_fp8(raw, ue8m0_scale(e));
+  } else if (FMT == 2) {
+    return dequant8_fp8(*reinterpret_cast<const u32x2*>(kv + a.latent + 8 * c), 1.0f);
   } else {
     return *reinterpret_cast<const u32x4*>(kv + a.latent + 16 * c);
   }
@@ -107,6 +114,7 @@ __device__ __forceinline__ u32x4 load_latent8(const uint8_t* __restrict__ kv, co
 // Load rope dims [512 + 8j, 512 + 8j + 8) (j in 0..7) as 8 bf16 values.
 template <int FMT>
 __device__ __forceinline__ u32x4 load_rope8(const uint8_t* __restrict__ kv, const SlotAddr& a, int j) {
+  if (FMT == 2) return dequant8_fp8(*reinterpret_cast<const u32x2*>(kv + a.rope + 8 * j), 1.0f);
   return *reinterpret_cast<const u32x4*>(kv + a.rope + 16 * j);
 }
 

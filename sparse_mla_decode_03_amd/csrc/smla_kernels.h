@@ -21,7 +21,8 @@ struct DecodeArgs {
   int32_t R, H, K, S, chunk, B;
   int32_t ps_log2, num_pages, num_slots, max_pages, index_mode;
   int32_t write_partials;
-  float scale_log2;             // softmax_scale * log2(e)
+  float scale_log2;             // softmax_scale * log2(e) (times the tensor scale, FMT 2)
+  float out_scale;              // value scale applied to the output (the tensor scale, FMT 2; else 1)
 };
 
 struct IndexerLogitsArgs {

@@ -45,6 +45,7 @@ import torch
 
 KV_BF16 = "bf16"
 KV_FP8 = "fp8"
+KV_FP8T = "fp8t"        # per-tensor FP8: e4m3fn [576] per entry, one scale for the cache
 
 LATENT = 512
 ROPE = 64
@@ -71,6 +72,7 @@ class WorkloadSpec:
     num_splits: int = 0              # 0 = planner decides
     softmax_scale: float = 1.0 / math.sqrt(576.0)
     causal: bool = False             # row i of n rows draws from positions < ctx - n + 1 + i
+    kv_scale: float = 1.0            # per-tensor FP8: the cache's one scale
 
     def scaled(self, **kw) -> "WorkloadSpec":
         return dataclasses.replace(self, **kw)
@@ -89,6 +91,9 @@ WORKLOADS = {
                                         shared_frac=0.1),
     # prefill chunks and decode rows in one launch: requests with 1, 4 or 256 query rows,
     # each row with its own causal top-k list
+    # the headline shape over the contiguous per-tensor FP8 cache
+    "b128_mtp4_h128_fp8t": WorkloadSpec("b128_mtp4_h128_fp8t", 128, (4,), 128, 2048, 8192,
+                                        131072, KV_FP8T, kv_scale=1.0 / 64),
     "mixed_b24_h128_fp8": WorkloadSpec("mixed_b24_h128_fp8", 24, (1, 4, 256), 128, 2048, 8192,
                                        65536, KV_FP8, causal=True),
 }
@@ -132,7 +137,7 @@ class Inputs:
 
 
 def page_bytes(kv_format: str, page_size: int) -> int:
-    return (648 if kv_format == KV_FP8 else 1152) * page_size
+    return {KV_FP8: 648, KV_FP8T: 576, KV_BF16: 1152}[kv_format] * page_size
 
 
 def encode_fp8_groups(x: torch.Tensor):
@@ -168,7 +173,7 @@ def pack_fp8_pages(codes: torch.Tensor, rope_bf16: torch.Tensor, scale_bytes: to
 
 
 def make_cache(num_pages: int, page_size: int, kv_format: str, seed: int,
-               device="cpu", chunk_pages: int = 2048) -> torch.Tensor:
+               device="cpu", chunk_pages: int = 2048, kv_scale: float = 1.0) -> torch.Tensor:
     """Random paged cache: N(0,1) values, FP8+UE8M0 latent with bf16 rope, or plain bf16."""
     gen = torch.Generator(device=device)
     gen.manual_seed(int(seed))
@@ -180,6 +185,10 @@ def make_cache(num_pages: int, page_size: int, kv_format: str, seed: int,
         if kv_format == KV_BF16:
             vals = torch.randn((ntok, WIDTH), generator=gen, device=device, dtype=torch.float32)
             cache[p0:p1] = vals.to(torch.bfloat16).view(torch.uint8).reshape(p1 - p0, pb)
+        elif kv_format == KV_FP8T:
+            vals = torch.randn((ntok, WIDTH), generator=gen, device=device, dtype=torch.float32)
+            codes = (vals / kv_scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+            cache[p0:p1] = codes.view(torch.uint8).reshape(p1 - p0, pb)
         else:
             lat = torch.randn((ntok, LATENT), generator=gen, device=device, dtype=torch.float32)
             rope = torch.randn((ntok, ROPE), generator=gen, device=device, dtype=torch.float32)
@@ -245,7 +254,7 @@ def make_inputs(spec: WorkloadSpec, seed: int, device="cpu", cache_device=None) 
         if spec.sinks == "half_neg_inf":
             sinks[: spec.num_heads // 2] = -np.inf
         sinks = torch.from_numpy(sinks)
-    cache = make_cache(num_pages, ps, spec.kv_format, seed, device=cache_device)
+    cache = make_cache(num_pages, ps, spec.kv_format, seed, device=cache_device, kv_scale=spec.kv_scale)
     mv = lambda t: None if t is None else t.to(device)  # noqa: E731
     return Inputs(spec, mv(q), cache, mv(torch.from_numpy(indices)), mv(torch.from_numpy(row_req)),
                   mv(torch.from_numpy(page_table)), mv(sinks),
@@ -256,7 +265,7 @@ def compulsory_bytes(inp: Inputs) -> int:
     """Bytes the method must move once: q, gathered entries, indices, page-table rows
     of the requests, out (bf16) and lse (fp32), sinks."""
     R, H, K = inp.num_rows, inp.num_heads, inp.spec.topk
-    entry = 648 if inp.spec.kv_format == KV_FP8 else 1152
+    entry = {KV_FP8: 648, KV_FP8T: 576, KV_BF16: 1152}[inp.spec.kv_format]
     n = inp.num_valid()
     ctx = inp.context_lens.cpu().numpy().astype(np.int64)
     pt = int((-(-ctx // inp.spec.page_size)).sum()) * 4

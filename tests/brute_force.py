@@ -23,12 +23,15 @@ def _e4m3_list(raw: bytes):
     return [float(x) for x in t.double().tolist()]
 
 
-def entry(cache: bytes, fmt: str, page_size: int, slot: int):
+def entry(cache: bytes, fmt: str, page_size: int, slot: int, kv_scale: float = 1.0):
     """Dequantized 576-vector of one cache slot."""
     page, row = divmod(slot, page_size)
     if fmt == "bf16":
         base = page * 1152 * page_size + row * 1152
         return _bf16_list(cache[base: base + 1152])
+    if fmt == "fp8t":
+        base = page * 576 * page_size + row * 576
+        return [v * kv_scale for v in _e4m3_list(cache[base: base + 576])]
     base = page * 648 * page_size
     lat = _e4m3_list(cache[base + 512 * row: base + 512 * row + 512])
     rope_at = base + 512 * page_size + 128 * row
@@ -38,13 +41,14 @@ def entry(cache: bytes, fmt: str, page_size: int, slot: int):
     return [lat[d] * math.ldexp(1.0, sc[d // 64] - 127) for d in range(512)] + rope
 
 
-def decode_row(q_row, cache: bytes, fmt: str, page_size: int, idx_row, slot_of, scale, sinks):
+def decode_row(q_row, cache: bytes, fmt: str, page_size: int, idx_row, slot_of, scale, sinks,
+               kv_scale: float = 1.0):
     """q_row: list of H lists of 576 floats; idx_row: list of ints; slot_of(t) -> slot.
 
     Returns (o, lse): H lists of 512 floats and H floats.  Each list position with an
     index other than -1 is one term (a repeated index counts as often as it appears).
     """
-    ks = [entry(cache, fmt, page_size, slot_of(t)) for t in idx_row if t != -1]
+    ks = [entry(cache, fmt, page_size, slot_of(t), kv_scale) for t in idx_row if t != -1]
     outs, lses = [], []
     for h, qh in enumerate(q_row):
         sig = -math.inf if sinks is None else float(sinks[h])

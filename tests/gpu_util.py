@@ -17,7 +17,7 @@ MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
 LSE_REL = 1e-3
 
-KV = {"bf16": orc.KV_BF16, "fp8": orc.KV_FP8_UE8M0}
+KV = {"bf16": orc.KV_BF16, "fp8": orc.KV_FP8_UE8M0, "fp8t": orc.KV_FP8_TENSOR}
 
 
 def announce(msg: str) -> None:
@@ -40,7 +40,7 @@ def gpu_decode(inp: W.Inputs, num_splits=None, flags=0, index_mode=B.IDX_LOGICAL
         g(inp.page_table if page_table is None else page_table), g(s), inp.spec.kv_format,
         inp.spec.page_size, inp.spec.softmax_scale, index_mode=index_mode,
         num_splits=inp.spec.num_splits if num_splits is None else num_splits, flags=flags,
-        return_info=return_info)
+        return_info=return_info, kv_scale=inp.spec.kv_scale)
 
 
 def oracle_decode(inp: W.Inputs, rows=None, indices=None, sinks="same", index_mode=orc.IDX_LOGICAL,
@@ -52,7 +52,7 @@ def oracle_decode(inp: W.Inputs, rows=None, indices=None, sinks="same", index_mo
         (inp.indices if indices is None else indices).cpu().numpy(), inp.row_req.cpu().numpy(),
         (inp.page_table if page_table is None else page_table).cpu().numpy(),
         None if s is None else s.cpu().numpy(), inp.spec.softmax_scale, index_mode=index_mode,
-        rows=rows)
+        rows=rows, kv_scale=inp.spec.kv_scale)
 
 
 def compare(out: torch.Tensor, lse: torch.Tensor, o_ref: np.ndarray, l_ref: np.ndarray,

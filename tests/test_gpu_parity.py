@@ -31,9 +31,9 @@ REDUCED = {
 
 
 def _small(fmt="fp8", heads=64, topk=256, nreq=3, rows=(1, 2), ctx=(300, 900), ps=64,
-           sinks="normal", valid="all", seed=101):
+           sinks="normal", valid="all", seed=101, kv_scale=1.0):
     spec = W.WorkloadSpec("small", nreq, rows, heads, topk, ctx[0], ctx[1], fmt, page_size=ps,
-                          valid=valid, sinks=sinks)
+                          valid=valid, sinks=sinks, kv_scale=kv_scale)
     return W.make_inputs(spec, seed)
 
 
@@ -79,7 +79,24 @@ def test_gather_all_codes_and_scales_bit_exact():
     assert bad[0].size == 0, f"{bad[0].size} mismatches, first at {bad[0][0]},{bad[1][0]}"
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_gather_per_tensor_fp8_all_codes_bit_exact():
+    """Per-tensor FP8: every finite e4m3fn code at every one of the 576 dims comes back as
+    its own value (the tensor scale is applied by the decode as two scalar factors)."""
+    ps, npg = 8, 16
+    codes = np.arange(256, dtype=np.uint8)
+    codes[[0x7F, 0xFF]] = 0
+    ent = np.stack([np.roll(np.tile(codes, 3)[:576], 41 * s) for s in range(npg * ps)])
+    pages = ent.reshape(npg, 576 * ps)
+    slots = np.arange(npg * ps, dtype=np.int32)
+    want = _bf16_bits_exact(orc.decode_entries(pages, orc.KV_FP8_TENSOR, ps, slots))
+    announce("gather_debug per-tensor fp8 all codes")
+    got = B.gather_debug(torch.from_numpy(pages).to(DEV), "fp8t", ps,
+                         torch.from_numpy(slots).to(DEV)).cpu().view(torch.int16).numpy()
+    bad = np.nonzero(got != want)
+    assert bad[0].size == 0, f"{bad[0].size} mismatches, first at {bad[0][0]},{bad[1][0]}"
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "fp8t"])
 def test_gather_random_slots_bit_exact(fmt):
     inp = _small(fmt=fmt, ctx=(500, 700), ps=16)
     n = inp.num_pages * 16
@@ -393,3 +410,85 @@ def test_mixed_prefill_and_decode_rows_in_one_launch(full):
     else:
         o, l = oracle_decode(inp, rows=rows)
     compare(out[rows], lse[rows], o, l, what=f"mixed rows={len(rows)}")
+
+
+# ------------------------------------------------------------------ per-tensor FP8 cache
+
+FP8T = W.WORKLOADS["b128_mtp4_h128_fp8t"]
+
+
+def test_parity_per_tensor_fp8_reduced():
+    inp = W.make_inputs(FP8T.scaled(num_requests=2, ctx_hi=16384), 61)
+    announce(f"parity fp8t R={inp.num_rows} H={inp.num_heads} K={inp.spec.topk}")
+    out, lse = gpu_decode(inp)
+    o, l = oracle_decode(inp)
+    compare(out, lse, o, l, what="fp8t reduced")
+
+
+@pytest.mark.parametrize("splits", [1, 3, 16])
+def test_per_tensor_fp8_forced_splits(splits):
+    inp = _small(fmt="fp8t", heads=64, topk=256, nreq=2, rows=(1, 2), valid="uniform",
+                 seed=62, kv_scale=1.0 / 32)
+    idx = inp.indices.clone()
+    idx[0, :50] = -1
+    o, l = oracle_decode(inp, indices=idx)
+    announce(f"fp8t forced splits {splits}")
+    out, lse = gpu_decode(inp, indices=idx, num_splits=splits)
+    compare(out, lse, o, l, what=f"fp8t S={splits}")
+
+
+def test_per_tensor_fp8_partials_only():
+    splits = 5
+    inp = _small(fmt="fp8t", heads=32, topk=128, nreq=2, rows=(2,), seed=63, kv_scale=0.05)
+    announce(f"fp8t partials only S={splits}")
+    po, pl = gpu_decode(inp, num_splits=splits, flags=B.F_PARTIALS_ONLY)
+    oc, lc = orc.sparse_mla_decode_partials(
+        q_bits(inp.q), inp.kv_cache.numpy(), KV["fp8t"], 64, inp.indices.numpy(),
+        inp.row_req.numpy(), inp.page_table.numpy(), inp.spec.softmax_scale, splits,
+        kv_scale=inp.spec.kv_scale)
+    d = np.abs(po.cpu().double().numpy() - oc)
+    assert d.max() <= 2e-2 and d.mean() <= 2e-3
+    pg = pl.cpu().double().numpy()
+    assert np.array_equal(np.isneginf(pg), np.isneginf(lc))
+    f = ~np.isneginf(lc)
+    assert np.all(np.abs(pg[f] - lc[f]) <= 1e-3 * np.maximum(1, np.abs(lc[f])))
+
+
+@pytest.mark.parametrize("heads,ps", [(16, 1), (48, 16), (128, 256)])
+def test_per_tensor_fp8_heads_and_page_sizes(heads, ps):
+    inp = _small(fmt="fp8t", heads=heads, topk=100, nreq=2, rows=(1, 2), ctx=(600, 1000),
+                 ps=ps, seed=64 + ps, kv_scale=1.0 / 64)
+    announce(f"fp8t heads {heads} page size {ps}")
+    out, lse = gpu_decode(inp)
+    o, l = oracle_decode(inp)
+    compare(out, lse, o, l, what=f"fp8t H={heads} ps={ps}")
+
+
+def test_per_tensor_fp8_kv_scale_is_a_pure_rescale():
+    """Halving kv_scale while the cache codes stay put equals decoding with the keys and
+    values halved: scores scale through softmax_scale, the output by the same factor."""
+    inp = _small(fmt="fp8t", heads=32, topk=96, nreq=2, rows=(1,), seed=65, kv_scale=0.5)
+    announce("fp8t kv_scale rescale")
+    out1, lse1 = gpu_decode(inp)
+    spec2 = inp.spec.scaled(kv_scale=0.25, softmax_scale=inp.spec.softmax_scale * 2.0)
+    inp2 = W.Inputs(spec2, inp.q, inp.kv_cache, inp.indices, inp.row_req, inp.page_table,
+                    inp.sinks, inp.context_lens)
+    out2, lse2 = gpu_decode(inp2)
+    torch.cuda.synchronize()
+    # same scores, output halved exactly (a power-of-two factor)
+    assert torch.equal(lse1, lse2)
+    assert torch.equal(out1.float() * 0.5, out2.float())
+
+
+def test_per_tensor_fp8_full_size_sampled():
+    inp = W.make_inputs(FP8T, 66, device="cpu", cache_device=DEV)
+    announce(f"full fp8t R={inp.num_rows} pages={inp.num_pages}")
+    out, lse = gpu_decode(inp)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    R = inp.num_rows
+    rng = np.random.default_rng(66)
+    rows = sorted({0, R - 1, *rng.choice(R, size=4, replace=False).tolist()})
+    sub_cache, sub_pt = page_subset(inp, rows)
+    o, l = oracle_decode(inp, rows=rows, kv_cache=sub_cache, page_table=sub_pt)
+    compare(out[rows], lse[rows], o, l, what=f"fp8t full rows={len(rows)}")

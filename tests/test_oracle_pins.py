@@ -25,7 +25,7 @@ from sparse_mla_decode_03_amd import workloads as W
 from tests import brute_force
 from tests.golden_io import e4m3fn_points, fp8_page_fixture
 
-KV = {"bf16": orc.KV_BF16, "fp8": orc.KV_FP8_UE8M0}
+KV = {"bf16": orc.KV_BF16, "fp8": orc.KV_FP8_UE8M0, "fp8t": orc.KV_FP8_TENSOR}
 
 
 def _q_bits(inp):
@@ -37,13 +37,14 @@ def _np(inp):
                 page_size=inp.spec.page_size, indices=inp.indices.numpy(),
                 row_req=inp.row_req.numpy(), page_table=inp.page_table.numpy(),
                 sinks=None if inp.sinks is None else inp.sinks.numpy(),
-                softmax_scale=inp.spec.softmax_scale)
+                softmax_scale=inp.spec.softmax_scale, kv_scale=inp.spec.kv_scale)
 
 
 def _tiny(fmt, seed, heads=3, topk=12, ps=4, ctx=(20, 40), sinks="normal", valid="all",
           rows=(1, 2), nreq=2):
     spec = W.WorkloadSpec("tiny", nreq, rows, heads, topk, ctx[0], ctx[1], fmt, page_size=ps,
-                          valid=valid, sinks=sinks)
+                          valid=valid, sinks=sinks,
+                          kv_scale=1.0 / 64 if fmt == "fp8t" else 1.0)
     return W.make_inputs(spec, seed)
 
 
@@ -53,7 +54,7 @@ def _oracle(d, rows=None, index_mode=orc.IDX_LOGICAL, **over):
     return orc.sparse_mla_decode(args["q_bits"], args["cache"], args["kv_format"],
                                  args["page_size"], args["indices"], args["row_req"],
                                  args["page_table"], args["sinks"], args["softmax_scale"],
-                                 index_mode=index_mode, rows=rows)
+                                 index_mode=index_mode, rows=rows, kv_scale=args["kv_scale"])
 
 
 # ---------------------------------------------------------------- number formats
@@ -112,6 +113,43 @@ def test_fp8_layout_fixture_decodes_by_hand_values():
         assert rows[slot].tolist() == brute_force.entry(page, "fp8", ps, slot)
 
 
+def test_fp8_tensor_page_decodes_by_hand_values():
+    """Per-tensor FP8 entry: 576 e4m3fn codes in a row, each times the one tensor scale."""
+    ps = 2
+    page = np.zeros(576 * ps, dtype=np.uint8)
+    page[0] = 0x38                  # slot 0 dim 0: 1.0
+    page[511] = 0xC0                # slot 0 dim 511: -2.0
+    page[512] = 0x01                # slot 0 dim 512 (first rope dim): 2^-9
+    page[575] = 0x7E                # slot 0 dim 575: 448
+    page[576 + 5] = 0xB4            # slot 1 dim 5: -0.75
+    page[576 + 575] = 0x30          # slot 1 dim 575: 0.5
+    rows = orc.decode_entries(page, orc.KV_FP8_TENSOR, ps, [0, 1], kv_scale=0.25)
+    want = np.zeros((2, 576))
+    want[0, 0], want[0, 511], want[0, 512], want[0, 575] = 0.25, -0.5, 2.0 ** -11, 112.0
+    want[1, 5], want[1, 575] = -0.1875, 0.125
+    assert np.array_equal(rows, want)
+    for slot in (0, 1):
+        assert rows[slot].tolist() == brute_force.entry(page.tobytes(), "fp8t", ps, slot, 0.25)
+
+
+def test_fp8_tensor_equals_bf16_cache_of_the_same_values():
+    """Every e4m3fn value times a power of two is a bf16 value, so a per-tensor FP8 cache
+    and the BF16 cache holding its decoded values give the same attention."""
+    inp = _tiny("fp8t", 4)
+    d = _np(inp)
+    o, lse = _oracle(d)
+    npg = d["cache"].shape[0]
+    ps = d["page_size"]
+    vals = orc.decode_entries(d["cache"], orc.KV_FP8_TENSOR, ps, np.arange(npg * ps),
+                              kv_scale=d["kv_scale"])
+    bf = torch.from_numpy(vals).to(torch.bfloat16)
+    assert np.array_equal(bf.double().numpy(), vals)
+    d2 = dict(d, cache=bf.view(torch.uint8).reshape(npg, ps * 1152).numpy(),
+              kv_format=orc.KV_BF16, kv_scale=1.0)
+    o2, lse2 = _oracle(d2)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+
+
 def test_packer_writes_fixture_layout():
     """The generator's page packer puts each region where the layout says."""
     page, ps, _ = fp8_page_fixture()
@@ -151,7 +189,7 @@ def test_encoder_roundtrip_within_fp8_resolution():
 
 # ---------------------------------------------------------------- brute force
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "fp8t"])
 @pytest.mark.parametrize("seed", [1, 2, 3])
 def test_oracle_matches_brute_force(fmt, seed):
     inp = _tiny(fmt, seed, heads=2, topk=8, ctx=(9, 30))
@@ -171,7 +209,7 @@ def test_oracle_matches_brute_force(fmt, seed):
         slot_of = lambda t: int(pt[b, t // ps]) * ps + t % ps  # noqa: E731
         qr = [[float(x) for x in inp.q[r, h].double().tolist()] for h in range(inp.num_heads)]
         bo, bl = brute_force.decode_row(qr, cache, fmt, ps, idx[r].tolist(), slot_of,
-                                        inp.spec.softmax_scale, d["sinks"])
+                                        inp.spec.softmax_scale, d["sinks"], inp.spec.kv_scale)
         np.testing.assert_allclose(o[r], np.array(bo), rtol=1e-12, atol=1e-14)
         np.testing.assert_allclose(lse[r], np.array(bl), rtol=1e-12, atol=1e-14)
 
@@ -386,11 +424,18 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     def sink_ignored(q, k, scale, sink):
         return good_attend(q, k, scale, None)
 
-    def scale_group_32(cache, fmt, ps, slots):  # wrong group size for the UE8M0 scales
-        rows = good_decode(cache, fmt, ps, slots)
+    def scale_group_32(cache, fmt, ps, slots, kv_scale=1.0):  # wrong UE8M0 group size
+        rows = good_decode(cache, fmt, ps, slots, kv_scale)
         if fmt == orc.KV_FP8_UE8M0 and rows.shape[0]:
             rows = rows.copy()
             rows[:, 32:64] *= 2.0
+        return rows
+
+    def tensor_scale_on_latent_only(cache, fmt, ps, slots, kv_scale=1.0):
+        rows = good_decode(cache, fmt, ps, slots, kv_scale)
+        if fmt == orc.KV_FP8_TENSOR and rows.shape[0]:
+            rows = rows.copy()
+            rows[:, 512:] /= kv_scale
         return rows
 
     def e4m3_bias8(codes):
@@ -403,6 +448,9 @@ def test_pins_catch_planted_mistakes(monkeypatch):
                          lambda: test_sink_identity(2.0)),
         "scale_group": (lambda: monkeypatch.setattr(orc, "decode_entries", scale_group_32),
                         lambda: test_oracle_matches_brute_force("fp8", 1)),
+        "tensor_scale_rope": (lambda: monkeypatch.setattr(orc, "decode_entries",
+                                                          tensor_scale_on_latent_only),
+                              lambda: test_oracle_matches_brute_force("fp8t", 1)),
         "e4m3_bias": (lambda: monkeypatch.setattr(orc, "e4m3fn_to_f64", e4m3_bias8),
                       test_e4m3fn_all_codes_match_torch),
     }
