@@ -21,6 +21,15 @@ a group is the smallest power of two that keeps every code finite, i.e.
   the latent codes, the token's 64 bf16 rope values and its 8 scale bytes are written to
   the token's slot of the region-split page; a BF16 cache stores the 576 bf16 values;
   slots that are negative or past the cache are skipped.
+The per-tensor FP8 cache ([vllm#43827] implementation breakdown 4 and 5: the compressor
+writes a contiguous per-tensor FP8 cache given the tensor's fp8 scale) stores all 576 values
+of a token as e4m3fn codes.  The reading taken here, in the kernel's precision:
+
+  y[d] = float32(x[d]) / float32(kv_scale), an IEEE float32 division (correctly rounded);
+  y clamped to [-448, 448] (the saturating conversion of FP8 quantizers);
+  code[d] = the e4m3fn code nearest to y[d], ties to the even code.
+
+The float32 quotient decides the code, so the oracle forms it in float32 as the kernel does.
 Inputs are bf16 (the model's latent and rope rows), decoded exactly to float64.
 """
 
@@ -28,8 +37,9 @@ from __future__ import annotations
 
 import numpy as np
 
-from .sparse_mla_oracle import (BF16_ENTRY_BYTES, FP8_ENTRY_BYTES, KV_BF16, KV_FP8_UE8M0,
-                                bf16_bits_to_f64, e4m3fn_to_f64)
+from .sparse_mla_oracle import (BF16_ENTRY_BYTES, FP8_ENTRY_BYTES, FP8_TENSOR_ENTRY_BYTES,
+                                KV_BF16, KV_FP8_TENSOR, KV_FP8_UE8M0, bf16_bits_to_f64,
+                                e4m3fn_to_f64)
 
 LATENT = 512
 ROPE = 64
@@ -98,8 +108,21 @@ def quantize_fp8_ue8m0(latent_bits: np.ndarray):
     return codes, e
 
 
+def quantize_fp8_tensor(latent_bits: np.ndarray, rope_bits: np.ndarray, kv_scale: float):
+    """bf16 latent [n, 512] and rope [n, 64] (uint16 bit patterns) -> e4m3fn codes [n, 576]
+    of the per-tensor FP8 cache with the one scale `kv_scale`."""
+    if not (np.isfinite(kv_scale) and kv_scale > 0):
+        raise ValueError("kv_scale must be finite and > 0")
+    lat = bf16_bits_to_f64(np.asarray(latent_bits, dtype=np.uint16)).reshape(-1, LATENT)
+    rope = bf16_bits_to_f64(np.asarray(rope_bits, dtype=np.uint16)).reshape(-1, ROPE)
+    x = np.concatenate([lat, rope], axis=1).astype(np.float32)      # exact: bf16 values
+    y = np.divide(x, np.float32(kv_scale), dtype=np.float32)
+    y = np.clip(y.astype(np.float64), -E4M3_MAX, E4M3_MAX)
+    return e4m3fn_nearest(y)
+
+
 def cache_store(cache: np.ndarray, kv_format: int, page_size: int, latent_bits: np.ndarray,
-                rope_bits: np.ndarray, slots: np.ndarray) -> np.ndarray:
+                rope_bits: np.ndarray, slots: np.ndarray, kv_scale: float = 1.0) -> np.ndarray:
     """Return a copy of `cache` ([num_pages, page bytes] uint8) with the tokens written.
 
     Tokens are applied in order, so a slot named twice keeps the last token's bytes.
@@ -111,6 +134,8 @@ def cache_store(cache: np.ndarray, kv_format: int, page_size: int, latent_bits: 
     slots = np.asarray(slots, dtype=np.int64).reshape(-1)
     if kv_format == KV_FP8_UE8M0:
         codes, scales = quantize_fp8_ue8m0(latent_bits)
+    elif kv_format == KV_FP8_TENSOR:
+        codes = quantize_fp8_tensor(latent_bits, rope_bits, kv_scale)
     for t, slot in enumerate(slots):
         if slot < 0 or slot >= num_pages * page_size:
             continue
@@ -124,6 +149,8 @@ def cache_store(cache: np.ndarray, kv_format: int, page_size: int, latent_bits: 
         elif kv_format == KV_BF16:
             row = np.concatenate([latent_bits[t], rope_bits[t]]).astype("<u2").view(np.uint8)
             out[page, r * BF16_ENTRY_BYTES:(r + 1) * BF16_ENTRY_BYTES] = row
+        elif kv_format == KV_FP8_TENSOR:
+            out[page, r * FP8_TENSOR_ENTRY_BYTES:(r + 1) * FP8_TENSOR_ENTRY_BYTES] = codes[t]
         else:
             raise ValueError("unknown kv_format")
     assert FP8_ENTRY_BYTES == LATENT + 2 * ROPE + 8
