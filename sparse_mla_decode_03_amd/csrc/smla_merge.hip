@@ -5,7 +5,10 @@
 // produces per-chunk results that are merged afterwards; here one kernel does both:
 //   M = max(max_c lse_c, sigma), w_c = exp(lse_c - M), w_s = exp(sigma - M),
 //   out = sum_c w_c o_c / (sum_c w_c + w_s), lse = M + ln(sum_c w_c + w_s).
-// One 64-lane wave per (row, head); each lane owns 8 of the 512 output dims.
+// One 64-lane wave per (row, head); each lane owns 8 of the 512 output dims.  All chunk
+// LSEs, then the partial rows of eight chunks at a time, are loaded before use, so a merge
+// costs a few memory round trips instead of one per chunk.
+#include "sparse_mla.h"
 #include "smla_device.h"
 #include "smla_kernels.h"
 
@@ -13,10 +16,15 @@ namespace smla {
 
 namespace {
 
+constexpr int kMaxChunks = 256;   // the largest split count a plan allows
+static_assert(kMaxChunks >= SMLA_MAX_SPLITS, "merge chunk capacity below the plan limit");
+
 __global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ po,
                                                    const float* __restrict__ pl, int R, int S,
                                                    int H, const float* __restrict__ sinks,
                                                    uint16_t* __restrict__ out, float* __restrict__ lse) {
+  // chunk weights, shared by the wave (S <= kMaxChunks)
+  __shared__ float sw[kMaxChunks];
   const long long rh = blockIdx.x;
   const int r = (int)(rh / H);
   const int h = (int)(rh % H);
@@ -24,26 +32,59 @@ __global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ po,
   const float sink = (sinks != nullptr) ? sinks[h] : -INFINITY;
   const float sig2 = sink * kLog2e;
   const float* plr = pl + (size_t)r * S * H + h;
+  // every chunk's LSE is loaded at once: lane l holds chunks l, l + 64, ... (log2 domain)
+  float l2[kMaxChunks / 64];
   float mc = -INFINITY;
-  for (int c = 0; c < S; ++c) mc = fmaxf(mc, plr[(size_t)c * H] * kLog2e);
+#pragma unroll
+  for (int i = 0; i < kMaxChunks / 64; ++i) {
+    const int c = lane + 64 * i;
+    l2[i] = c < S ? plr[(size_t)c * H] * kLog2e : -INFINITY;
+    mc = fmaxf(mc, l2[i]);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mc = fmaxf(mc, __shfl_xor(mc, off));
   const float M = fmaxf(mc, sig2);
   u32x4 res = u32x4{0u, 0u, 0u, 0u};
   float lse_v = sink;  // every chunk empty: out = 0, LSE = the sink (or -inf)
   if (mc != -INFINITY) {
-    float z = (sig2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sig2 - M);
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < S; ++c) {
-      const float l2 = plr[(size_t)c * H] * kLog2e;
-      if (l2 == -INFINITY) continue;
-      const float w = __builtin_amdgcn_exp2f(l2 - M);
-      z += w;
-      const float* src = po + (((size_t)r * S + c) * H + h) * kV + 8 * lane;
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+    // w_c = 2^(l2_c - M); an empty chunk (LSE -inf) has weight 0 and is skipped below
+    float zs = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[i] += w * x0[i];
-        acc[4 + i] += w * x1[i];
+    for (int i = 0; i < kMaxChunks / 64; ++i) {
+      const int c = lane + 64 * i;
+      const float w = l2[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(l2[i] - M);
+      if (c < S) sw[c] = w;
+      zs += w;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) zs += __shfl_xor(zs, off);
+    const float z = zs + ((sig2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sig2 - M));
+    __syncthreads();
+    // out = sum_c w_c o_c / z: lane owns dims 8l..8l+7; the partial rows of kBatch chunks
+    // are loaded before any of them is used, so their latencies overlap
+    const float* src0 = po + ((size_t)r * S * H + h) * kV + 8 * lane;
+    const size_t cstride = (size_t)H * kV;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    constexpr int kBatch = 8;
+    for (int c0 = 0; c0 < S; c0 += kBatch) {
+      f32x4 x[kBatch][2];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int c = min(c0 + j, S - 1);
+        const float* src = src0 + c * cstride;
+        x[j][0] = *reinterpret_cast<const f32x4*>(src);
+        x[j][1] = *reinterpret_cast<const f32x4*>(src + 4);
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const float w = (c0 + j < S) ? sw[c0 + j] : 0.f;   // wave-uniform
+        if (w > 0.f) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[i] += w * x[j][0][i];
+            acc[4 + i] += w * x[j][1][i];
+          }
+        }
       }
     }
     const float inv = 1.0f / z;
