@@ -308,17 +308,19 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // only) the scales of tile + 1.  `ln` is an opaque copy of the lane id: the per-lane
   // address terms are recomputed at each part instead of being hoisted out of the tile loop
   // (which costs registers, then spills whose reloads would wait on the copies).
+  // LDS byte addresses of the copy destinations (wave-uniform, in SGPRs)
+  const uint32_t lds_k = lds_offset(sK), lds_raw = lds_offset(sRaw), lds_scl = lds_offset(sScl);
   auto issue_part = [&](int tile, int j, const int (&sl)[NDMA], int ln) {
     const int st = C::NS > 0 ? tile % (FMT != 0 ? C::NS : C::NK) : 0;
-    uint16_t* K = sK + (FMT != 0 ? 0 : st) * kTile;
-    uint8_t* raw = sRaw + (FMT != 0 ? st : 0) * (20 * 1024);
+    const uint32_t K = lds_k + (FMT != 0 ? 0 : st) * (2 * kTile);
+    const uint32_t raw = lds_raw + (FMT != 0 ? st : 0) * (20 * 1024);
     if (j < LP) {
       const int ins = wave + NW * j;
       if (ins < C::NL) {
         const int t = lat_token(ins, ln);
         const uint32_t slot = (uint32_t)sl[j];
         size_t off;
-        uint8_t* dst;
+        uint32_t dst;
         if (FMT == 1) {
           off = fp8_off(slot, fp8_row(slot) * 512u + 16u * (ln & 31));
           dst = raw + ins * 1024;
@@ -328,9 +330,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         } else {
           // lane = physical chunk of the destination row; it copies logical chunk lane ^ swz
           off = (size_t)slot * kBf16Entry + 16u * (ln ^ lat_swz(t));
-          dst = reinterpret_cast<uint8_t*>(K + t * kLat);
+          dst = K + t * (2 * kLat);
         }
-        dma16(a.kv + off, dst);
+        dma16_at(a.kv + off, dst);
       }
     } else if (j < LP + RP) {
       const int ins = wave + NW * (j - LP);
@@ -338,7 +340,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         const int t = rope_token(ins, ln);
         const uint32_t slot = (uint32_t)sl[j];
         size_t off;
-        uint8_t* dst;
+        uint32_t dst;
         if (FMT == 1) {
           off = fp8_off(slot, (512u << a.ps_log2) + fp8_row(slot) * 128u + 16u * (ln & 7));
           dst = raw + (16 + ins) * 1024;
@@ -347,15 +349,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
           dst = raw + (16 + ins) * 1024;
         } else {
           off = (size_t)slot * kBf16Entry + 1024u + 16u * ((ln & 7) ^ ((t >> 1) & 7));
-          dst = reinterpret_cast<uint8_t*>(K + kRopeOff) + ins * 1024;
+          dst = K + 2 * kRopeOff + ins * 1024;
         }
-        dma16(a.kv + off, dst);
+        dma16_at(a.kv + off, dst);
       }
     } else if (scale_wave()) {
       // scales of tile + 1: lane l copies 4 bytes of token l/2
       const uint32_t slot = (uint32_t)sl[LP + RP];
       const size_t off = fp8_off(slot, (640u << a.ps_log2) + fp8_row(slot) * 8u + 4u * (ln & 1));
-      dma4(a.kv + off, sScl + ((tile + 1) % (C::NS + 1)) * 256);
+      dma4_at(a.kv + off, lds_scl + ((tile + 1) % (C::NS + 1)) * 256);
     }
   };
   auto issue_dma = [&](int tile, const int (&sl)[NDMA]) {
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     asm volatile("" : "+v"(ln));
     const uint32_t slot = (uint32_t)sSlots[ln >> 1];
     const size_t off = fp8_off(slot, (640u << a.ps_log2) + fp8_row(slot) * 8u + 4u * (ln & 1));
-    dma4(a.kv + off, sScl);
+    dma4_at(a.kv + off, lds_scl);
   };
   // Wait for the oldest tile in flight; the NS - 1 younger ones may stay pending.
   // A wave issues one group of copies per tile (its parts of tile + NS, in issue order).

@@ -136,6 +136,17 @@ __device__ __forceinline__ void dma4(const void* src, const void* lds_wave_base)
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :: "v"(src), "s"(lds_offset(lds_wave_base)) : "memory");
 }
+// The same copies to an LDS byte address already in an SGPR (an LDS array's address from
+// lds_offset plus wave-uniform integer offsets), which spares the generic-to-LDS pointer
+// conversion and its null test at every copy.
+__device__ __forceinline__ void dma16_at(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_addr) : "memory");
+}
+__device__ __forceinline__ void dma4_at(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(lds_addr) : "memory");
+}
 // Wait until at most N of this wave's global loads (LDS copies included) are pending.
 // The builtin lets the compiler's own wait insertion see the wait; the empty asm with a
 // memory clobber keeps LDS reads of the copied data below it.
