@@ -142,6 +142,60 @@ def decode_measure(B, W, torch, dev, name: str, reps: int, seed: int):
                          "flops_per_launch": flops}}
 
 
+def workload_measure(B, W, torch, dev, name: str, seed: int, reps: int):
+    """One decode call (split decode and merge included) on another of the five workloads:
+    warm launches back to back, and cold launches each after a 1 GiB write that evicts the
+    caches; throughput and roofline fractions are taken on the cold median."""
+    spec = W.WORKLOADS[name]
+    inp = W.make_inputs(spec, seed, device=dev, cache_device=dev)
+    R, H = inp.num_rows, inp.num_heads
+    prob = B.make_problem(R, spec.num_requests, H, spec.topk, spec.page_size, inp.num_pages,
+                          inp.page_table.shape[1], kv_code(B, spec.kv_format), B.IDX_LOGICAL,
+                          spec.num_splits, 0, spec.softmax_scale, spec.kv_scale)
+    info = B.plan(prob)
+    out = torch.empty((R, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((R, H), dtype=torch.float32, device=dev)
+    ws = (torch.empty(info.workspace_bytes, dtype=torch.uint8, device=dev)
+          if info.workspace_bytes else None)
+    stream = torch.cuda.current_stream()
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def step():
+        B.run(info, inp.q, inp.kv_cache, inp.indices, inp.row_req, inp.page_table, inp.sinks,
+              out, lse, None, None, ws, stream)
+
+    for _ in range(3):
+        step()
+    times = {}
+    for mode in ("warm", "cold"):
+        ms = []
+        for i in range(reps):
+            if mode == "cold":
+                scratch.fill_(i & 255)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        ms.sort()
+        times[mode] = ms[len(ms) // 2]
+    t = times["cold"] / 1e3
+    n = inp.num_valid()
+    flops = W.algorithmic_flops(inp)
+    cbytes = W.compulsory_bytes(inp)
+    hbm_frac = cbytes / t / 1e9 / PEAK_HBM_GBS
+    mfma_frac = flops / t / 1e12 / PEAK_BF16_TFLOPS
+    del inp, scratch
+    return {"kv_format": spec.kv_format, "rows": R, "heads": H, "num_splits": info.num_splits,
+            "attended_entries": n, "launch_ms_p50": times["warm"], "cold_cache_launch_ms_p50": times["cold"],
+            "entries_per_s": n / t, "tokens_per_s": R / t,
+            "hbm_tb_s": cbytes / t / 1e12, "hbm_frac": hbm_frac,
+            "mfma_tflop_s": flops / t / 1e12, "mfma_frac": mfma_frac,
+            "bound": "hbm" if hbm_frac >= mfma_frac else "mfma",
+            "compulsory_bytes": cbytes, "flops": flops}
+
+
 def indexer_measure(B, W, torch, dev, name: str, reps: int):
     """Time the indexer on one workload: the logits kernel and the top-k kernel, each
     launched `reps` times after warm-up, HIP events on the launch stream."""
@@ -254,6 +308,9 @@ def main() -> int:
                          "(empty: skip)")
     ap.add_argument("--indexer", default="idx_b128_mtp4_h64",
                     help="indexer workload measured beside the decode ('' to skip)")
+    ap.add_argument("--other-workloads",
+                    default="tiny_bf16:1,b32_h64_fp8:2,b2_h128_bf16_split16:4,ragged_b256_h64_fp8:5",
+                    help="the other decode workloads (name:seed, comma separated; '' to skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run only a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -437,6 +494,11 @@ def main() -> int:
         res["per_tensor_fp8"] = decode_measure(B, W, torch, dev, args.fp8_tensor, 20, 43)
     if args.indexer:
         res["indexer"] = indexer_measure(B, W, torch, dev, args.indexer, 20)
+    if args.other_workloads:
+        res["workloads"] = {}
+        for item in args.other_workloads.split(","):
+            name, seed = item.split(":")
+            res["workloads"][name] = workload_measure(B, W, torch, dev, name, int(seed), 20)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
     print(json.dumps(res), flush=True)
