@@ -30,9 +30,9 @@ namespace smla {
 namespace {
 
 constexpr int kT = 32;                  // tokens per tile (MFMA M dimension)
-constexpr int kLat = 512;               // bf16 per latent row of a K tile (1024 B, 64 chunks)
-constexpr int kRopeOff = kT * kLat;     // rope region: [32][64] bf16 after the latent rows
-constexpr int kTile = kRopeOff + kT * 64;  // bf16 per tile (36,864 bytes)
+constexpr int kRowB = 1280;             // LDS bytes per latent row slot (1024 B of data + pad)
+constexpr int kRopeOff = kT * kRowB / 2;   // rope region: [32][64] bf16 after the latent rows
+constexpr int kTile = kRopeOff + kT * 64;  // bf16 per tile (45,056 bytes)
 constexpr int kCMax = 2048;             // positions per split handled by one workgroup
 constexpr int kDepth = 4;               // LDS operand loads kept in flight (QK)
 constexpr int kDepthV = 3;              // LDS operand load pairs kept in flight (PV)
@@ -45,14 +45,19 @@ constexpr unsigned kRestartBits = 0x4F800000u;   // bit pattern of 2^kRestartLog
 constexpr unsigned kInfBits = 0x7F800000u;       // bit pattern of +inf
 
 // K tile layout.  LDS serves 64 banks of 4 bytes: 16 lanes per cycle for 16-byte reads
-// and 32 lanes per cycle for 8-byte (and transpose) reads.  Latent rows are 1024 bytes of
-// 64 chunks of 16 bytes; within each 256-byte bank row the chunk index is XORed with
-// lat_swz(row) = (row%4)*4 + (row/4)%4, which keeps both operand patterns conflict free:
-//   QK A operand: 16 consecutive rows at one chunk -> 16 different chunk slots;
-//   PV transpose reads: 4 consecutive rows x 4 consecutive chunks -> 16 different slots.
-// Rope rows are 128 bytes (two per bank row) with the chunk XORed with (row/2)%8.
-// A chunk is 16 bytes (8 bf16 dims).
-__device__ __forceinline__ int lat_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+// and 32 lanes per cycle for 8-byte (and transpose) reads.  Latent row r is 1024 contiguous
+// bytes (64 chunks of 16 bytes) at lat_row_byte(r) = 1280 r + 16 pad(r), with
+// pad(r) = 4 (r%4) + (r/4)%4.  A row slot is a multiple of 256 bytes, so a row starts on bank
+// 4 pad(r), and both operand patterns are conflict free:
+//   QK A operand: 16 consecutive rows at one chunk -> pad takes all 16 values, 16 different
+//   4-bank groups;
+//   PV transpose reads: 4 consecutive rows 4m..4m+3 x 64 bytes -> pads m, 4+m, 8+m, 12+m,
+//   four disjoint 16-bank windows.
+// Since each row is contiguous, a lane's operand addresses differ only by constants (one
+// base register for all latent QK steps, two for PV).  Rope rows are 128 bytes (two per bank
+// row) with the chunk XORed with (row/2)%8.  A chunk is 16 bytes (8 bf16 dims).
+__device__ __forceinline__ int lat_pad(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ int lat_row_byte(int row) { return row * kRowB + 16 * lat_pad(row); }
 
 // Cross-half reductions: lanes l and l ^ 32 hold the same head (other tokens); one
 // permlane32 swap gives every lane both values.
@@ -328,9 +333,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
           off = (size_t)slot * kQK + 16u * (ln & 31);
           dst = raw + ins * 1024;
         } else {
-          // lane = physical chunk of the destination row; it copies logical chunk lane ^ swz
-          off = (size_t)slot * kBf16Entry + 16u * (ln ^ lat_swz(t));
-          dst = K + t * (2 * kLat);
+          // lane = chunk of the destination row
+          off = (size_t)slot * kBf16Entry + 16u * ln;
+          dst = K + lat_row_byte(t);
         }
         dma16_at(a.kv + off, dst);
       }
@@ -402,8 +407,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // scale byte from LDS) and a write step, so the parts can be spread over the MFMAs with
   // each load a few MFMAs ahead of its write.  All addresses are a per-tile lane base plus
   // wave-uniform terms: for latent instruction i the unit of token t = 2i + G, dims
-  // 16c..16c+15 (c = lane % 32) goes to swizzled chunks 2c and 2c + 1 of row t, and
-  // (2c ^ swz(t)) = (2c ^ 4G) ^ U(i) with U(i) = 8(i % 2) + (i / 2) % 4; rope instruction r
+  // 16c..16c+15 (c = lane % 32) goes to chunks 2c and 2c + 1 of row t, at byte
+  // lat_row_byte(2i + G) + 32c = 1344 G + 32c + U(i) with U(i) = 2560 i + 128 (i % 2) +
+  // 16 ((i / 2) % 4) (pad(2i + G) = 8 (i % 2) + 4G + (i / 2) % 4); rope instruction r
   // puts token 8r + lane / 8, chunk lane % 8, at chunk (lane % 8) ^ (lane / 16) ^ 4(r % 2);
   // per-tensor FP8 rope instruction r holds token 16r + lane / 4, codes 16(lane % 4) .. +15,
   // converted to logical chunks 2(lane % 4) and 2(lane % 4) + 1 of the token's rope row.
@@ -413,7 +419,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   struct DqBase {
     int raw;    // byte offset into sRaw of the half of this lane's unit written first
     int scl;    // byte offset into sScl of this lane's scale byte for instruction `wave`
-    int lat;    // lane part of the latent write offset (bits 4..10)
+    int lat;    // lane part of the latent write offset (first half)
     int rope;   // lane part of the rope write offset (bits 4..9)
     int kb;     // byte offset of the destination K buffer
   };
@@ -422,7 +428,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     const int G_ = ln >> 5, c = ln & 31;
     d.raw = (C::NS > 0 ? tile % C::NS : 0) * (20 * 1024) + wave * 1024 + 16 * ln + 8 * ((c >> 3) & 1);
     d.scl = (tile % (C::NS + 1)) * 256 + 16 * wave + 8 * G_ + (c >> 2);
-    d.lat = 1024 * G_ + ((32 * c) ^ (64 * G_) ^ (16 * ((c >> 3) & 1)));
+    d.lat = (kRowB + 64) * G_ + 32 * c + 16 * ((c >> 3) & 1);
     d.rope = FMT == 2 ? 128 * (ln >> 2) + 16 * ((2 * (ln & 3)) ^ ((ln >> 3) & 7))
                       : 128 * (ln >> 3) + 16 * ((ln & 7) ^ (ln >> 4));
     d.kb = 2 * kbuf_of(tile) * kTile;
@@ -450,10 +456,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     if (j < LP) {
       const int ins = wave + NW * j;
       if (ins < C::NL) {
-        const int U16 = 16 * (((ins & 1) << 3) | ((ins >> 1) & 3));
+        const int U = 2 * kRowB * ins + 128 * (ins & 1) + 16 * ((ins >> 1) & 3);
         const float sc = ue8m0_scale(u.e);
-        *reinterpret_cast<u32x4*>(Kb + 2048 * ins + (d.lat ^ U16)) = dequant8_fp8(u32x2{u.rv[0], u.rv[1]}, sc);
-        *reinterpret_cast<u32x4*>(Kb + 2048 * ins + (d.lat ^ U16 ^ 16)) = dequant8_fp8(u32x2{u.rv[2], u.rv[3]}, sc);
+        *reinterpret_cast<u32x4*>(Kb + U + d.lat) = dequant8_fp8(u32x2{u.rv[0], u.rv[1]}, sc);
+        *reinterpret_cast<u32x4*>(Kb + U + (d.lat ^ 16)) = dequant8_fp8(u32x2{u.rv[2], u.rv[3]}, sc);
       }
     } else if (FMT == 2) {
       const int r = wave + NW * (j - LP);
@@ -477,8 +483,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       half[2 * (q & 1) + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.rv[q], sc, true));
       if (q & 1) {
         uint8_t* Kb = reinterpret_cast<uint8_t*>(sK) + d.kb;
-        const int U16 = 16 * (((ins & 1) << 3) | ((ins >> 1) & 3));
-        *reinterpret_cast<u32x4*>(Kb + 2048 * ins + (d.lat ^ U16 ^ (q == 3 ? 16 : 0))) = half;
+        const int U = 2 * kRowB * ins + 128 * (ins & 1) + 16 * ((ins >> 1) & 3);
+        *reinterpret_cast<u32x4*>(Kb + U + (q == 3 ? d.lat ^ 16 : d.lat)) = half;
       }
     }
   };
@@ -497,24 +503,23 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     }
   };
 
-  // Lane parts of the LDS operand addresses (bf16 elements).  The swizzle only touches
-  // address bits 3..6, so each operand address is (lane base XOR constant) + constant.
-  //   QK step ks < 32: logical chunk 2ks + G of row hl -> (qk_base ^ 16(ks%8)) + 128(ks/8);
-  //   QK rope step 32 + i: (rope_base ^ 16i);
-  //   PV (see the B-operand note in the loop): (pv_base ^ 8(4(b%4) + 2hh)) + 8192 s2 +
-  //   4096 hh + 128 (b/4).
+  // Lane parts of the LDS operand addresses.
+  //   QK step ks < 32 (bytes): chunk 2ks + G of row hl -> qk_base + 32 ks;
+  //   QK rope step 32 + i (bf16 elements): (rope_base ^ 16i);
+  //   PV (bytes; see the B-operand note in the loop): row 16 s2 + 8 hh + 4G + j/4, columns
+  //   32b + 16 (gamma % 2) + 4 (j % 4) -> pv_base(hh) + 1280 (16 s2 + 8 hh) + 64 b, where the
+  //   row's pad 4 (j/4) + (2 hh + G) % 4 depends on hh.
   auto qk_base_of = [&](int ln) {
     const int hl_ = ln & 31, G_ = ln >> 5;
-    return hl_ * kLat + ((G_ ^ lat_swz(hl_)) << 3);
+    return lat_row_byte(hl_) + 16 * G_;
   };
   auto rope_base_of = [&](int ln) {
     const int hl_ = ln & 31, G_ = ln >> 5;
     return kRopeOff + hl_ * 64 + ((G_ ^ ((hl_ >> 1) & 7)) << 3);
   };
-  auto pv_base_of = [&](int ln) {
-    const int pj = ln & 15, G_ = ln >> 5, jq = pj >> 2;
-    const int cl = 2 * ((ln >> 4) & 1) + ((pj & 3) >> 1);
-    return (4 * G_ + jq) * kLat + ((4 * jq + (cl ^ G_)) << 3) + 4 * (pj & 1);
+  auto pv_base_of = [&](int ln, int hh) {
+    const int pj = ln & 15, G_ = ln >> 5, jq = pj >> 2, gam = (ln >> 4) & 1;
+    return (4 * G_ + jq) * kRowB + 16 * (4 * jq + ((2 * hh + G_) & 3)) + 32 * gam + 8 * (pj & 3);
   };
 
   f32x16 O[16];
@@ -571,21 +576,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     {
       int ln = lane_id;
       asm volatile("" : "+v"(ln));
-      // byte offsets into sK of the eight latent (ks % 8) and four rope lane bases of this
-      // tile's buffer, opaque to the compiler so each load is one LDS instruction with a
-      // constant offset
+      // byte offsets into sK of the latent and the four rope lane bases of this tile's
+      // buffer, opaque to the compiler so each load is one LDS instruction with a constant
+      // offset
       const int kbytes = 2 * kbuf_of(tile) * kTile;
-      int qoff[8], roff[4];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qoff[i] = kbytes + 2 * (qk_base_of(ln) ^ (16 * i));
+      int qoff = kbytes + qk_base_of(ln), roff[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) roff[i] = kbytes + 2 * (rope_base_of(ln) ^ (16 * i));
-#pragma unroll
-      for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(qoff[i]));
+      asm volatile("" : "+v"(qoff));
 #pragma unroll
       for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(roff[i]));
       auto kload = [&](int ks) {
-        const int off = ks < 32 ? qoff[ks & 7] + 256 * (ks >> 3) : roff[ks - 32];
+        const int off = ks < 32 ? qoff + 32 * ks : roff[ks - 32];
         return *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(sK) + off);
       };
       u32x4 kq[kDepth];
@@ -635,27 +637,23 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     // PV B-operand: dv block b, k-step s2: lane l needs V[acc_row(8*s2 + kk, G)][32b + l%32]
     // for kk = 0..7.  Two transpose reads give kk 0..3 and 4..7: in each 16-lane group
     // (gamma = l/16, j = l%16) lane j addresses row 16*s2 + 8*hh + 4*G + j/4 at columns
-    // 32b + 16*(gamma%2) + 4*(j%4) .. +3, i.e. logical chunk 4b + 2*(gamma%2) + (j%4)/2.
+    // 32b + 16*(gamma%2) + 4*(j%4) .. +3.
     int pln = lane_id;
     asm volatile("" : "+v"(pln));
-    // byte offsets into sK of the eight lane bases (b % 4, hh), opaque as for QK
-    int poff[8];
+    // byte offsets into sK of the two lane bases (hh), opaque as for QK
+    int poff[2];
     {
       const int kbytes = 2 * kbuf_of(tile) * kTile;
-      const int pv_base = pv_base_of(pln);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int bb = i >> 1, hh = i & 1;
-        poff[i] = kbytes + 2 * ((pv_base ^ (8 * (4 * bb + 2 * hh))) + 4096 * hh);
-      }
+      for (int hh = 0; hh < 2; ++hh) poff[hh] = kbytes + pv_base_of(pln, hh);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(poff[i]));
+      for (int i = 0; i < 2; ++i) asm volatile("" : "+v"(poff[i]));
     }
     // PV steps run k-step major: step = 16 * s2 + b
     auto vaddr = [&](int step, int hh) {
       const int b = step & 15, s2 = step >> 4;
-      return reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(sK) + poff[(b & 3) * 2 + hh] +
-                                               2 * (8192 * s2 + 128 * (b >> 2)));
+      return reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(sK) + poff[hh] +
+                                               kRowB * (16 * s2 + 8 * hh) + 64 * b);
     };
     u32x2 vq[kDepthV][2];
 #pragma unroll
