@@ -34,6 +34,9 @@ constexpr int kRowB = 1280;             // LDS bytes per latent row slot (1024 B
 constexpr int kRopeOff = kT * kRowB / 2;   // rope region: [32][64] bf16 after the latent rows
 constexpr int kTile = kRopeOff + kT * 64;  // bf16 per tile (45,056 bytes)
 constexpr int kCMax = 2048;             // positions per split handled by one workgroup
+// Slot list length: the copies run up to three tiles past the last one and the scale copies
+// one tile further, so indices reach (kCMax / kT + 4) * kT - 1; the tail repeats a valid slot.
+constexpr int kSlotLen = kCMax + 4 * kT;
 constexpr int kDepth = 4;               // LDS operand loads kept in flight (QK)
 constexpr int kDepthV = 3;              // LDS operand load pairs kept in flight (PV)
 // Exponentials are taken against a per-head reference max fixed at the first tile, so P
@@ -110,11 +113,14 @@ struct Cfg {
 template <int NW, int FMT>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   using C = Cfg<NW, FMT>;
+  // load_slots(tile) reads up to index (tile + 1) * kT + kT - 1 (the scale copy of the next
+  // tile), for tile <= kCMax / kT - 1 + max(NS, 1)
+  static_assert((kCMax / kT + (C::NS > 1 ? C::NS : 1) + 1) * kT <= kSlotLen, "slot list too short");
   constexpr int NT = NW * 64;
   __shared__ __attribute__((aligned(16))) uint16_t sK[C::NK * kTile];
   __shared__ __attribute__((aligned(16))) uint8_t sRaw[C::RAW_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sScl[C::SCL_BYTES];
-  __shared__ int sSlots[kCMax];
+  __shared__ int sSlots[kSlotLen];
   __shared__ int sWcnt[8 * NW];
   __shared__ int sRestart;
 
@@ -265,7 +271,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   {
     const int first = n_valid > 0 ? sSlots[0] : 0;
     __syncthreads();
-    for (int i = n_valid + tid; i < kCMax; i += NT) sSlots[i] = first;
+    for (int i = n_valid + tid; i < kSlotLen; i += NT) sSlots[i] = first;
     __syncthreads();
   }
   // land q before the tile copies start, so no wait on them is placed at its first use
@@ -296,11 +302,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     const int t0 = tile * kT;
     // positions past the valid count read the split's first valid slot
 #pragma unroll
-    for (int j = 0; j < LP; ++j) sl[j] = sSlots[min(t0 + lat_token(min(wave + NW * j, C::NL - 1), ln), kCMax - 1)];
+    for (int j = 0; j < LP; ++j) sl[j] = sSlots[t0 + lat_token(min(wave + NW * j, C::NL - 1), ln)];
 #pragma unroll
-    for (int j = 0; j < RP; ++j) sl[LP + j] = sSlots[min(t0 + rope_token(min(wave + NW * j, C::RR - 1), ln), kCMax - 1)];
+    for (int j = 0; j < RP; ++j) sl[LP + j] = sSlots[t0 + rope_token(min(wave + NW * j, C::RR - 1), ln)];
     // the scale wave copies the scales of the following tile
-    if (FMT == 1) sl[LP + RP] = sSlots[min(t0 + kT + (ln >> 1), kCMax - 1)];
+    if (FMT == 1) sl[LP + RP] = sSlots[t0 + kT + (ln >> 1)];
   };
   // FP8 byte offset of a region of a slot's page: page * (648 << ps_log2) + add, with the
   // 32-bit page stride (at most 648 KB) in one 32 x 32 -> 64-bit multiply-add
