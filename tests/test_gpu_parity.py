@@ -217,22 +217,28 @@ def test_partials_only_match_oracle_partials(splits):
     assert np.all(np.abs(pg[f] - lc[f]) <= 1e-3 * np.maximum(1, np.abs(lc[f])))
 
 
-def test_merge_kernel_matches_oracle_merge():
-    rng = np.random.default_rng(2)
-    R, S, H = 5, 7, 40
+# S = 7 and 8: a partial and a whole batch of eight chunks loaded together; 65, 129 and 256
+# (the plan's maximum): more chunk LSEs than lanes, held two, three and four per lane
+@pytest.mark.parametrize("R,S,H", [(5, 7, 40), (3, 8, 32), (3, 65, 16), (2, 129, 16), (2, 256, 16)])
+def test_merge_kernel_matches_oracle_merge(R, S, H):
+    rng = np.random.default_rng(2 + S)
     oc = rng.standard_normal((R, S, H, 512))
     lc = rng.standard_normal((R, S, H)) * 3
     lc[rng.random((R, S, H)) < 0.3] = -np.inf
     lc[0, :, 0] = -np.inf                                 # an all-empty (row, head)
     sinks = rng.standard_normal(H).astype(np.float32)
-    sinks[:10] = -np.inf
+    sinks[:H // 4] = -np.inf
     o, l = orc.merge_partials(oc.astype(np.float32).astype(np.float64),
                               lc.astype(np.float32).astype(np.float64), sinks)
-    announce("merge kernel")
+    announce(f"merge kernel R={R} S={S} H={H}")
     out, lse = B.merge_partials(torch.from_numpy(oc).float().to(DEV),
                                 torch.from_numpy(lc).float().to(DEV),
                                 torch.from_numpy(sinks).to(DEV))
-    compare(out, lse, o, l, max_abs=8e-3, mean_abs=1e-3, lse_rel=1e-5, what="merge")
+    # N(0,1) partial rows merge to outputs of a few units, so the output's bf16 rounding (half
+    # an ulp: 2^-8 of the value at most) dominates; fp32 accumulation adds far less than 1e-5
+    compare(out, lse, o, l, max_abs=0.05, mean_abs=1e-3, lse_rel=1e-5, what="merge")
+    d = np.abs(out.float().cpu().double().numpy() - o)
+    assert np.all(d <= np.abs(o) * 2.0 ** -8 + 1e-5), "merge: beyond one bf16 rounding of the oracle"
 
 
 # ------------------------------------------------------------------ edge cases
