@@ -528,14 +528,23 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     return (4 * G_ + jq) * kRowB + 16 * (4 * jq + ((2 * hh + G_) & 3)) + 32 * gam + 8 * (pj & 3);
   };
 
-  f32x16 O[16];
+  // O blocks are accumulated by compiler-scheduled MFMAs in AGPRs.  With three or four
+  // waves, block 15 instead lives in VGPRs (a VGPR-form MFMA): that leaves 16 AGPRs for the
+  // QK scores, so no O block has to be moved out of the accumulation registers and back each
+  // tile.  (Smaller workgroups keep more copy registers live and stay all-AGPR.)
+  constexpr bool kO15V = NW >= 3;
+  f32x16 O[kO15V ? 15 : 16];
+  f32x16 O15;
+  // array slot of an AGPR block (block 15 never reaches it when it lives in VGPRs)
+  auto ob_index = [&](int b) { return kO15V ? b % 15 : b; };
   float l_part;
   const int ntiles = (n_valid + kT - 1) / kT;
   // The pass over the tiles is repeated only if some head's reference max had to be
   // raised (kRestartLog2); O is dead across the repeat.
   for (;;) {
 #pragma unroll
-  for (int b = 0; b < 16; ++b) O[b] = f32x16{};
+  for (int b = 0; b < (kO15V ? 15 : 16); ++b) O[b] = f32x16{};
+  O15 = f32x16{};
   l_part = 0.f;
   if (ntiles > 0) {
     if (FMT == 1) issue_first_scales();
@@ -677,7 +686,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         vq[step % kDepthV][0] = lds_read_tr16(vaddr(step + kDepthV, 0));
         vq[step % kDepthV][1] = lds_read_tr16(vaddr(step + kDepthV, 1));
       }
-      O[step & 15] = mfma32x32x16(u32x4{v0[0], v0[1], v1[0], v1[1]}, p, O[step & 15]);
+      const u32x4 va = u32x4{v0[0], v0[1], v1[0], v1[1]};
+      if (kO15V && (step & 15) == 15)
+        mfma32x32x16_vgpr(va, p, O15);
+      else
+        O[ob_index(step & 15)] = mfma32x32x16(va, p, O[ob_index(step & 15)]);
     };
     auto pack8 = [&](int s2) {
       return u32x4{pack_bf16x2(s[8 * s2 + 0], s[8 * s2 + 1]), pack_bf16x2(s[8 * s2 + 2], s[8 * s2 + 3]),
@@ -791,6 +804,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     }
   }
   wait_vm();  // drain the copies issued past the last tile
+  if (kO15V) mfma_vgpr_drain();
   if (!restart) break;
   __syncthreads();  // every thread has seen the flag
   if (tid == 0) sRestart = 0;
@@ -833,7 +847,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       float* po = a.part_o + (rs * a.H + h) * kV + 4 * G;
 #pragma unroll
       for (int b = 0; b < 16; ++b) {
-        const f32x16 ob = O[b];
+        const f32x16 ob = kO15V && b == 15 ? O15 : O[ob_index(b)];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           *reinterpret_cast<f32x4*>(po + 32 * b + 8 * k) =
@@ -859,7 +873,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
       for (int bb = 0; bb < 8; ++bb) {
-        const f32x16 ob = O[8 * half + bb];
+        const f32x16 ob = kO15V && 8 * half + bb == 15 ? O15 : O[ob_index(8 * half + bb)];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           *reinterpret_cast<u32x2*>(stage + w_off + 64 * bb + 16 * k) =

@@ -28,6 +28,16 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const u32x4& a, const u32x4& b, f
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
+// The same MFMA with its accumulator in VGPRs, accumulating in place.  The compiler does not
+// see its latency: the s_nop in front covers a VALU write of an operand just before it, and
+// mfma_vgpr_drain() must run before any other instruction reads `c` after the last one.
+__device__ __forceinline__ void mfma32x32x16_vgpr(const u32x4& a, const u32x4& b, f32x16& c) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+// Wait states for the result of a VGPR-form 32x32x16 MFMA (8 passes) to be readable.
+__device__ __forceinline__ void mfma_vgpr_drain() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
 
 // LDS transpose read of four 16-bit values.  Within each group of 16 lanes, lane i
 // receives element i%4 of the 8-byte blocks addressed by lanes 4k + i/4, k = 0..3.
