@@ -842,20 +842,43 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // registers 4k..4k+3 are four consecutive dv, stored as one 8-byte (bf16) or 16-byte
   // (fp32 partial) piece.
   if (a.write_partials) {
+    // fp32 partials through a per-wave LDS stage, in four quarters of 128 dv: each lane
+    // writes its 16-byte runs into rows of 528 bytes (one per head; the 16-byte pad keeps the
+    // 32 rows' writes on different banks), then reads back 16-byte chunks along dv, so every
+    // global store writes two whole 512-byte row quarters instead of 32-byte pieces of 32 rows.
+    // A wave reads back only what it wrote, in order, so no barrier is needed between passes.
+    constexpr int kPitchP = 528;
+    static_assert(NW * 32 * kPitchP <= (int)sizeof(sK), "partial stage exceeds the K buffers");
     const size_t rs = (size_t)row * a.S + split;
-    if (h_ok) {
-      float* po = a.part_o + (rs * a.H + h) * kV + 4 * G;
+    __syncthreads();   // every wave is past its last read of sK (and its copies drained)
+    uint8_t* stage = reinterpret_cast<uint8_t*>(sK) + wave * (32 * kPitchP);
+    int ln = lane_id;
+    asm volatile("" : "+v"(ln));
+    const int w_off = (ln & 31) * kPitchP + 16 * (ln >> 5);        // row = head, +4 dv for G
+    const int r_off = (ln >> 5) * kPitchP + 16 * (ln & 31);        // row (ln / 32) + 2i, chunk
 #pragma unroll
-      for (int b = 0; b < 16; ++b) {
+    for (int qd = 0; qd < 4; ++qd) {
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int b = 4 * qd + bb;
         const f32x16 ob = kO15V && b == 15 ? O15 : O[ob_index(b)];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          *reinterpret_cast<f32x4*>(po + 32 * b + 8 * k) =
+          *reinterpret_cast<f32x4*>(stage + w_off + 128 * bb + 32 * k) =
               f32x4{ob[4 * k] * factor, ob[4 * k + 1] * factor, ob[4 * k + 2] * factor, ob[4 * k + 3] * factor};
-        __builtin_amdgcn_sched_barrier(0);
       }
-      if (G == 0) a.part_lse[rs * a.H + h] = lse_v;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int hr = 32 * wave + 2 * i + (ln >> 5);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(stage + r_off + 2 * i * kPitchP);
+        if (hr < a.H)
+          *reinterpret_cast<f32x4*>(a.part_o + (rs * a.H + hr) * kV + 128 * qd + 4 * (ln & 31)) = v;
+        if (i % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // four reads in flight at most
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if (G == 0 && h_ok) a.part_lse[rs * a.H + h] = lse_v;
   } else {
     // bf16 output through a per-wave LDS stage (the K buffers are free now), in two halves
     // of 256 dv: each lane writes its 8-byte runs into rows of 520 bytes (one per head;
