@@ -5,9 +5,9 @@
 // produces per-chunk results that are merged afterwards; here one kernel does both:
 //   M = max(max_c lse_c, sigma), w_c = exp(lse_c - M), w_s = exp(sigma - M),
 //   out = sum_c w_c o_c / (sum_c w_c + w_s), lse = M + ln(sum_c w_c + w_s).
-// One 64-lane wave per (row, head); each lane owns 8 of the 512 output dims.  All chunk
-// LSEs, then the partial rows of eight chunks at a time, are loaded before use, so a merge
-// costs a few memory round trips instead of one per chunk.
+// One 64-lane wave per (row, head); each lane owns 8 of the 512 output dims.  The partial
+// rows of the first sixteen chunks and all chunk LSEs are loaded together, later chunks
+// sixteen at a time, so a merge costs one memory round trip per sixteen chunks.
 #include "sparse_mla.h"
 #include "smla_device.h"
 #include "smla_kernels.h"
@@ -18,6 +18,7 @@ namespace {
 
 constexpr int kMaxChunks = 256;   // the largest split count a plan allows
 static_assert(kMaxChunks >= SMLA_MAX_SPLITS, "merge chunk capacity below the plan limit");
+constexpr int kBatch = 16;        // partial rows loaded together
 
 __global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ po,
                                                    const float* __restrict__ pl, int R, int S,
@@ -32,7 +33,21 @@ __global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ po,
   const float sink = (sinks != nullptr) ? sinks[h] : -INFINITY;
   const float sig2 = sink * kLog2e;
   const float* plr = pl + (size_t)r * S * H + h;
-  // every chunk's LSE is loaded at once: lane l holds chunks l, l + 64, ... (log2 domain)
+  // lane owns output dims 8l..8l+7; the partial rows of the first kBatch chunks are loaded
+  // together with the chunk LSEs (before the weights are known), so a merge of up to kBatch
+  // chunks costs one memory round trip
+  const float* src0 = po + ((size_t)r * S * H + h) * kV + 8 * lane;
+  const size_t cstride = (size_t)H * kV;
+  f32x4 x[kBatch][2];
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) {
+    if (j < S) {   // wave-uniform; rows past S are never read (their weight is 0)
+      const float* src = src0 + j * cstride;
+      x[j][0] = *reinterpret_cast<const f32x4*>(src);
+      x[j][1] = *reinterpret_cast<const f32x4*>(src + 4);
+    }
+  }
+  // every chunk's LSE at once: lane l holds chunks l, l + 64, ... (log2 domain)
   float l2[kMaxChunks / 64];
   float mc = -INFINITY;
 #pragma unroll
@@ -60,20 +75,17 @@ __global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ po,
     for (int off = 32; off >= 1; off >>= 1) zs += __shfl_xor(zs, off);
     const float z = zs + ((sig2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sig2 - M));
     __syncthreads();
-    // out = sum_c w_c o_c / z: lane owns dims 8l..8l+7; the partial rows of kBatch chunks
-    // are loaded before any of them is used, so their latencies overlap
-    const float* src0 = po + ((size_t)r * S * H + h) * kV + 8 * lane;
-    const size_t cstride = (size_t)H * kV;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    constexpr int kBatch = 8;
     for (int c0 = 0; c0 < S; c0 += kBatch) {
-      f32x4 x[kBatch][2];
+      if (c0 > 0) {   // later batches: their loads, all before any use
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int c = min(c0 + j, S - 1);
-        const float* src = src0 + c * cstride;
-        x[j][0] = *reinterpret_cast<const f32x4*>(src);
-        x[j][1] = *reinterpret_cast<const f32x4*>(src + 4);
+        for (int j = 0; j < kBatch; ++j) {
+          if (c0 + j < S) {
+            const float* src = src0 + (c0 + j) * cstride;
+            x[j][0] = *reinterpret_cast<const f32x4*>(src);
+            x[j][1] = *reinterpret_cast<const f32x4*>(src + 4);
+          }
+        }
       }
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
