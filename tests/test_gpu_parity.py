@@ -320,14 +320,17 @@ def test_small_topk_with_strong_sinks(topk, sink):
         assert np.abs(od[0] - o[0]).max() > 2e-2
 
 
-@pytest.mark.parametrize("fmt,alpha", [("fp8", 20.0), ("fp8", 40.0), ("bf16", 40.0)])
-def test_score_far_above_the_first_tiles(fmt, alpha):
+# 128 heads: four waves, whose last O block is accumulated in VGPRs and zeroed again for the
+# repeated pass
+@pytest.mark.parametrize("fmt,alpha,heads", [("fp8", 20.0, 32), ("fp8", 40.0, 32), ("bf16", 40.0, 32),
+                                             ("fp8", 40.0, 128), ("bf16", 40.0, 128)])
+def test_score_far_above_the_first_tiles(fmt, alpha, heads):
     """One entry in a later tile whose rope part is alpha times head j's rope query: its
     score lies far above everything the kernel saw in the first tile, so the reference
     max must be raised and the pass repeated.  alpha = 40 puts the excess past the fp32
     range of exp2 (the probability computed against the old reference is +inf)."""
     from oracle import cache_store_oracle as cso
-    inp = _small(fmt=fmt, heads=32, topk=256, nreq=2, rows=(1, 1), ctx=(700, 900), seed=91)
+    inp = _small(fmt=fmt, heads=heads, topk=256, nreq=2, rows=(1, 1), ctx=(700, 900), seed=91)
     ps, j, t = inp.spec.page_size, 5, 5 * 32 + 3
     pos = int(inp.indices[0, t])
     page = int(inp.page_table[int(inp.row_req[0]), pos // ps])
@@ -348,7 +351,7 @@ def test_score_far_above_the_first_tiles(fmt, alpha):
     first = (rows[:32] @ qd).max() * c
     spike = float(rows[32] @ qd) * c
     assert spike - first > (120.0 if alpha >= 40 else 40.0), (spike, first)
-    announce(f"restart {fmt} alpha={alpha} excess={spike - first:.1f}")
+    announce(f"restart {fmt} alpha={alpha} heads={heads} excess={spike - first:.1f}")
     out, lse = gpu_decode(inp)
     o, l = oracle_decode(inp)
     compare(out, lse, o, l, what=f"restart {fmt} alpha={alpha}")
