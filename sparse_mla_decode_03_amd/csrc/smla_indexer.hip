@@ -244,6 +244,19 @@ __device__ __forceinline__ void load_keys4(const float* lg, int i4, int n, uint3
   }
 }
 
+constexpr int kPerThread = 8;                  // consecutive positions per thread and round
+// Keys of positions i .. i + kPerThread - 1: all their loads issued before any key is formed.
+__device__ __forceinline__ void load_keys_run(const float* lg, int ip, int n, uint32_t (&k)[kPerThread]) {
+  uint32_t q[kPerThread / 4][4];
+#pragma unroll
+  for (int g = 0; g < kPerThread / 4; ++g) load_keys4(lg, ip + 4 * g, n, q[g]);
+#pragma unroll
+  for (int g = 0; g < kPerThread / 4; ++g)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) k[4 * g + e] = q[g][e];
+}
+constexpr int kRound = kPerThread * kTopkThreads;
+
 // The bin holding the need-th largest of a histogram counted from the top: thread i owns
 // bins nbins-1-per*i .. nbins-per*(i+1) (descending).  Writes (bin, count still needed
 // from it) to sel.  All threads call it.
@@ -296,12 +309,12 @@ __global__ __launch_bounds__(kTopkThreads) void indexer_topk_kernel(IndexerTopkA
     sCount = 0;
   }
   __syncthreads();
-  for (int i4 = 4 * tid; i4 < n; i4 += 4 * kTopkThreads) {
-    uint32_t k[4];
-    load_keys4(lg, i4, n, k);
+  for (int ip = kPerThread * tid; ip < n; ip += kRound) {
+    uint32_t k[kPerThread];
+    load_keys_run(lg, ip, n, k);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (i4 + e < n) atomicAdd(&sHist[k[e] >> 21], 1);
+    for (int e = 0; e < kPerThread; ++e)
+      if (ip + e < n) atomicAdd(&sHist[k[e] >> 21], 1);
   }
   __syncthreads();
   find_bin(sHist, 2048, K, sScan, sSel);
@@ -314,15 +327,15 @@ __global__ __launch_bounds__(kTopkThreads) void indexer_topk_kernel(IndexerTopkA
   int ties_total = -1;                          // known only on the LDS path
   if (c1 <= kCandCap) {
     // ---- pass 2: the first bin's keys and positions into LDS, then select there ----
-    for (int i4 = 4 * tid; i4 < n; i4 += 4 * kTopkThreads) {
-      uint32_t k[4];
-      load_keys4(lg, i4, n, k);
+    for (int ip = kPerThread * tid; ip < n; ip += kRound) {
+      uint32_t k[kPerThread];
+      load_keys_run(lg, ip, n, k);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (i4 + e < n && (k[e] >> 21) == b1) {
+      for (int e = 0; e < kPerThread; ++e)
+        if (ip + e < n && (k[e] >> 21) == b1) {
           const int slot = atomicAdd(&sCount, 1);
           sCandKey[slot] = k[e];
-          sCandPos[slot] = i4 + e;
+          sCandPos[slot] = ip + e;
         }
     }
     uint32_t prefix = b1 << 21, mask = 0x7FFu << 21;
@@ -354,12 +367,12 @@ __global__ __launch_bounds__(kTopkThreads) void indexer_topk_kernel(IndexerTopkA
       const int nbins = pass == 0 ? 2048 : 1024;
       for (int i = tid; i < 2048; i += kTopkThreads) sHist[i] = 0;
       __syncthreads();
-      for (int i4 = 4 * tid; i4 < n; i4 += 4 * kTopkThreads) {
-        uint32_t k[4];
-        load_keys4(lg, i4, n, k);
+      for (int ip = kPerThread * tid; ip < n; ip += kRound) {
+        uint32_t k[kPerThread];
+        load_keys_run(lg, ip, n, k);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (i4 + e < n && (k[e] & mask) == prefix) atomicAdd(&sHist[(k[e] >> shift) & (nbins - 1)], 1);
+        for (int e = 0; e < kPerThread; ++e)
+          if (ip + e < n && (k[e] & mask) == prefix) atomicAdd(&sHist[(k[e] >> shift) & (nbins - 1)], 1);
       }
       __syncthreads();
       find_bin(sHist, nbins, need, sScan, sSel);
@@ -371,31 +384,33 @@ __global__ __launch_bounds__(kTopkThreads) void indexer_topk_kernel(IndexerTopkA
     T = prefix;
   }
   // ---- last pass: every key above T and the first `need` keys equal to T, written in
-  // ascending position order.  When every tie is taken, one scan per round suffices.
+  // ascending position order: a thread owns kPerThread consecutive positions of each round, so a
+  // block scan over the threads keeps that order.  When every tie is taken, one scan per
+  // round suffices.
   const bool all_ties = ties_total == need;
   int ties_before = 0, out_before = 0;
 #pragma unroll 1
-  for (int base = 0; base < n; base += 4 * kTopkThreads) {
-    const int i4 = base + 4 * tid;
-    uint32_t k[4];
-    load_keys4(lg, i4, n, k);
-    int sel[4], cnt = 0;
+  for (int base = 0; base < n; base += kRound) {
+    const int ip = base + kPerThread * tid;
+    uint32_t k[kPerThread];
+    load_keys_run(lg, ip, n, k);
+    int sel[kPerThread], cnt = 0;
     if (all_ties) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sel[e] = (i4 + e < n && k[e] >= T) ? 1 : 0;
+      for (int e = 0; e < kPerThread; ++e) {
+        sel[e] = (ip + e < n && k[e] >= T) ? 1 : 0;
         cnt += sel[e];
       }
     } else {
       int tie = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) tie += (i4 + e < n && k[e] == T) ? 1 : 0;
+      for (int e = 0; e < kPerThread; ++e) tie += (ip + e < n && k[e] == T) ? 1 : 0;
       int tie_total;
       int tie_rank = ties_before + block_excl_scan(tie, sScan, tie_total);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < kPerThread; ++e) {
         bool s2 = false;
-        if (i4 + e < n) {
+        if (ip + e < n) {
           if (k[e] > T) s2 = true;
           else if (k[e] == T) { s2 = tie_rank < need; ++tie_rank; }
         }
@@ -407,8 +422,8 @@ __global__ __launch_bounds__(kTopkThreads) void indexer_topk_kernel(IndexerTopkA
     int out_total;
     int pos = out_before + block_excl_scan(cnt, sScan, out_total);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (sel[e] && pos < K) out[pos] = i4 + e;
+    for (int e = 0; e < kPerThread; ++e) {
+      if (sel[e] && pos < K) out[pos] = ip + e;
       pos += sel[e];
     }
     out_before += out_total;
