@@ -419,9 +419,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // puts token 8r + lane / 8, chunk lane % 8, at chunk (lane % 8) ^ (lane / 16) ^ 4(r % 2);
   // per-tensor FP8 rope instruction r holds token 16r + lane / 4, codes 16(lane % 4) .. +15,
   // converted to logical chunks 2(lane % 4) and 2(lane % 4) + 1 of the token's rope row.
-  // The lanes with bit 3 of c set convert and write the second 16-byte half of their
-  // unit first (they load the two 8-byte halves of the raw unit swapped): each 16-byte
-  // write then covers 16 different chunk slots per 16 lanes instead of every other one.
+  // The lanes with bit 2 of c set convert and write the second 16-byte half of their
+  // unit first (they load the two 8-byte halves of the raw unit swapped).  A 16-byte LDS
+  // write is served eight lanes at a time against 128 bytes of banks: units c and c + 4
+  // start 128 bytes apart, so with the swap each group of eight lanes writes eight
+  // different 16-byte bank slots.
   struct DqBase {
     int raw;    // byte offset into sRaw of the half of this lane's unit written first
     int scl;    // byte offset into sScl of this lane's scale byte for instruction `wave`
@@ -432,9 +434,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   auto dq_base = [&](int tile, int ln) {
     DqBase d;
     const int G_ = ln >> 5, c = ln & 31;
-    d.raw = (C::NS > 0 ? tile % C::NS : 0) * (20 * 1024) + wave * 1024 + 16 * ln + 8 * ((c >> 3) & 1);
+    d.raw = (C::NS > 0 ? tile % C::NS : 0) * (20 * 1024) + wave * 1024 + 16 * ln + 8 * ((c >> 2) & 1);
     d.scl = (tile % (C::NS + 1)) * 256 + 16 * wave + 8 * G_ + (c >> 2);
-    d.lat = (kRowB + 64) * G_ + 32 * c + 16 * ((c >> 3) & 1);
+    d.lat = (kRowB + 64) * G_ + 32 * c + 16 * ((c >> 2) & 1);
     d.rope = FMT == 2 ? 128 * (ln >> 2) + 16 * ((2 * (ln & 3)) ^ ((ln >> 3) & 7))
                       : 128 * (ln >> 3) + 16 * ((ln & 7) ^ (ln >> 4));
     d.kb = 2 * kbuf_of(tile) * kTile;
