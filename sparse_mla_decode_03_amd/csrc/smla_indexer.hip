@@ -206,6 +206,7 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kCandCap = 6144;                 // candidates of the first bin kept in LDS
+constexpr int kMergeCap = 2048;                // largest K whose selection is merged in LDS
 
 // Block-wide exclusive prefix sum of one value per thread; returns the prefix and the
 // total.  Uses `scratch` (kTopkWaves ints).
@@ -257,6 +258,16 @@ __device__ __forceinline__ void load_keys_run(const float* lg, int ip, int n, ui
 }
 constexpr int kRound = kPerThread * kTopkThreads;
 
+// Number of entries of the ascending list arr[0 .. len) below p.
+__device__ __forceinline__ int count_below(const int* arr, int len, int p) {
+  int lo = 0, hi = len;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (arr[mid] < p) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
 // The bin holding the need-th largest of a histogram counted from the top: thread i owns
 // bins nbins-1-per*i .. nbins-per*(i+1) (descending).  Writes (bin, count still needed
 // from it) to sel.  All threads call it.
@@ -287,9 +298,9 @@ __global__ __launch_bounds__(kTopkThreads) void indexer_topk_kernel(IndexerTopkA
   __shared__ int sHist[2048];
   __shared__ uint32_t sCandKey[kCandCap];
   __shared__ int sCandPos[kCandCap];
+  __shared__ int sAbove[kMergeCap];
   __shared__ int sScan[kTopkWaves];
   __shared__ int sSel[2];
-  __shared__ int sCount;
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int n = max(0, min(a.row_len[r], a.width));
@@ -306,7 +317,6 @@ __global__ __launch_bounds__(kTopkThreads) void indexer_topk_kernel(IndexerTopkA
   if (tid == 0) {
     sSel[0] = 0;
     sSel[1] = K;
-    sCount = 0;
   }
   __syncthreads();
   for (int ip = kPerThread * tid; ip < n; ip += kRound) {
@@ -325,18 +335,46 @@ __global__ __launch_bounds__(kTopkThreads) void indexer_topk_kernel(IndexerTopkA
 
   uint32_t T;
   int ties_total = -1;                          // known only on the LDS path
+  // With K <= kMergeCap the row is read twice: pass 2 also keeps, in position order, the
+  // positions of the bins above b1 (fewer than K of them), and the selection from b1's
+  // candidates is merged with that list in LDS instead of a third pass over the row.
+  const bool merge = c1 <= kCandCap && K <= kMergeCap;   // block uniform
+  int n_above = 0;
   if (c1 <= kCandCap) {
-    // ---- pass 2: the first bin's keys and positions into LDS, then select there ----
-    for (int ip = kPerThread * tid; ip < n; ip += kRound) {
+    // ---- pass 2: the first bin's keys and positions into LDS in position order (one block
+    // scan per round over packed counts: candidates in the low half, higher bins in the
+    // high half; each total is at most kRound), then select there ----
+    int cand_before = 0;
+#pragma unroll 1
+    for (int base = 0; base < n; base += kRound) {
+      const int ip = base + kPerThread * tid;
       uint32_t k[kPerThread];
       load_keys_run(lg, ip, n, k);
+      int nc = 0, na = 0;
 #pragma unroll
       for (int e = 0; e < kPerThread; ++e)
-        if (ip + e < n && (k[e] >> 21) == b1) {
-          const int slot = atomicAdd(&sCount, 1);
-          sCandKey[slot] = k[e];
-          sCandPos[slot] = ip + e;
+        if (ip + e < n) {
+          nc += (k[e] >> 21) == b1 ? 1 : 0;
+          na += (k[e] >> 21) > b1 ? 1 : 0;
         }
+      int tot;
+      const int pre = block_excl_scan(nc | (na << 16), sScan, tot);
+      int pc = cand_before + (pre & 0xFFFF), pa = n_above + (pre >> 16);
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e)
+        if (ip + e < n) {
+          const uint32_t b = k[e] >> 21;
+          if (b == b1) {
+            sCandKey[pc] = k[e];
+            sCandPos[pc] = ip + e;
+            ++pc;
+          } else if (b > b1) {
+            if (merge) sAbove[pa] = ip + e;
+            ++pa;
+          }
+        }
+      cand_before += tot & 0xFFFF;
+      n_above += tot >> 16;
     }
     uint32_t prefix = b1 << 21, mask = 0x7FFu << 21;
 #pragma unroll 1
@@ -358,6 +396,45 @@ __global__ __launch_bounds__(kTopkThreads) void indexer_topk_kernel(IndexerTopkA
       if (pass == 1) ties_total = sHist[sSel[0]];
     }
     T = prefix;
+    if (merge) {
+      // ---- selection from the candidates (position order): keys above T and the first
+      // `need` keys equal to T, compacted into sHist; then the two ascending lists are
+      // merged into the output by rank ----
+      int* sPick = sHist;
+      const bool all_ties = ties_total == need;
+      __syncthreads();                           // every thread has read ties_total
+      int ties_before = 0, n_pick = 0;
+#pragma unroll 1
+      for (int c0 = 0; c0 < c1; c0 += kTopkThreads) {
+        const int c = c0 + tid;
+        const uint32_t kc = c < c1 ? sCandKey[c] : 0u;
+        const bool in = c < c1;
+        bool sel = in && kc > T;
+        if (all_ties) {
+          sel = sel || (in && kc == T);
+        } else {
+          const int tie = in && kc == T ? 1 : 0;
+          int tie_total;
+          const int rank = ties_before + block_excl_scan(tie, sScan, tie_total);
+          if (tie) sel = rank < need;
+          ties_before += tie_total;
+        }
+        int pick_total;
+        const int at = n_pick + block_excl_scan(sel ? 1 : 0, sScan, pick_total);
+        if (sel) sPick[at] = sCandPos[c];
+        n_pick += pick_total;
+      }
+      __syncthreads();
+      for (int i = tid; i < n_above; i += kTopkThreads) {
+        const int p = sAbove[i];
+        out[i + count_below(sPick, n_pick, p)] = p;
+      }
+      for (int j = tid; j < n_pick; j += kTopkThreads) {
+        const int p = sPick[j];
+        out[j + count_below(sAbove, n_above, p)] = p;
+      }
+      return;
+    }
   } else {
     // ---- passes 2 and 3 over the row (a crowded first bin) ----
     uint32_t prefix = b1 << 21, mask = 0x7FFu << 21;
