@@ -172,6 +172,13 @@ def test_topk_edges():
     _topk_case(big, torch.tensor([20000, 20000, 19999], dtype=torch.int32), 2048, "crowded first bin")
     _topk_case(lg, lens, 1, "K = 1")
     _topk_case(lg, lens, 3000, "K = 3000")
+    _topk_case(lg, lens, 700, "K = 700")
+    _topk_case(tied, lens, 1000, "five distinct values, K = 1000")
+    # about 5000 ties in the boundary bin (held in LDS; their ranks are taken over several
+    # rounds of the workgroup), with and without distinct larger values above them
+    four = torch.from_numpy(rng.integers(0, 4, (2, 20000)).astype(np.float32))
+    four[1, ::50] = torch.from_numpy(10.0 + rng.standard_normal(400).astype(np.float32))
+    _topk_case(four, torch.tensor([20000, 19999], dtype=torch.int32), 2048, "four values, ties in LDS")
 
 
 def test_indexer_then_decode():
