@@ -46,45 +46,59 @@ __device__ __forceinline__ uint32_t e4m3fn_rne(float v) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// Tokens per wave.  A wave issues its tokens' slot, latent and rope loads together, before
+// the slot is checked, so it waits for one memory round trip instead of two (slot, then
+// data).  More tokens per wave leave fewer waves to cover the latency: 2 and 4 were slower.
+constexpr int kTokPerWave = 1;
+
 template <int FMT>
 __global__ __launch_bounds__(256) void store_kernel(const uint16_t* __restrict__ latent,
                                                     const uint16_t* __restrict__ rope,
                                                     const int32_t* __restrict__ slots, int n,
                                                     int ps_log2, int num_slots, uint8_t* __restrict__ kv) {
-  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int tok0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kTokPerWave;
   const int lane = threadIdx.x & 63;
-  if (tok >= n) return;                       // the whole wave
-  const int slot = slots[tok];
-  if (slot < 0 || slot >= num_slots) return;  // the whole wave: skipped
-  const SlotAddr sa = slot_addr<FMT>(slot, ps_log2);
-  const u32x4 w = *reinterpret_cast<const u32x4*>(latent + (size_t)tok * 512 + 8 * lane);
-  if (lane < 8)
-    *reinterpret_cast<u32x4*>(kv + sa.rope + 16 * lane) =
-        *reinterpret_cast<const u32x4*>(rope + (size_t)tok * 64 + 8 * lane);
-  if (FMT == 1) {
-    float x[8];
+  if (tok0 >= n) return;                      // the whole wave
+  int slot[kTokPerWave];
+  u32x4 w[kTokPerWave], rv[kTokPerWave];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = bf16_lo(w[i]);
-      x[2 * i + 1] = bf16_hi(w[i]);
+  for (int i = 0; i < kTokPerWave; ++i) {
+    const int tok = tok0 + i;
+    const bool ok = tok < n;                  // wave uniform
+    slot[i] = ok ? slots[tok] : -1;
+    w[i] = ok ? *reinterpret_cast<const u32x4*>(latent + (size_t)tok * 512 + 8 * lane) : u32x4{};
+    rv[i] = ok && lane < 8 ? *reinterpret_cast<const u32x4*>(rope + (size_t)tok * 64 + 8 * lane) : u32x4{};
+  }
+#pragma unroll
+  for (int i = 0; i < kTokPerWave; ++i) {
+    if (slot[i] < 0 || slot[i] >= num_slots) continue;   // the whole wave: token skipped
+    const SlotAddr sa = slot_addr<FMT>(slot[i], ps_log2);
+    if (lane < 8) *reinterpret_cast<u32x4*>(kv + sa.rope + 16 * lane) = rv[i];
+    if (FMT == 1) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[2 * j] = bf16_lo(w[i][j]);
+        x[2 * j + 1] = bf16_hi(w[i][j]);
+      }
+      float am = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(x[j]));
+      // the group's eight lanes are lanes 8g .. 8g+7
+      am = fmaxf(am, __shfl_xor(am, 1));
+      am = fmaxf(am, __shfl_xor(am, 2));
+      am = fmaxf(am, __shfl_xor(am, 4));
+      const uint32_t e = ue8m0_for_amax(am);
+      const int sh = 127 - (int)e;            // x * 2^sh is exact
+      uint32_t c[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = e4m3fn_rne(__builtin_amdgcn_ldexpf(x[j], sh));
+      *reinterpret_cast<u32x2*>(kv + sa.latent + 8 * lane) =
+          u32x2{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
+      if ((lane & 7) == 0) kv[sa.scales + (lane >> 3)] = (uint8_t)e;
+    } else {
+      *reinterpret_cast<u32x4*>(kv + sa.latent + 16 * lane) = w[i];
     }
-    float am = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(x[i]));
-    // the group's eight lanes are lanes 8g .. 8g+7
-    am = fmaxf(am, __shfl_xor(am, 1));
-    am = fmaxf(am, __shfl_xor(am, 2));
-    am = fmaxf(am, __shfl_xor(am, 4));
-    const uint32_t e = ue8m0_for_amax(am);
-    const int sh = 127 - (int)e;              // x * 2^sh is exact
-    uint32_t c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = e4m3fn_rne(__builtin_amdgcn_ldexpf(x[i], sh));
-    *reinterpret_cast<u32x2*>(kv + sa.latent + 8 * lane) =
-        u32x2{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
-    if ((lane & 7) == 0) kv[sa.scales + (lane >> 3)] = (uint8_t)e;
-  } else {
-    *reinterpret_cast<u32x4*>(kv + sa.latent + 16 * lane) = w;
   }
 }
 
@@ -92,7 +106,7 @@ __global__ __launch_bounds__(256) void store_kernel(const uint16_t* __restrict__
 
 hipError_t launch_store(const uint16_t* latent, const uint16_t* rope, const int32_t* slots, int n,
                         int kv_format, int ps_log2, int num_slots, uint8_t* kv, hipStream_t st) {
-  const unsigned blocks = (unsigned)((n + 3) / 4);
+  const unsigned blocks = (unsigned)((n + 4 * kTokPerWave - 1) / (4 * kTokPerWave));
   if (kv_format == 1)
     hipLaunchKernelGGL(store_kernel<1>, dim3(blocks), dim3(256), 0, st, latent, rope, slots, n, ps_log2,
                        num_slots, kv);
