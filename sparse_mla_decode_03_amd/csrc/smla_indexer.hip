@@ -91,6 +91,10 @@ __global__ __launch_bounds__(256, 3) void indexer_logits_kernel(IndexerLogitsArg
   const int row = row0 + ri;
   const int row_len = min(a.row_len[row], a.width);
 
+  // the chunk's page ids are loaded first and stored to LDS after the query loads are
+  // issued, so storing them waits for the oldest load only
+  const int pt_p = p0 + tid;
+  const int pid = tid < kChunkPages && pt_p < npages_b ? a.page_table[(size_t)b * a.max_pages + pt_p] : 0;
   // A operands (queries) and weights of this wave's row: head block mb holds heads
   // 32mb + lane%32; k-step ks covers dims 64ks .. 64ks+63, lane half lane/32 its bytes
   // 32*(lane/32) .. +31.  The accumulator register j of a block holds head
@@ -117,14 +121,13 @@ __global__ __launch_bounds__(256, 3) void indexer_logits_kernel(IndexerLogitsArg
     }
   }
   if (tid < kChunkPages) {
-    const int p = p0 + tid;
-    const int pid = p < npages_b ? a.page_table[(size_t)b * a.max_pages + p] : 0;
-    const bool ok = p < npages_b && pid >= 0 && pid < a.num_pages;
+    const bool ok = pt_p < npages_b && pid >= 0 && pid < a.num_pages;
     sPage[tid] = ok ? pid : 0;                      // invalid pages are read from page 0
     sOk[tid] = ok;
   }
-  wait_vm();
-  __syncthreads();
+  // LDS-only barrier: the first page copies go out while the query and weight loads are
+  // still in flight (those are older, so the per-page vmcnt waits below also cover them)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   // Page copies: wave w's instruction j fills 1 KB of codes (tokens 8(4j + w) .. +7, lane
   // = physical chunk); wave 0 also copies the 64 scales.
