@@ -99,9 +99,12 @@ __global__ __launch_bounds__(256, 3) void indexer_logits_kernel(IndexerLogitsArg
   // 32mb + lane%32; k-step ks covers dims 64ks .. 64ks+63, lane half lane/32 its bytes
   // 32*(lane/32) .. +31.  The accumulator register j of a block holds head
   // 8(j/4) + 4(lane/32) + j%4, whose weight is wj[mb][j].
+  // Every wave loads (an inactive wave's row, row0 + wave % NN, is a real row whose values
+  // go unused): with no branch around these loads, storing the page ids below waits for the
+  // page-id load alone.
   i32x8 qa[2][2];
   float wj[2][16];
-  if (active) {
+  {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       const uint8_t* qh = a.q + ((size_t)row * kIdxHeads + 32 * mb + (lane & 31)) * kIdxDim + 32 * (lane >> 5);
@@ -125,9 +128,10 @@ __global__ __launch_bounds__(256, 3) void indexer_logits_kernel(IndexerLogitsArg
     sPage[tid] = ok ? pid : 0;                      // invalid pages are read from page 0
     sOk[tid] = ok;
   }
-  // LDS-only barrier: the first page copies go out while the query and weight loads are
-  // still in flight (those are older, so the per-page vmcnt waits below also cover them)
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // No wait for the query and weight loads here (the barrier waits for LDS operations
+  // only): the first page copies go out while those loads are still in flight.  They are
+  // older than the copies, so the per-page vmcnt waits below also cover them.
+  __syncthreads();
 
   // Page copies: wave w's instruction j fills 1 KB of codes (tokens 8(4j + w) .. +7, lane
   // = physical chunk); wave 0 also copies the 64 scales.
