@@ -201,6 +201,21 @@ def test_forced_splits_match_unsplit(splits):
     compare(out, lse, o, l, what=f"S={splits}")
 
 
+@pytest.mark.parametrize("splits", [None, 3])
+def test_topk_above_one_workgroup_capacity(splits):
+    """K = 5000 exceeds the 2048 positions one workgroup takes: the planner must split (at
+    least three chunks, the last one ragged), and the merged result matches the oracle."""
+    inp = _small(heads=64, topk=5000, nreq=2, rows=(1,), ctx=(6000, 9000), seed=29)
+    idx = inp.indices.clone()
+    idx[1, :300] = -1                     # a partly empty first chunk
+    o, l = oracle_decode(inp, indices=idx)
+    announce(f"K=5000 splits={splits}")
+    out, lse, info, _ = gpu_decode(inp, indices=idx, num_splits=0 if splits is None else splits,
+                                   return_info=True)
+    assert info.num_splits >= 3
+    compare(out, lse, o, l, what=f"K=5000 S={info.num_splits}")
+
+
 @pytest.mark.parametrize("splits", [2, 5, 16])
 def test_partials_only_match_oracle_partials(splits):
     inp = _small(heads=32, topk=128, nreq=2, rows=(2,), seed=23)
