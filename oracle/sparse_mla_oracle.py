@@ -147,23 +147,36 @@ def decode_entries(cache: np.ndarray, kv_format: int, page_size: int, slots,
     return out
 
 
-def translate(idx_row: np.ndarray, index_mode: int, request: int, page_table, page_size: int):
+def translate(idx_row: np.ndarray, index_mode: int, request: int, page_table, page_size: int,
+              num_pages: int):
     """Request-local top-k positions -> (list positions kept, global slots).
 
     LOGICAL mode is the block-table translation that vllm#43477 runs before its kernel
     (triton_convert_req_index_to_global_index over req_id_per_token and block_table):
     slot = block_table[request][t // page_size] * page_size + t % page_size.
-    GLOBAL mode takes t as the slot.  -1 entries are dropped and never dereferenced
-    (sglang#24692 review highlights: invalid ids).
+    GLOBAL mode takes t as the slot.  Invalid ids are dropped and never dereferenced
+    (sglang#24692 review highlights: invalid ids): -1, and with it every entry that names
+    no cache slot - a negative t, a page index past the request's block-table row, a page
+    id outside [0, num_pages), a request outside the table, or (GLOBAL) a slot outside
+    [0, num_pages * page_size).
     """
     idx_row = np.asarray(idx_row, dtype=np.int64)
-    pos = np.nonzero(idx_row != -1)[0]
-    t = idx_row[pos]
+    keep = idx_row >= 0
     if index_mode == IDX_GLOBAL:
-        return pos, t
-    pt = np.asarray(page_table, dtype=np.int64)[request]
-    slots = pt[t // page_size] * page_size + t % page_size
-    return pos, slots
+        keep &= idx_row < num_pages * page_size
+        pos = np.nonzero(keep)[0]
+        return pos, idx_row[pos]
+    pt = np.asarray(page_table, dtype=np.int64)
+    if not 0 <= request < pt.shape[0]:
+        return np.zeros(0, dtype=np.int64), np.zeros(0, dtype=np.int64)
+    row = pt[request]
+    pi = np.where(keep, idx_row // page_size, 0)
+    keep &= pi < row.shape[0]
+    page = np.where(keep, row[np.where(keep, pi, 0)], -1)
+    keep &= (page >= 0) & (page < num_pages)
+    pos = np.nonzero(keep)[0]
+    t = idx_row[pos]
+    return pos, page[pos] * page_size + t % page_size
 
 
 # ---------------------------------------------------------------------------------------
@@ -194,7 +207,9 @@ def attend(q: np.ndarray, k: np.ndarray, scale: float, sink) -> tuple[np.ndarray
 def _row_inputs(r, q_bits, cache, kv_format, page_size, indices, row_req, page_table, index_mode,
                 kv_scale=1.0):
     req = int(row_req[r]) if index_mode == IDX_LOGICAL else -1
-    pos, slots = translate(indices[r], index_mode, req, page_table, page_size)
+    flat_bytes = np.asarray(cache).nbytes
+    pos, slots = translate(indices[r], index_mode, req, page_table, page_size,
+                           flat_bytes // page_bytes(kv_format, page_size))
     k = decode_entries(cache, kv_format, page_size, slots, kv_scale)
     q = bf16_bits_to_f64(q_bits[r])
     return q, pos, k

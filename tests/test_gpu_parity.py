@@ -305,10 +305,8 @@ def test_index_check_records_first_bad_and_masks_it():
     announce("index check")
     out, lse, info, ws = gpu_decode(inp, indices=idx, flags=B.F_CHECK_INDICES, return_info=True)
     assert B.read_index_error(info, ws) == (2, 5)
-    clean = idx.clone()
-    clean[clean < -1] = -1
-    clean[clean >= 10 ** 6] = -1
-    o, l = oracle_decode(inp, indices=clean)
+    # the oracle masks the same entries (raw indices on both sides)
+    o, l = oracle_decode(inp, indices=idx)
     compare(out, lse, o, l, what="masked bad indices")
     out2, lse2, info2, ws2 = gpu_decode(inp, flags=B.F_CHECK_INDICES, return_info=True)
     assert B.read_index_error(info2, ws2) == (-1, -1)

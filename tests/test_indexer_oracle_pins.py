@@ -171,3 +171,72 @@ def test_generator_layout_is_the_oracle_layout():
     assert np.all(scales > 0)
     assert np.allclose(np.abs(codes).max(axis=1), 448.0)
     assert np.all(inp.row_len.numpy() <= inp.width) and inp.width % 64 == 0
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def _passes(check) -> bool:
+    try:
+        check()
+    except AssertionError:
+        return False
+    return True
+
+
+def test_pins_catch_planted_indexer_mistakes(monkeypatch):
+    """Each mutation is a plausible slip in the indexer oracle; a pin above must fail."""
+    good_logits = io.indexer_logits
+    good_decode = io.decode_keys
+
+    def mutated_logits(relu=True, reverse_weights=False):
+        def f(q_codes, weights, cache, page_size, row_req, row_len, page_table, width, rows=None):
+            q_codes = np.asarray(q_codes, dtype=np.uint8)
+            w = np.asarray(weights, dtype=np.float64)
+            if reverse_weights:
+                w = w[:, ::-1]
+            rows_ = range(q_codes.shape[0]) if rows is None else list(rows)
+            out = np.full((len(rows_), width), -np.inf)
+            for i, r in enumerate(rows_):
+                n = int(row_len[r])
+                if n == 0:
+                    continue
+                codes, scale = io.decode_keys(cache, page_size,
+                                              io.row_slots(int(row_req[r]), n, page_table, page_size))
+                dots = scale[None, :] * (io.e4m3fn_to_f64(q_codes[r]) @ codes.T)
+                out[i, :n] = w[r] @ (np.maximum(dots, 0.0) if relu else dots)
+            return out
+        return f
+
+    def no_key_scale(cache, page_size, slots):
+        codes, scales = good_decode(cache, page_size, slots)
+        return codes, np.ones_like(scales)
+
+    def ties_to_larger(logits, row_len, topk):
+        logits = np.asarray(logits, dtype=np.float64)
+        out = np.full((logits.shape[0], topk), -1, dtype=np.int64)
+        for r in range(logits.shape[0]):
+            n = int(row_len[r])
+            pos = np.arange(n)
+            order = np.lexsort((-pos, -logits[r, :n]))
+            take = np.sort(order[:min(topk, n)])
+            out[r, :take.size] = take
+        return out
+
+    checks = {
+        "no_relu": (lambda: monkeypatch.setattr(io, "indexer_logits", mutated_logits(relu=False)),
+                    lambda: test_logits_match_loops_over_torch_decode(1)),
+        "weights_reversed": (lambda: monkeypatch.setattr(io, "indexer_logits",
+                                                         mutated_logits(reverse_weights=True)),
+                             lambda: test_logits_match_loops_over_torch_decode(2)),
+        "no_key_scale": (lambda: monkeypatch.setattr(io, "decode_keys", no_key_scale),
+                         lambda: test_logits_match_loops_over_torch_decode(1)),
+        "ties_to_larger_position": (lambda: monkeypatch.setattr(io, "indexer_topk", ties_to_larger),
+                                    test_topk_ties_go_to_smaller_positions),
+    }
+    assert good_logits is io.indexer_logits
+    for name, (plant, check) in checks.items():
+        plant()
+        assert not _passes(check), f"planted mistake {name} went unnoticed"
+        monkeypatch.undo()
+    for name, (_, check) in checks.items():
+        assert _passes(check), name

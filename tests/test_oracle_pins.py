@@ -359,6 +359,85 @@ def test_page_relocation_and_global_mode():
     assert np.array_equal(o0, o2) and np.array_equal(l0, l2)
 
 
+
+def test_invalid_ids_are_masked_hand_worked():
+    """Every id that names no cache slot is dropped like -1 (hand-worked cases): negative
+    ids, a page index past the request's block-table row, a page id outside the pool, a
+    request outside the table, and (GLOBAL) a slot outside the pool."""
+    pt = np.array([[2, -1, 7], [5, 1, 0]], dtype=np.int32)
+    num_pages = 6                                   # page id 7 is outside the pool
+    row0 = np.array([3, -1, -7, 5, 9, 12, 1, 2])
+    pos, slots = orc.translate(row0, orc.IDX_LOGICAL, 0, pt, 4, num_pages)
+    assert pos.tolist() == [0, 6, 7] and slots.tolist() == [11, 9, 10]
+    pos, slots = orc.translate(np.array([4, 11, 0]), orc.IDX_LOGICAL, 1, pt, 4, num_pages)
+    assert pos.tolist() == [0, 1, 2] and slots.tolist() == [4, 3, 20]
+    for req in (2, -1):
+        pos, slots = orc.translate(row0, orc.IDX_LOGICAL, req, pt, 4, num_pages)
+        assert pos.size == 0 and slots.size == 0
+    pos, slots = orc.translate(np.array([3, -1, -7, 23, 24, 0]), orc.IDX_GLOBAL, -1, pt, 4, num_pages)
+    assert pos.tolist() == [0, 3, 5] and slots.tolist() == [3, 23, 0]
+
+
+def test_invalid_ids_decode_like_minus_one():
+    """A row with planted bad ids decodes to the brute force over its valid ids alone."""
+    inp = _tiny("fp8", 21, heads=2, topk=10, ctx=(20, 30))
+    d = _np(inp)
+    idx = d["indices"].copy()
+    npg = d["cache"].shape[0]
+    idx[0, 1] = -5
+    idx[0, 4] = d["page_table"].shape[1] * 4 + 2         # past the block-table row
+    pt = d["page_table"].copy()
+    b1 = int(d["row_req"][-1])
+    pt[b1, 0] = npg + 3                                  # a page id outside the pool
+    o, lse = _oracle(dict(d, indices=idx, page_table=pt))
+    cache = inp.kv_cache.numpy().tobytes()
+    for r in range(inp.num_rows):
+        b = int(d["row_req"][r])
+        keep = [int(t) for t in idx[r] if t >= 0 and t // 4 < pt.shape[1]
+                and 0 <= pt[b, t // 4] < npg]
+        slot_of = lambda t: int(pt[b, t // 4]) * 4 + t % 4  # noqa: E731
+        qr = [[float(x) for x in inp.q[r, h].double().tolist()] for h in range(2)]
+        bo, bl = brute_force.decode_row(qr, cache, "fp8", 4, keep, slot_of, d["softmax_scale"],
+                                        d["sinks"])
+        np.testing.assert_allclose(o[r], np.array(bo), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse[r], np.array(bl), rtol=1e-12, atol=1e-14)
+
+
+def test_chunk_bounds_by_hand():
+    """Chunk c holds list positions [c*C, (c+1)*C), C = ceil(K/S): the 16 chunks of 128
+    positions of the split-16 workload, and hand-listed ragged cases whose last chunks
+    are short or empty."""
+    assert orc.chunk_bounds(2048, 16) == [(128 * c, 128 * c + 128) for c in range(16)]
+    assert orc.chunk_bounds(24, 16) == [(2 * c, 2 * c + 2) for c in range(12)] + [(24, 24)] * 4
+    assert orc.chunk_bounds(20, 8) == [(0, 3), (3, 6), (6, 9), (9, 12), (12, 15), (15, 18),
+                                       (18, 20), (20, 20)]
+    assert orc.chunk_bounds(5, 1) == [(0, 5)]
+    assert orc.chunk_bounds(7, 7) == [(c, c + 1) for c in range(7)]
+
+
+def test_partials_are_the_chunks_of_list_positions():
+    """Each sink-free partial equals the brute force over exactly its chunk's list
+    positions (-1 entries inside a chunk included), K = 20 in 8 chunks of 3."""
+    inp = _tiny("bf16", 22, heads=2, topk=20, ctx=(40, 60), rows=(1,), nreq=2)
+    d = _np(inp)
+    idx = d["indices"].copy()
+    idx[0, [4, 5, 19]] = -1
+    oc, lc = orc.sparse_mla_decode_partials(d["q_bits"], d["cache"], d["kv_format"], 4, idx,
+                                            d["row_req"], d["page_table"], d["softmax_scale"], 8)
+    cache = inp.kv_cache.numpy().tobytes()
+    pt = d["page_table"]
+    hand = [(0, 3), (3, 6), (6, 9), (9, 12), (12, 15), (15, 18), (18, 20), (20, 20)]
+    for r in range(inp.num_rows):
+        b = int(d["row_req"][r])
+        slot_of = lambda t: int(pt[b, t // 4]) * 4 + t % 4  # noqa: E731
+        qr = [[float(x) for x in inp.q[r, h].double().tolist()] for h in range(2)]
+        for c, (lo, hi) in enumerate(hand):
+            bo, bl = brute_force.decode_row(qr, cache, "bf16", 4, idx[r, lo:hi].tolist(), slot_of,
+                                            d["softmax_scale"], None)
+            np.testing.assert_allclose(oc[r, c], np.array(bo), rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(lc[r, c], np.array(bl), rtol=1e-12, atol=1e-14)
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 16, 24])
 def test_split_merge_reproduces_unsplit(splits):
     inp = _tiny("fp8", 18, heads=3, topk=24, ctx=(30, 60), valid="uniform")
@@ -402,9 +481,11 @@ def test_merge_random_partitions_and_empty_chunks():
 # ---------------------------------------------------------------- planted mistakes
 
 def _run_pin(check):
+    """True when the pin passes; a failed assertion or an error (a slip that indexes out of
+    range) both count as the pin catching the mistake."""
     try:
         check()
-    except AssertionError:
+    except (AssertionError, IndexError, ValueError):
         return False
     return True
 
@@ -441,6 +522,48 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     def e4m3_bias8(codes):
         return good_e4m3(codes) / 2.0
 
+    def dropped_term(q, k, scale, sink):       # the last entry of the set never counts
+        return good_attend(q, k[:-1], scale, sink)
+
+    def wrong_sign(q, k, scale, sink):         # scores with the sign flipped
+        return good_attend(-q, k, scale, sink)
+
+    def value_off_by_64(q, k, scale, sink):    # V read from the wrong 512 dims (64..575)
+        k2 = k.copy()
+        k2[:, :512] = k[:, 64:]
+        o, _ = good_attend(q, k2, scale, sink)
+        return o, good_attend(q, k, scale, sink)[1]
+
+    def lse_base2(q, k, scale, sink):          # LSE in log2 instead of the natural log
+        o, lse = good_attend(q, k, scale, sink)
+        return o, lse / math.log(2.0)
+
+    def only_minus_one(idx_row, index_mode, request, page_table, page_size, num_pages):
+        # masks -1 alone: other negative ids wrap through the table's last entries
+        idx_row = np.asarray(idx_row, dtype=np.int64)
+        pos = np.nonzero(idx_row != -1)[0]
+        t = idx_row[pos]
+        if index_mode == orc.IDX_GLOBAL:
+            return pos, t
+        row = np.asarray(page_table, dtype=np.int64)[request]
+        return pos, row[t // page_size] * page_size + t % page_size
+
+    def remainder_last(topk, num_splits):      # K // S per chunk, the remainder in the last
+        c = topk // num_splits
+        return [(i * c, (i + 1) * c if i < num_splits - 1 else topk) for i in range(num_splits)]
+
+    good_merge = orc.merge_partials
+
+    def sink_per_chunk(o_c, lse_c, sinks):     # the sink folded into every chunk's weight
+        o_c = np.asarray(o_c, dtype=np.float64)
+        lse_c = np.asarray(lse_c, dtype=np.float64)
+        if sinks is None:
+            return good_merge(o_c, lse_c, sinks)
+        sig = np.broadcast_to(np.asarray(sinks, dtype=np.float64), lse_c.shape)
+        with np.errstate(invalid="ignore"):
+            lse2 = np.logaddexp(lse_c, sig)
+        return good_merge(o_c * np.exp(lse_c - lse2)[..., None], lse2, None)
+
     checks = {
         "no_rope": (lambda: monkeypatch.setattr(orc, "attend", no_rope),
                     lambda: test_one_hot_query_scores_one_dim(575)),
@@ -453,6 +576,23 @@ def test_pins_catch_planted_mistakes(monkeypatch):
                               lambda: test_oracle_matches_brute_force("fp8t", 1)),
         "e4m3_bias": (lambda: monkeypatch.setattr(orc, "e4m3fn_to_f64", e4m3_bias8),
                       test_e4m3fn_all_codes_match_torch),
+        "dropped_term": (lambda: monkeypatch.setattr(orc, "attend", dropped_term),
+                         lambda: test_oracle_matches_brute_force("bf16", 2)),
+        "wrong_sign": (lambda: monkeypatch.setattr(orc, "attend", wrong_sign),
+                       lambda: test_oracle_matches_brute_force("fp8", 2)),
+        "value_off_by_64": (lambda: monkeypatch.setattr(orc, "attend", value_off_by_64),
+                            test_single_entry_is_exact),
+        "lse_base2": (lambda: monkeypatch.setattr(orc, "attend", lse_base2),
+                      test_single_entry_is_exact),
+        "only_minus_one_masked": (lambda: monkeypatch.setattr(orc, "translate", only_minus_one),
+                                  test_invalid_ids_are_masked_hand_worked),
+        "chunks_remainder_last": (lambda: monkeypatch.setattr(orc, "chunk_bounds", remainder_last),
+                                  test_chunk_bounds_by_hand),
+        "chunks_remainder_last_partials": (
+            lambda: monkeypatch.setattr(orc, "chunk_bounds", remainder_last),
+            test_partials_are_the_chunks_of_list_positions),
+        "sink_per_chunk": (lambda: monkeypatch.setattr(orc, "merge_partials", sink_per_chunk),
+                           lambda: test_split_merge_reproduces_unsplit(3)),
     }
     for name, (plant, check) in checks.items():
         plant()
