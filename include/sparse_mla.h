@@ -149,9 +149,17 @@ typedef struct {
 } smla_plan;
 
 /* Choose the split count and launch shape for a problem and report the workspace size.
+ * This is the decode's scheduler metadata: built on the host from shapes alone, so one plan
+ * serves every step and every graph replay of a batch shape, with the work split derived
+ * inside the library from the literal compute-unit total (prhub vllm#52164 "[Attention][DSA]
+ * Take the native decode path for MTP=3 on SM90", implementation breakdown step 4 and design
+ * highlight 3: graph-stable, preallocated scheduler metadata whose slot count the wrapper
+ * derives from the plain SM count itself).  The split-KV decode it plans and the merge that
+ * follows are the split path of prhub sglang#24692, implementation breakdown items 2-3.
  *   p               problem description (host memory, read only)
- *   num_cus         compute units to plan for; <= 0 queries the current HIP device
- *                   (the only HIP call this function makes)
+ *   num_cus         compute units of the device the run will use (the total, as the device
+ *                   reports it); <= 0 queries the current HIP device (the only HIP call this
+ *                   function makes).  Passing the count keeps the plan a pure host function.
  *   plan            output (host memory)
  *   workspace_bytes output: device bytes that sparse_mla_decode_run needs (0 when none)
  * Depends only on shapes and num_cus, never on data; no device memory is touched.
@@ -162,7 +170,13 @@ smla_status sparse_mla_decode_plan(const smla_problem* p, int32_t num_cus, smla_
 /* Number of splits S chosen by a plan (>= 1), or -1 for an invalid plan. */
 int32_t sparse_mla_plan_num_splits(const smla_plan* plan);
 
-/* Run the decode on `stream`.  All pointers are device pointers.
+/* Run the decode on `stream`: the sparse-MLA attention call of the serving engine's
+ * forward_mqa, which consumes each token's top-k index list and writes the output of shape
+ * [tokens, heads, kv_lora_rank] in q's dtype (prhub vllm#43477 "DSv4 and GLM-5.1 on Blackwell
+ * SM120", key code excerpts: FlashInferMLASparseSM120Impl.forward_mqa), computing the
+ * gather + dequant, tiled online softmax, sink and split merge of prhub sglang#24692
+ * implementation breakdown items 2-3 as defined at the top of this header.  All pointers
+ * are device pointers.
  *   q           bf16 [R][H][576]; 16-byte aligned
  *   kv_cache    num_pages pages in the layout above; 16-byte aligned
  *   indices     int32 [R][K]; -1 = empty; 16-byte aligned (K is a multiple of 4)
@@ -270,8 +284,11 @@ smla_status sparse_mla_translate_indices(const int32_t* indices, const int32_t* 
                                         int32_t num_pages, int32_t* slots, void* stream);
 
 /* Test helper: decode n cache slots (global slot numbers, device int32 [n]) into bf16
- * rows out[n][576] with the same device code the decode kernel uses for its gather and
- * dequantisation.  Slots outside [0, num_pages*page_size) give a zero row.  For
+ * rows out[n][576] with a plain per-element reference decoder on the GPU (one thread per
+ * 8 dims, direct loads).  It is NOT the decode kernel's gather: that one copies entries into
+ * LDS with its own addressing and dequantizes them there, and is checked bit for bit
+ * through sparse_mla_decode_run itself.  Slots outside [0, num_pages*page_size) give a zero
+ * row.  The cache layout is the one at the top of this header.  For
  * SMLA_KV_FP8_TENSOR the row holds the code values e4m3fn(code[d]): the decode applies
  * kv_scale as two scalar factors, not per element.
  * Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED, MISALIGNED, HIP. */

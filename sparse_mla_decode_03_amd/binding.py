@@ -268,7 +268,8 @@ def merge_partials(partial_o: torch.Tensor, partial_lse: torch.Tensor,
 
 def gather_debug(kv_cache: torch.Tensor, kv_format, page_size: int, slots: torch.Tensor,
                  stream=None) -> torch.Tensor:
-    """Dequantize cache slots to bf16 [n, 576] with the decode kernel's gather code."""
+    """Dequantize cache slots to bf16 [n, 576] with the library's plain reference decoder
+    (a test helper; not the decode kernel's LDS gather)."""
     lib = load_library()
     dev = kv_cache.device
     _require(kv_cache, "kv_cache", torch.uint8, dev)

@@ -40,11 +40,16 @@ constexpr int kSlotLen = kCMax + 4 * kT;
 constexpr int kDepth = 4;               // LDS operand loads kept in flight (QK)
 constexpr int kDepthV = 3;              // LDS operand load pairs kept in flight (PV)
 // Exponentials are taken against a per-head reference max fixed at the first tile, so P
-// may exceed 1.  When a later tile's max exceeds the reference by more than 2^32 the
-// workgroup repeats the pass over the row with the larger reference; fp32 and bf16 hold
-// P <= 2^32 without overflow.
-constexpr float kRestartLog2 = 32.0f;
-constexpr unsigned kRestartBits = 0x4F800000u;   // bit pattern of 2^kRestartLog2
+// may exceed 1.  fp32 and bf16 hold P <= 2^64 without overflow (and the sum over 2048
+// entries of P times a value below 2^50 stays inside fp32), so the reference stays put
+// while no score exceeds it by more than 64 log2 units.  Beyond that the reference is
+// raised to the tile's max and the workgroup repeats the pass over the row: where the
+// tile's max is known before its exponentials (the first tile, a partial tile, a repeated
+// pass) it is that max; in the steady state (exponentials first) it is read off the
+// exponent of the head's largest probability, or is the reference plus 128 when that
+// probability is +inf (a score past exp2's fp32 range against the reference).
+constexpr float kRestartLog2 = 64.0f;
+constexpr unsigned kRestartBits = 0x5F800000u;   // bit pattern of 2^kRestartLog2
 constexpr unsigned kInfBits = 0x7F800000u;       // bit pattern of +inf
 
 // K tile layout.  LDS serves 64 banks of 4 bytes: 16 lanes per cycle for 16-byte reads
@@ -67,6 +72,10 @@ __device__ __forceinline__ int lat_row_byte(int row) { return row * kRowB + 16 *
 __device__ __forceinline__ float max_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ unsigned umax_halves(unsigned x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max(r[0], r[1]);
 }
 __device__ __forceinline__ float sum_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -540,6 +549,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // array slot of an AGPR block (block 15 never reaches it when it lives in VGPRs)
   auto ob_index = [&](int b) { return kO15V ? b % 15 : b; };
   float l_part;
+  // O and the row sum times alpha (per head: this lane's column), for a raised reference
   const int ntiles = (n_valid + kT - 1) / kT;
   // The pass over the tiles is repeated only if some head's reference max had to be
   // raised (kRestartLog2); O is dead across the repeat.
@@ -706,7 +716,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     // and me the reference, and nothing precedes the exps: k-step 0's probabilities come
     // first and the rest of the softmax (k-step 1's probabilities, the row sum, the
     // overflow check) runs inside k-step 0's MFMAs.  A probability above 2^kRestartLog2
-    // means a score beyond the reference: the pass is repeated on the careful path.
+    // means a score far beyond the reference: the pass is repeated (see kRestartLog2).
     // Otherwise (the first tile, a partial tile, a repeated pass) the tile's max is taken
     // first and may raise the reference; x is then the scaled, masked score minus the
     // reference, with ce = 1 and me = 0.
@@ -731,7 +741,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       }
       mx = max_halves(mx);
       if (m_used == -INFINITY) m_used = mx;       // first tile: O and l are still zero
-      if (mx > m_used + kRestartLog2) {           // rare: raise the reference and restart
+      if (mx > m_used + kRestartLog2) {           // rare: raise the reference and repeat
         m_used = mx;
         sRestart = 1;
       }
@@ -773,9 +783,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       pv_step(step, p1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // +inf counts (a score past the fp32 range of exp2 against this reference); NaN,
-    // whose patterns lie above +inf's, does not: a NaN score must not repeat the pass.
-    if (steady && pbits > kRestartBits && pbits <= kInfBits) sRestart = 1;
+    // A head's largest probability above 2^kRestartLog2 repeats the pass, with the
+    // reference raised by the probability's exponent (by 128 for +inf).  NaN, whose
+    // patterns lie above +inf's, does not: a NaN score must not repeat the pass.
+    if (steady) {
+      const unsigned hb = umax_halves(pbits);
+      if (hb > kRestartBits && hb <= kInfBits) {
+        m_used += hb < kInfBits ? (float)((int)(hb >> 23) - 127) : 128.f;
+        sRestart = 1;
+      }
+    }
     have_ref = true;
 
     // ---- next tile: finish its gather -------------------------------------------------

@@ -514,3 +514,52 @@ def test_per_tensor_fp8_full_size_sampled():
     sub_cache, sub_pt = page_subset(inp, rows)
     o, l = oracle_decode(inp, rows=rows, kv_cache=sub_cache, page_table=sub_pt)
     compare(out[rows], lse[rows], o, l, what=f"fp8t full rows={len(rows)}")
+
+
+def _plant_spikes(inp, fmt, j, spikes, seed=5):
+    """Write cache entries of row 0 whose scores for head j lie `excess` log2 units above
+    the largest score of the row's first tile: spikes = [(list position, excess)].  The
+    entry's rope is a multiple of head j's rope query (a bf16 rounding of the solved
+    multiple); the latent part is redrawn.  Returns the realised excesses, measured with
+    the oracle's decoder."""
+    from oracle import cache_store_oracle as cso
+    ps = inp.spec.page_size
+    c = inp.spec.softmax_scale / np.log(2.0)                 # log2 units per score unit
+    qd = inp.q[0, j].double().numpy()
+    qr = inp.q[0, j].float()[512:]
+    bits = lambda x: x.contiguous().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+    cache = inp.kv_cache.cpu().numpy()
+    slot_of = lambda p: int(inp.page_table[int(inp.row_req[0]), int(inp.indices[0, p]) // ps]) * ps \
+        + int(inp.indices[0, p]) % ps  # noqa: E731
+    first = orc.decode_entries(cache, KV[fmt], ps, np.array([slot_of(p) for p in range(32)]))
+    ref = float((first @ qd).max()) * c
+    realised = []
+    for n, (pos, excess) in enumerate(spikes):
+        lat = torch.randn((1, 512), generator=torch.Generator().manual_seed(seed + n)).to(torch.bfloat16)
+        lat_dot = float(lat.double()[0] @ torch.from_numpy(qd[:512]))
+        alpha = ((ref + excess) / c - lat_dot) / float(qr.double() @ qr.double())
+        rope = (alpha * qr).to(torch.bfloat16)
+        cache = cso.cache_store(cache, KV[fmt], ps, bits(lat), bits(rope[None]), np.array([slot_of(pos)]))
+        x = float(orc.decode_entries(cache, KV[fmt], ps, np.array([slot_of(pos)]))[0] @ qd) * c
+        realised.append(x - ref)
+    inp.kv_cache = torch.from_numpy(cache)
+    return realised
+
+
+# Excesses (log2 units over the first tile's largest score) of a spike in tile 3 and one in
+# tile 7: both within 2^64 (no repeated pass); the second beyond (one repeat, the reference
+# raised to it); the first past exp2's range (+inf: the reference raised by 128, then its
+# remaining excess raised again on the careful pass); the first beyond and the second within
+# 64 of it (one repeat)
+@pytest.mark.parametrize("fmt,heads", [("fp8", 32), ("fp8", 128), ("bf16", 128)])
+@pytest.mark.parametrize("e1,e2", [(40.0, 60.0), (50.0, 100.0), (200.0, 100.0), (100.0, 150.0)])
+def test_two_spikes_in_different_tiles(fmt, heads, e1, e2):
+    inp = _small(fmt=fmt, heads=heads, topk=320, nreq=2, rows=(1, 1), ctx=(900, 1100), seed=95)
+    j = 7
+    realised = _plant_spikes(inp, fmt, j, [(3 * 32 + 5, e1), (7 * 32 + 11, e2)])
+    for want, got in zip((e1, e2), realised):
+        assert abs(got - want) < 2.0, (want, got)
+    announce(f"two spikes {fmt} H={heads} excess={realised[0]:.1f},{realised[1]:.1f}")
+    out, lse = gpu_decode(inp)
+    o, l = oracle_decode(inp)
+    compare(out, lse, o, l, what=f"two spikes {fmt} {e1}/{e2}")
