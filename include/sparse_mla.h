@@ -96,6 +96,8 @@ extern "C" {
 #define SMLA_BF16_ENTRY_BYTES 1152
 #define SMLA_MAX_HEADS 128
 #define SMLA_MAX_SPLITS 256
+/* Device scratch held by the library for sparse_mla_decode_run_noalloc, per GPU (16 MiB) */
+#define SMLA_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 typedef enum {
   SMLA_OK = 0,
@@ -198,6 +200,27 @@ smla_status sparse_mla_decode_run(const smla_plan* plan, const void* q, const vo
                                   const int32_t* page_table, const float* sinks, void* out,
                                   float* lse, float* partial_o, float* partial_lse,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same decode as sparse_mla_decode_run, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): it
+ * takes no workspace.  A split plan's fp32 partials go to scratch the library holds, one
+ * SMLA_NOALLOC_SCRATCH_BYTES array per GPU in the library's own device memory, reserved
+ * when the library is loaded and kept until the process ends; no call allocates or frees
+ * anything.  Arguments as for sparse_mla_decode_run, without partial_o, partial_lse and
+ * the workspace.
+ *   - Plans whose workspace exceeds SMLA_NOALLOC_SCRATCH_BYTES return
+ *     SMLA_ERR_WORKSPACE_TOO_SMALL before anything else happens (raise the split count's
+ *     ceiling differently: force fewer splits, or call sparse_mla_decode_run).
+ *   - Plans with SMLA_F_PARTIALS_ONLY or SMLA_F_CHECK_INDICES return SMLA_ERR_UNSUPPORTED.
+ *   - Every call on one GPU uses that GPU's one scratch array: calls that may overlap on a
+ *     GPU (other streams, other host threads) race on it and give wrong results; calls in
+ *     one stream are ordered and safe.  The scratch keeps the last call's contents; nothing
+ *     in it needs to start at zero.
+ * Errors: BAD_PLAN, UNSUPPORTED, WORKSPACE_TOO_SMALL, NULL_ARG, MISALIGNED, HIP. */
+smla_status sparse_mla_decode_run_noalloc(const smla_plan* plan, const void* q, const void* kv_cache,
+                                          const int32_t* indices, const int32_t* row_req,
+                                          const int32_t* page_table, const float* sinks, void* out,
+                                          float* lse, void* stream);
 
 /* LSE-merge S sink-free partials and apply the sink once (the merge and sink steps that
  * follow the split decode on prhub sglang#24692, key files: flash_mla_sm120_triton.py).

@@ -45,7 +45,9 @@ EXPORTED = [
     "sparse_mla_indexer_logits",
     "sparse_mla_indexer_topk",
     "sparse_mla_translate_indices",
+    "sparse_mla_decode_run_noalloc",
 ]
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class Problem(ctypes.Structure):
@@ -89,6 +91,9 @@ def load_library(path: str = LIB_PATH):
     lib.sparse_mla_decode_run.argtypes = [ctypes.POINTER(Plan), vp, vp, i32p, i32p, i32p, f32p, vp,
                                           f32p, f32p, f32p, vp, ctypes.c_size_t, vp]
     lib.sparse_mla_decode_run.restype = ctypes.c_int
+    lib.sparse_mla_decode_run_noalloc.argtypes = [ctypes.POINTER(Plan), vp, vp, i32p, i32p, i32p, f32p,
+                                                  vp, f32p, vp]
+    lib.sparse_mla_decode_run_noalloc.restype = ctypes.c_int
     lib.sparse_mla_merge_partials.argtypes = [f32p, f32p, i32, i32, i32, f32p, vp, f32p, vp]
     lib.sparse_mla_merge_partials.restype = ctypes.c_int
     lib.sparse_mla_gather_debug.argtypes = [vp, i32, i32, i32, i32p, i32, vp, vp]
@@ -167,6 +172,17 @@ def run(info: PlanInfo, q, kv_cache, indices, row_req, page_table, sinks, out, l
                                      _ptr(row_req), _ptr(page_table), _ptr(sinks), _ptr(out),
                                      _ptr(lse), _ptr(partial_o), _ptr(partial_lse), _ptr(workspace),
                                      ctypes.c_size_t(ws_bytes), _stream(stream)))
+
+
+def run_noalloc(info: PlanInfo, q, kv_cache, indices, row_req, page_table, sinks, out, lse=None,
+                stream=None) -> None:
+    """Raw run through the allocation-free entry point (no workspace; split partials in the
+    library's own per-GPU scratch)."""
+    lib = load_library()
+    _check("sparse_mla_decode_run_noalloc",
+           lib.sparse_mla_decode_run_noalloc(ctypes.byref(info.plan), _ptr(q), _ptr(kv_cache),
+                                             _ptr(indices), _ptr(row_req), _ptr(page_table),
+                                             _ptr(sinks), _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def _kv_format_of(kv_format) -> int:

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "sparse_mla.h"
 #include "smla_kernels.h"
@@ -27,6 +28,29 @@ struct PlanImpl {
 static_assert(sizeof(PlanImpl) <= sizeof(smla_plan), "plan does not fit its opaque storage");
 
 std::atomic<int> g_cu_count[kMaxDevices];
+
+// Scratch of the allocation-free run entry point: the fp32 split partials (and their LSEs)
+// that sparse_mla_decode_run keeps in the caller's workspace.  One copy per GPU, for the
+// life of the process.  Host code never uses the array's name as an address: the device
+// address comes from hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = (size_t)SMLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+void* g_scratch_ptr[kMaxDevices];
+bool g_scratch_ready[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// This device's scratch address, or nullptr if the runtime could not resolve it.
+void* scratch_on(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ready[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+    g_scratch_ready[dev] = true;
+  }
+  return g_scratch_ptr[dev];
+}
 
 int cu_count(int* out) {
   int dev = 0;
@@ -153,28 +177,44 @@ int32_t sparse_mla_plan_num_splits(const smla_plan* plan) {
   return pi ? pi->num_splits : -1;
 }
 
-smla_status sparse_mla_decode_run(const smla_plan* plan, const void* q, const void* kv_cache,
-                                  const int32_t* indices, const int32_t* row_req,
-                                  const int32_t* page_table, const float* sinks, void* out,
-                                  float* lse, float* partial_o, float* partial_lse,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
-  const PlanImpl* pi = as_impl(plan);
-  if (pi == nullptr) return SMLA_ERR_BAD_PLAN;
+}  // extern "C"
+
+namespace {
+
+// Pointer checks of a run (host only; rows > 0).
+smla_status check_run_args(const PlanImpl* pi, const void* q, const void* kv_cache,
+                           const int32_t* indices, const int32_t* row_req, const int32_t* page_table,
+                           const float* sinks, const void* out, const float* lse,
+                           const float* partial_o, const float* partial_lse) {
   const smla_problem& p = pi->p;
   const bool partials_only = (p.flags & SMLA_F_PARTIALS_ONLY) != 0;
   const bool logical = p.index_mode == SMLA_IDX_LOGICAL;
-  if (p.num_rows == 0) return SMLA_OK;  // nothing to do; empty tensors may pass NULL
   if (q == nullptr || kv_cache == nullptr || indices == nullptr) return SMLA_ERR_NULL_ARG;
   if (logical && (row_req == nullptr || page_table == nullptr)) return SMLA_ERR_NULL_ARG;
   if (partials_only ? (partial_o == nullptr || partial_lse == nullptr) : out == nullptr)
     return SMLA_ERR_NULL_ARG;
-  if (pi->ws_bytes > 0 && workspace == nullptr) return SMLA_ERR_NULL_ARG;
-  if (workspace_bytes < pi->ws_bytes) return SMLA_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(indices, 16) || !aligned(out, 16) ||
       !aligned(partial_o, 16) || !aligned(partial_lse, 4) || !aligned(lse, 4) ||
-      !aligned(sinks, 4) || !aligned(row_req, 4) || !aligned(page_table, 4) ||
-      !aligned(workspace, 256))
+      !aligned(sinks, 4) || !aligned(row_req, 4) || !aligned(page_table, 4))
     return SMLA_ERR_MISALIGNED;
+  return SMLA_OK;
+}
+
+// The body of sparse_mla_decode_run, shared with the allocation-free entry point.
+smla_status run_impl(const PlanImpl* pi, const void* q, const void* kv_cache, const int32_t* indices,
+                     const int32_t* row_req, const int32_t* page_table, const float* sinks, void* out,
+                     float* lse, float* partial_o, float* partial_lse, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  const smla_problem& p = pi->p;
+  const bool partials_only = (p.flags & SMLA_F_PARTIALS_ONLY) != 0;
+  const bool logical = p.index_mode == SMLA_IDX_LOGICAL;
+  if (p.num_rows == 0) return SMLA_OK;  // nothing to do; empty tensors may pass NULL
+  const smla_status ca = check_run_args(pi, q, kv_cache, indices, row_req, page_table, sinks, out, lse,
+                                        partial_o, partial_lse);
+  if (ca != SMLA_OK) return ca;
+  if (pi->ws_bytes > 0 && workspace == nullptr) return SMLA_ERR_NULL_ARG;
+  if (workspace_bytes < pi->ws_bytes) return SMLA_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned(workspace, 256)) return SMLA_ERR_MISALIGNED;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
@@ -225,6 +265,44 @@ smla_status sparse_mla_decode_run(const smla_plan* plan, const void* q, const vo
       return SMLA_ERR_HIP;
   }
   return SMLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+smla_status sparse_mla_decode_run(const smla_plan* plan, const void* q, const void* kv_cache,
+                                  const int32_t* indices, const int32_t* row_req,
+                                  const int32_t* page_table, const float* sinks, void* out,
+                                  float* lse, float* partial_o, float* partial_lse,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  const PlanImpl* pi = as_impl(plan);
+  if (pi == nullptr) return SMLA_ERR_BAD_PLAN;
+  return run_impl(pi, q, kv_cache, indices, row_req, page_table, sinks, out, lse, partial_o,
+                  partial_lse, workspace, workspace_bytes, stream);
+}
+
+smla_status sparse_mla_decode_run_noalloc(const smla_plan* plan, const void* q, const void* kv_cache,
+                                          const int32_t* indices, const int32_t* row_req,
+                                          const int32_t* page_table, const float* sinks, void* out,
+                                          float* lse, void* stream) {
+  const PlanImpl* pi = as_impl(plan);
+  if (pi == nullptr) return SMLA_ERR_BAD_PLAN;
+  if (pi->p.flags & (SMLA_F_PARTIALS_ONLY | SMLA_F_CHECK_INDICES)) return SMLA_ERR_UNSUPPORTED;
+  if (pi->ws_bytes > kScratchBytes) return SMLA_ERR_WORKSPACE_TOO_SMALL;
+  if (pi->p.num_rows == 0) return SMLA_OK;
+  const smla_status ca = check_run_args(pi, q, kv_cache, indices, row_req, page_table, sinks, out, lse,
+                                        nullptr, nullptr);
+  if (ca != SMLA_OK) return ca;   // every argument check comes before the first HIP call
+  void* ws = nullptr;
+  if (pi->ws_bytes > 0) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return SMLA_ERR_HIP;
+    ws = scratch_on(dev);
+    if (ws == nullptr) return SMLA_ERR_HIP;
+  }
+  return run_impl(pi, q, kv_cache, indices, row_req, page_table, sinks, out, lse, nullptr, nullptr,
+                  ws, pi->ws_bytes > 0 ? kScratchBytes : 0, stream);
 }
 
 smla_status sparse_mla_merge_partials(const float* partial_o, const float* partial_lse,

@@ -255,3 +255,33 @@ def test_translate_validation(lib):
     assert tr(None, v(FAKE), v(FAKE), 4, 16, 2, 8, 64, 100, v(FAKE), None) == B.ERR_NULL_ARG
     assert tr(v(FAKE), v(FAKE), v(FAKE), 4, 16, 2, 8, 64, 100, v(FAKE + 2), None) == B.ERR_MISALIGNED
     assert tr(None, None, None, 0, 16, 2, 8, 64, 100, None, None) == B.OK
+
+
+def _run_noalloc(lib, plan, q=FAKE, kv=FAKE, idx=FAKE, rr=FAKE, pt=FAKE, sinks=None, out=FAKE, lse=None):
+    v = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    return lib.sparse_mla_decode_run_noalloc(ctypes.byref(plan), v(q), v(kv), v(idx), v(rr), v(pt),
+                                             v(sinks), v(out), v(lse), None)
+
+
+def test_noalloc_run_validation_before_launch(lib):
+    """The allocation-free entry point: plans beyond its scratch, flags it cannot serve and
+    bad pointers are all refused before any device call."""
+    assert _run_noalloc(lib, B.Plan()) == B.ERR_BAD_PLAN
+    # 64 rows x 16 splits x 128 heads of fp32 partials: 268 MB, beyond the 16 MiB scratch
+    st, big, ws = _plan_status(lib, _prob(num_rows=64, num_heads=128, num_splits=16))
+    assert st == B.OK and ws > B.NOALLOC_SCRATCH_BYTES
+    assert _run_noalloc(lib, big) == B.ERR_WORKSPACE_TOO_SMALL
+    for flag in (B.F_PARTIALS_ONLY, B.F_CHECK_INDICES):
+        st, p, _ = _plan_status(lib, _prob(num_rows=2, num_splits=4, flags=flag))
+        assert st == B.OK and _run_noalloc(lib, p) == B.ERR_UNSUPPORTED
+    # a split plan that fits: argument errors come back before the scratch is looked up
+    st, p, ws = _plan_status(lib, _prob(num_rows=2, num_splits=4))
+    assert st == B.OK and 0 < ws <= B.NOALLOC_SCRATCH_BYTES
+    assert _run_noalloc(lib, p, q=None) == B.ERR_NULL_ARG
+    assert _run_noalloc(lib, p, rr=None) == B.ERR_NULL_ARG
+    assert _run_noalloc(lib, p, out=None) == B.ERR_NULL_ARG
+    assert _run_noalloc(lib, p, q=FAKE + 8) == B.ERR_MISALIGNED
+    assert _run_noalloc(lib, p, lse=FAKE + 2) == B.ERR_MISALIGNED
+    # zero rows: nothing to do
+    st, z, _ = _plan_status(lib, _prob(num_rows=0))
+    assert st == B.OK and _run_noalloc(lib, z, q=None, kv=None, idx=None, out=None) == B.OK
