@@ -326,8 +326,9 @@ smla_status sparse_mla_gather_debug(const void* kv_cache, int32_t kv_format, int
 smla_status sparse_mla_read_index_error(const smla_plan* plan, const void* workspace,
                                         int32_t* row_pos, void* stream);
 
-/* Static text for a status code (never NULL). */
-const char* sparse_mla_status_string(smla_status s);
+/* Static text for a status code (never NULL).  Takes any int32: a value that is not an
+ * smla_status gives "unknown status". */
+const char* sparse_mla_status_string(int32_t status);
 
 /* Library version as major*10000 + minor*100 + patch. */
 int32_t sparse_mla_version(void);

@@ -109,7 +109,7 @@ def load_library(path: str = LIB_PATH):
     lib.sparse_mla_cache_store.restype = ctypes.c_int
     lib.sparse_mla_read_index_error.argtypes = [ctypes.POINTER(Plan), vp, ctypes.POINTER(i32 * 2), vp]
     lib.sparse_mla_read_index_error.restype = ctypes.c_int
-    lib.sparse_mla_status_string.argtypes = [ctypes.c_int]
+    lib.sparse_mla_status_string.argtypes = [ctypes.c_int32]
     lib.sparse_mla_status_string.restype = ctypes.c_char_p
     lib.sparse_mla_version.argtypes = []
     lib.sparse_mla_version.restype = i32

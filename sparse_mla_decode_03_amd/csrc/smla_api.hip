@@ -452,8 +452,9 @@ smla_status sparse_mla_read_index_error(const smla_plan* plan, const void* works
   return SMLA_OK;
 }
 
-const char* sparse_mla_status_string(smla_status s) {
-  switch (s) {
+// The code arrives as a plain int: an out-of-range value must not be loaded as the enum.
+const char* sparse_mla_status_string(int32_t status) {
+  switch (status) {
     case SMLA_OK: return "ok";
     case SMLA_ERR_NULL_ARG: return "a required pointer is NULL";
     case SMLA_ERR_BAD_SHAPE: return "invalid or inconsistent size";

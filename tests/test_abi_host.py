@@ -16,11 +16,16 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sparse_mla.h")
 
 
+# The sanitizer test (test_host_sanitized.py) runs this module again in a child process
+# against the CPU-only, ASan/UBSan-instrumented build of the same host code.
+LIB = os.environ.get("SMLA_HOST_CHECK_LIB", B.LIB_PATH)
+
+
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(B.LIB_PATH):
+    if not os.path.exists(LIB):
         pytest.skip("library not built (python -m sparse_mla_decode_03_amd.build)")
-    return B.load_library()
+    return B.load_library(LIB)
 
 
 def _declared_functions():
