@@ -542,7 +542,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // O blocks are accumulated by compiler-scheduled MFMAs in AGPRs.  With three or four
   // waves, block 15 instead lives in VGPRs (a VGPR-form MFMA): that leaves 16 AGPRs for the
   // QK scores, so no O block has to be moved out of the accumulation registers and back each
-  // tile.  (Smaller workgroups keep more copy registers live and stay all-AGPR.)
+  // tile.  (Smaller workgroups keep more copy registers live and stay all-AGPR.)  The
+  // compiler does not see that MFMA's latency: until mfma_vgpr_drain() after the tile loop
+  // no other instruction may name O15's registers.  The library build checks this on the
+  // compiled assembly, over every control-flow path, and refuses a build that breaks it.
   constexpr bool kO15V = NW >= 3;
   f32x16 O[kO15V ? 15 : 16];
   f32x16 O15;
