@@ -390,6 +390,12 @@ smla_status sparse_mla_indexer_logits(const void* q_codes, const float* weights,
   a.max_pages = max_pages;
   a.num_pages = num_pages;
   a.width = width;
+  a.num_requests = num_requests;
+  // the schedule's slots: three workgroups per CU (what fits beside each other), so every
+  // CU streams an equal share of the key pages
+  int cus = 0;
+  if (cu_count(&cus) != 0) return SMLA_ERR_HIP;
+  a.slots = 3 * cus;
   if (smla::launch_indexer_logits(a, next_n, num_requests, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return SMLA_ERR_HIP;
   return SMLA_OK;

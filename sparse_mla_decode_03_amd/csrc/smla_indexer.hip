@@ -9,15 +9,16 @@
 // 128-dimensional e4m3fn queries and keys; top-k keeps the K largest logits, a tie at the
 // boundary going to the smaller position.
 //
-// Logits: one workgroup per (request, chunk of 16 key pages), four waves, three workgroups
-// per compute unit.  The chunk's pages stream through a four-page LDS ring by
-// global_load_lds; wave w serves row w % next_n of the request on its share of each
-// page's two 32-token blocks, so a page is read from HBM once for all rows.  Scores come from the FP8 MFMA 32x32x64 (rows = 32
-// heads, columns = 32 tokens); each lane then holds one token and 16 heads of a block, so
-// the weighted ReLU sum over heads is 32 FMAs and one swap between lane halves.  The key
-// scale multiplies the head sum (the ReLU is positively homogeneous; scales are >= 0).
-// Logits are staged in LDS and stored after the chunk, so the loop's vmcnt waits count
-// only the page copies.
+// Logits: a fixed grid of three workgroups per compute unit, each taking an equal run of
+// the key pages of all requests (request order), segment by segment; a segment's pages
+// stream through a four-page LDS ring by global_load_lds.  Wave w serves row w % next_n of
+// the request on its share of each page's two 32-token blocks, so a page is read from HBM
+// once for all rows.  Scores come from the FP8 MFMA 32x32x64 (rows = 32 heads, columns =
+// 32 tokens); each lane then holds one token and 16 heads of a block, so the weighted ReLU
+// sum over heads is 32 FMAs and one swap between lane halves.  The key scale multiplies
+// the head sum (the ReLU is positively homogeneous; scales are >= 0).  Logits are stored
+// from the loop through a buffer descriptor of the row's length, so stores past it are
+// dropped and every page issues the same stores, which the loop's vmcnt waits count.
 //
 // Top-k: one workgroup per row.  Logits map to order-preserving 32-bit keys; three
 // histogram passes (11 + 11 + 10 bits) over the row find the K-th largest key T and how
@@ -37,7 +38,7 @@ constexpr int kIdxHeads = 64;
 constexpr int kKeyPage = 64;                       // tokens per key page
 constexpr int kKeyPageCodes = kIdxDim * kKeyPage;  // 8192 bytes of codes, then 64 fp32 scales
 constexpr int kKeyPageBytes = kKeyPageCodes + 4 * kKeyPage;
-constexpr int kChunkPages = 16;
+constexpr int kSegPages = 256;                   // page ids staged per segment
 constexpr int kRing = 4;
 constexpr int kSlotBytes = kKeyPageBytes;          // one LDS ring slot
 
@@ -51,60 +52,149 @@ __device__ __forceinline__ float halves_sum(float x) {
 // different chunk slots; the scales follow at byte 8192.
 __device__ __forceinline__ int key_swz(int t) { return (t >> 1) & 7; }
 
-// Wait until this wave's copies of all but the `later` most recent pages (PER copies
-// each) have landed.
-template <int PER>
-__device__ __forceinline__ void wait_later(int later) {
-  static_assert(kRing <= 5, "wait_later covers up to four later pages");
-  switch (later) {
-    case 0: wait_vm(); break;
-    case 1: wait_vm_le<PER>(); break;
-    case 2: wait_vm_le<2 * PER>(); break;
-    case 3: wait_vm_le<3 * PER>(); break;
-    default: wait_vm_le<4 * PER>(); break;
+// Wait until this wave's copy of the current page has landed.  After it, in issue order,
+// the wave has issued the copies of `lc` later pages (PER instructions each) and the logit
+// stores of `ls` earlier pages (ST instructions each); all of those may stay in flight.
+template <int PER, int ST>
+__device__ __forceinline__ void wait_page_sched(int lc, int ls) {
+  static_assert(kRing == 4, "the table covers up to three later pages");
+#define SMLA_W(L, S) case 4 * L + S: wait_vm_le<L * PER + S * ST>(); break;
+  switch (4 * lc + ls) {
+    SMLA_W(0, 0) SMLA_W(0, 1) SMLA_W(0, 2) SMLA_W(0, 3)
+    SMLA_W(1, 0) SMLA_W(1, 1) SMLA_W(1, 2) SMLA_W(1, 3)
+    SMLA_W(2, 0) SMLA_W(2, 1) SMLA_W(2, 2) SMLA_W(2, 3)
+    SMLA_W(3, 0) SMLA_W(3, 1) SMLA_W(3, 2) SMLA_W(3, 3)
+    default: wait_vm(); break;
   }
+#undef SMLA_W
 }
 
+// Key pages of request b: its longest row, capped at the width, in 64-token pages.
+template <int NN>
+__device__ __forceinline__ int request_pages(const IndexerLogitsArgs& a, int b) {
+  int m = 0;
+#pragma unroll
+  for (int i = 0; i < NN; ++i) m = max(m, min(a.row_len[(size_t)b * NN + i], a.width));
+  return (m + kKeyPage - 1) / kKeyPage;
+}
+
+// Block-wide inclusive scan of one 64-bit value per thread (256 threads); `tmp` holds 4.
+__device__ __forceinline__ long long block_incl_scan64(long long v, long long* tmp, long long& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  long long x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const long long y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  long long before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    before += w < wave ? tmp[w] : 0;
+    total += tmp[w];
+  }
+  __syncthreads();
+  return x + before;
+}
+
+// Logits: a fixed grid of a.slots workgroups (a few per CU).  The key pages of all requests,
+// in request order, are cut into a.slots equal runs of consecutive pages; workgroup k takes
+// run k, request by request, in segments of at most kSegPages pages.  A segment loads the
+// request's queries, weights and page ids, fills the four-page ring, and then streams its
+// pages with the copies kRing - 1 pages ahead; a request's next_n rows are served by the
+// waves as before, so a key page is read once for all of them.
 template <int NN>
 __global__ __launch_bounds__(256, 3) void indexer_logits_kernel(IndexerLogitsArgs a) {
   // G groups of next_n waves split each page's two 32-token blocks
   constexpr int G = NN <= 2 ? 2 : 1;
+  // logit stores per page of an active wave (one per 32-token block it serves)
+  constexpr int ST = 2 / G;
   __shared__ __attribute__((aligned(16))) uint8_t sRing[kRing * kSlotBytes];
-  __shared__ __attribute__((aligned(16))) float sStage[NN][kChunkPages * kKeyPage];
-  __shared__ int sPage[kChunkPages];
-  __shared__ int sOk[kChunkPages];
+  __shared__ int sPage[kSegPages];
+  __shared__ int sOk[kSegPages];
+  __shared__ long long sScan[4];
+  __shared__ long long sStart[2];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = blockIdx.y;
-  const int p0 = blockIdx.x * kChunkPages;
-  const int row0 = b * NN;
-  int len_max = 0;
-#pragma unroll
-  for (int i = 0; i < NN; ++i) len_max = max(len_max, min(a.row_len[row0 + i], a.width));
-  const int npages_b = (len_max + kKeyPage - 1) / kKeyPage;
-  if (p0 >= npages_b) return;                       // the whole workgroup
-  const int np = min(kChunkPages, npages_b - p0);
+  const int B = a.num_requests;
+
+  // ---- this workgroup's run of pages [g0, g1) and the request and page it starts at
+  long long T = 0;
+  for (int base = 0; base < B; base += 256) {
+    const int bb = base + tid;
+    long long tot;
+    block_incl_scan64(bb < B ? request_pages<NN>(a, bb) : 0, sScan, tot);
+    T += tot;
+  }
+  const long long g0 = (long long)blockIdx.x * T / a.slots;
+  const long long g1 = (long long)(blockIdx.x + 1) * T / a.slots;
+  if (g0 >= g1) return;                              // the whole workgroup
+  {
+    long long run = 0;
+    for (int base = 0; base < B; base += 256) {
+      const int bb = base + tid;
+      const int np = bb < B ? request_pages<NN>(a, bb) : 0;
+      long long tot;
+      const long long incl = run + block_incl_scan64(np, sScan, tot);
+      if (np > 0 && incl - np <= g0 && g0 < incl) {
+        sStart[0] = bb;
+        sStart[1] = g0 - (incl - np);
+      }
+      run += tot;
+    }
+    __syncthreads();
+  }
+  // uniform: kept in SGPRs (so the output buffer descriptor below is scalar)
+  int b = __builtin_amdgcn_readfirstlane((int)sStart[0]);
+  int p = __builtin_amdgcn_readfirstlane((int)sStart[1]);
+  long long g = g0;
 
   const bool active = wave < NN * G;
   const int ri = wave % NN, grp = wave / NN;
-  const int row = row0 + ri;
-  const int row_len = min(a.row_len[row], a.width);
 
-  // the chunk's page ids are loaded first and stored to LDS after the query loads are
-  // issued, so storing them waits for the oldest load only
-  const int pt_p = p0 + tid;
-  const int pid = tid < kChunkPages && pt_p < npages_b ? a.page_table[(size_t)b * a.max_pages + pt_p] : 0;
-  // A operands (queries) and weights of this wave's row: head block mb holds heads
-  // 32mb + lane%32; k-step ks covers dims 64ks .. 64ks+63, lane half lane/32 its bytes
-  // 32*(lane/32) .. +31.  The accumulator register j of a block holds head
-  // 8(j/4) + 4(lane/32) + j%4, whose weight is wj[mb][j].
-  // Every wave loads (an inactive wave's row, row0 + wave % NN, is a real row whose values
-  // go unused): with no branch around these loads, storing the page ids below waits for the
-  // page-id load alone.
-  i32x8 qa[2][2];
-  float wj[2][16];
-  {
+  // Page copies: wave w's instruction j fills 1 KB of codes (tokens 8(4j + w) .. +7, lane
+  // = physical chunk); wave 0 also copies the 64 scales.
+  auto issue_page = [&](int it) {
+    uint8_t* slot = sRing + (it % kRing) * kSlotBytes;
+    const uint8_t* src = a.keys + (size_t)sPage[it] * kKeyPageBytes;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int t = 8 * (4 * j + wave) + (lane >> 3);
+      const int lc = (lane & 7) ^ key_swz(t);
+      dma16(src + t * kIdxDim + 16 * lc, slot + 1024 * (4 * j + wave));
+    }
+    if (wave == 0) dma4(src + kKeyPageCodes + 4 * lane, slot + kKeyPageCodes);
+  };
+
+  while (g < g1) {
+    const int npb = request_pages<NN>(a, b);
+    if (p >= npb) {                                 // next request (uniform)
+      ++b;
+      p = 0;
+      continue;
+    }
+    const int n = (int)min((long long)min(npb - p, kSegPages), g1 - g);
+    const int row = b * NN + ri;
+    const int row_len = __builtin_amdgcn_readfirstlane(min(a.row_len[row], a.width));
+
+    // page ids of the segment
+    if (tid < n) {
+      const int pid = a.page_table[(size_t)b * a.max_pages + p + tid];
+      const bool ok = pid >= 0 && pid < a.num_pages;
+      sPage[tid] = ok ? pid : 0;                    // invalid pages are read from page 0
+      sOk[tid] = ok;
+    }
+    // A operands (queries) and weights of this wave's row: head block mb holds heads
+    // 32mb + lane%32; k-step ks covers dims 64ks .. 64ks+63, lane half lane/32 its bytes
+    // 32*(lane/32) .. +31.  The accumulator register j of a block holds head
+    // 8(j/4) + 4(lane/32) + j%4, whose weight is wj[mb][j].  Inactive waves load a real
+    // row (row0 + wave % NN) whose values go unused.
+    i32x8 qa[2][2];
+    float wj[2][16];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       const uint8_t* qh = a.q + ((size_t)row * kIdxHeads + 32 * mb + (lane & 31)) * kIdxDim + 32 * (lane >> 5);
@@ -122,81 +212,71 @@ __global__ __launch_bounds__(256, 3) void indexer_logits_kernel(IndexerLogitsArg
         for (int e = 0; e < 4; ++e) wj[mb][4 * g4 + e] = w4[e];
       }
     }
-  }
-  if (tid < kChunkPages) {
-    const bool ok = pt_p < npages_b && pid >= 0 && pid < a.num_pages;
-    sPage[tid] = ok ? pid : 0;                      // invalid pages are read from page 0
-    sOk[tid] = ok;
-  }
-  // No wait for the query and weight loads here (the barrier waits for LDS operations
-  // only): the first page copies go out while those loads are still in flight.  They are
-  // older than the copies, so the per-page vmcnt waits below also cover them.
-  __syncthreads();
+    // this wave's row of logits as a range-checked buffer of row_len floats: a store at or
+    // past the row's length is dropped by the hardware, so every page issues the same store
+    // instructions (the waits below count them) and positions past the length stay untouched
+    const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        a.logits + (size_t)row * a.width, (short)0, active ? row_len * 4 : 0, 0x00020000);
+    __syncthreads();                                // page ids visible
 
-  // Page copies: wave w's instruction j fills 1 KB of codes (tokens 8(4j + w) .. +7, lane
-  // = physical chunk); wave 0 also copies the 64 scales.
-  auto issue_page = [&](int it) {
-    uint8_t* slot = sRing + (it % kRing) * kSlotBytes;
-    const uint8_t* src = a.keys + (size_t)sPage[it] * kKeyPageBytes;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int t = 8 * (4 * j + wave) + (lane >> 3);
-      const int lc = (lane & 7) ^ key_swz(t);
-      dma16(src + t * kIdxDim + 16 * lc, slot + 1024 * (4 * j + wave));
-    }
-    if (wave == 0) dma4(src + kKeyPageCodes + 4 * lane, slot + kKeyPageCodes);
-  };
-  // this wave's copies per page: 3 (wave 0) or 2; the pages issued after `it` may stay
-  // in flight
-  auto wait_page = [&](int it) {
-    const int later = min(np - 1, it + kRing - 1) - it;
-    if (wave == 0) wait_later<3>(later); else wait_later<2>(later);
-  };
+    for (int it = 0; it < min(n, kRing); ++it) issue_page(it);
+    // The compiler does not see the page copies (inline asm): one full wait here, which it
+    // does see, lets it count the query, weight and page-id loads as done, so it puts no
+    // waits of its own inside the page loop.  It costs the spread of the first copies.
+    wait_vm();
 
-  for (int it = 0; it < min(np, kRing); ++it) issue_page(it);
-  for (int it = 0; it < np; ++it) {
-    wait_page(it);
-    __syncthreads();
-    if (active) {
-      const uint8_t* slot = sRing + (it % kRing) * kSlotBytes;
-      const float* scl = reinterpret_cast<const float*>(slot + kKeyPageCodes);
-      const bool page_ok = sOk[it] != 0;
+    for (int it = 0; it < n; ++it) {
+      {
+        const int lc = min(kRing - 1, n - 1 - it), ls = min(it, kRing - 1);
+        if (wave == 0) wait_page_sched<3, ST>(lc, ls);
+        else if (active) wait_page_sched<2, ST>(lc, ls);
+        else wait_page_sched<2, 0>(lc, ls);
+      }
+      __syncthreads();
+      if (active) {
+        const uint8_t* slot = sRing + (it % kRing) * kSlotBytes;
+        const float* scl = reinterpret_cast<const float*>(slot + kKeyPageCodes);
+        const bool page_ok = sOk[it] != 0;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        if (nb % G != grp) continue;
-        const int tn = 32 * nb + (lane & 31);      // this lane's token in the page
-        f32x16 acc[2] = {f32x16{}, f32x16{}};
+        for (int nb = 0; nb < 2; ++nb) {
+          if (nb % G != grp) continue;
+          const int tn = 32 * nb + (lane & 31);      // this lane's token in the page
+          f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int lc = 4 * ks + 2 * (lane >> 5);
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(slot + tn * kIdxDim + 16 * (lc ^ key_swz(tn)));
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(slot + tn * kIdxDim + 16 * ((lc + 1) ^ key_swz(tn)));
-          const i32x8 kb = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          for (int ks = 0; ks < 2; ++ks) {
+            const int lc = 4 * ks + 2 * (lane >> 5);
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(slot + tn * kIdxDim + 16 * (lc ^ key_swz(tn)));
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(slot + tn * kIdxDim + 16 * ((lc + 1) ^ key_swz(tn)));
+            const i32x8 kb = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+              acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mb][ks], kb, acc[mb], 0, 0, 0, 127, 0, 127);
+          }
+          // ReLU as a signed-integer max on the bits (a negative float is a negative
+          // integer, so it becomes +0; a non-negative one is unchanged): one instruction,
+          // where fmaxf costs two (its NaN-quieting canonicalization, then the max).  Two
+          // partial sums, one per head block, halve the dependent FMA chain.
+          float part[2] = {0.f, 0.f};
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
-            acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mb][ks], kb, acc[mb], 0, 0, 0, 127, 0, 127);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const float r = __int_as_float(max(__float_as_int(acc[mb][j]), 0));
+              part[mb] = __builtin_fmaf(wj[mb][j], r, part[mb]);
+            }
+          const float logit = page_ok ? halves_sum(part[0] + part[1]) * scl[tn] : -INFINITY;
+          // lanes 32..63 hold the same sums: their offset is past any row, so they store nothing
+          const int t_rel = (p + it) * kKeyPage + tn;
+          const int off = lane < 32 ? 4 * t_rel : INT32_MAX - 3;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(logit), out_rsrc, off, 0, 0);
         }
-        float part = 0.f;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) part = __builtin_fmaf(wj[mb][j], fmaxf(acc[mb][j], 0.f), part);
-        const float logit = halves_sum(part) * scl[tn];
-        const int t_abs = (p0 + it) * kKeyPage + tn;
-        if (lane < 32) sStage[ri][it * kKeyPage + tn] = (page_ok && t_abs < row_len) ? logit : -INFINITY;
       }
+      __syncthreads();
+      if (it + kRing < n) issue_page(it + kRing);
     }
-    __syncthreads();
-    if (it + kRing < np) issue_page(it + kRing);
-  }
-  __syncthreads();
-  // store the chunk's logits of every row, positions below the row's length only
-  for (int i = 0; i < NN; ++i) {
-    const int rl = min(a.row_len[row0 + i], a.width);
-    const int base = p0 * kKeyPage;
-    const int n = min(np * kKeyPage, rl - base);
-    float* dst = a.logits + (size_t)(row0 + i) * a.width + base;
-    for (int t = tid; t < n; t += 256) dst[t] = sStage[i][t];
+    g += n;
+    p += n;
+    __syncthreads();                                // the ring and the page ids are free
   }
 }
 
@@ -551,8 +631,8 @@ hipError_t launch_translate(const int32_t* idx, const int32_t* row_req, const in
 }
 
 hipError_t launch_indexer_logits(const IndexerLogitsArgs& a, int next_n, int num_requests, hipStream_t st) {
-  const int chunks = (a.width / kKeyPage + kChunkPages - 1) / kChunkPages;
-  const dim3 grid(chunks, num_requests);
+  if (a.slots < 1 || a.num_requests != num_requests) return hipErrorInvalidValue;
+  const dim3 grid(a.slots);
   switch (next_n) {
     case 1: hipLaunchKernelGGL(indexer_logits_kernel<1>, grid, dim3(256), 0, st, a); break;
     case 2: hipLaunchKernelGGL(indexer_logits_kernel<2>, grid, dim3(256), 0, st, a); break;

@@ -33,6 +33,8 @@ struct IndexerLogitsArgs {
   const int32_t* page_table;    // [B][max_pages]
   float* logits;                // [R][width]
   int32_t max_pages, num_pages, width;
+  int32_t num_requests;          // B (rows = B * next_n)
+  int32_t slots;                 // workgroups of the balanced schedule (a few per CU)
 };
 
 struct IndexerTopkArgs {

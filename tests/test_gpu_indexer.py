@@ -109,6 +109,34 @@ def test_logits_chunk_edges_invalid_pages_and_width_clamp():
         assert np.all(d <= 2.0 ** -14 * mags[r][fin] + 1e-30)
 
 
+def test_logits_many_requests_empty_rows_and_untouched_tail():
+    """More requests than one pass of the workgroup's schedule scan (300 > 256), rows of
+    length 0, a request whose rows are all empty between non-empty ones, rows ending inside
+    a page, and rows of one request with different lengths.  Every position below a row's
+    length matches the oracle; every position at or past it keeps what the buffer held."""
+    spec = W.INDEXER_WORKLOADS["idx_small"].scaled(next_n=3, num_requests=300, ctx_lo=1, ctx_hi=400)
+    inp = W.make_indexer_inputs(spec, 31)
+    rl = inp.row_len.clone()
+    rl[0:3] = torch.tensor([0, 5, 0], dtype=torch.int32)           # request 0: mixed
+    rl[3 * 150: 3 * 151] = 0                                        # request 150: all empty
+    rl[3 * 151: 3 * 152] = torch.tensor([64, 63, 65], dtype=torch.int32)
+    rl[-3:] = torch.tensor([1, 0, 129], dtype=torch.int32)          # the last request
+    inp.row_len = rl
+    g = lambda t: t.to(DEV).contiguous()  # noqa: E731
+    sentinel = 12345.5
+    buf = torch.full((inp.num_rows, inp.width), sentinel, dtype=torch.float32, device=DEV)
+    announce(f"indexer logits: 300 requests x 3 rows, width {inp.width}")
+    B.indexer_logits(g(inp.q_codes), g(inp.weights), inp.key_cache.to(DEV), g(inp.row_len),
+                     g(inp.page_table), 3, inp.width, logits=buf)
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    lens = inp.row_len.numpy()
+    for r in range(inp.num_rows):
+        assert np.all(got[r, lens[r]:] == sentinel), f"row {r} written past its length {lens[r]}"
+    rows = [r for r in range(inp.num_rows) if lens[r] > 0]
+    _check_logits(inp, buf, rows, "logits, 300 requests")
+
+
 def test_logits_full_size_sampled():
     """The index lists of the headline decode workload: 128 requests x 4 rows over 8K..128K
     contexts, in the benchmark's launch configuration; sampled rows checked."""
