@@ -155,11 +155,14 @@ smla_status sparse_mla_decode_plan(const smla_problem* p, int32_t num_cus, smla_
   uint64_t off = 0;
   const bool partials_in_ws = s > 1 && !(p->flags & SMLA_F_PARTIALS_ONLY);
   if (partials_in_ws) {
-    const uint64_t rsh = (uint64_t)p->num_rows * s * p->num_heads;
+    // the decode's own split format: O blocks of whole 32-head groups (padded heads
+    // included), then (reference max, probability sum) per head
+    const uint64_t rs = (uint64_t)p->num_rows * s;
+    const uint64_t groups = (uint64_t)(p->num_heads + 31) / 32;
     pi.off_part_o = off;
-    off = round_up(off + rsh * SMLA_V_DIM * sizeof(float), 256);
+    off = round_up(off + rs * groups * 32 * SMLA_V_DIM * sizeof(float), 256);
     pi.off_part_lse = off;
-    off = round_up(off + rsh * sizeof(float), 256);
+    off = round_up(off + rs * p->num_heads * 2 * sizeof(float), 256);
   }
   if (p->flags & SMLA_F_CHECK_INDICES) {
     pi.off_err = off;
@@ -250,7 +253,7 @@ smla_status run_impl(const PlanImpl* pi, const void* q, const void* kv_cache, co
     a.part_o = partial_o;
     a.part_lse = partial_lse;
   } else if (merge) {
-    a.write_partials = 1;
+    a.write_partials = 2;
     a.part_o = reinterpret_cast<float*>(ws + pi->off_part_o);
     a.part_lse = reinterpret_cast<float*>(ws + pi->off_part_lse);
   } else {
@@ -260,8 +263,8 @@ smla_status run_impl(const PlanImpl* pi, const void* q, const void* kv_cache, co
   }
   if (smla::launch_decode(a, p.kv_format, st) != hipSuccess) return SMLA_ERR_HIP;
   if (merge) {
-    if (smla::launch_merge(a.part_o, a.part_lse, a.R, a.S, a.H, sinks,
-                           reinterpret_cast<uint16_t*>(out), lse, st) != hipSuccess)
+    if (smla::launch_merge_native(a.part_o, a.part_lse, a.R, a.S, a.H, sinks, a.out_scale,
+                                  reinterpret_cast<uint16_t*>(out), lse, st) != hipSuccess)
       return SMLA_ERR_HIP;
   }
   return SMLA_OK;

@@ -119,7 +119,10 @@ struct Cfg {
   static constexpr int NMIN = NL / NW + RR / NW;
 };
 
-template <int NW, int FMT>
+// NATIVE: the epilogue writes split partials in the merge's own format (write_partials 2)
+// and nothing else; otherwise it writes the output or the documented partials.  Two
+// instantiations, so neither epilogue changes the other's register allocation.
+template <int NW, int FMT, bool NATIVE>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   using C = Cfg<NW, FMT>;
   // load_slots(tile) reads up to index (tile + 1) * kT + kT - 1 (the scale copy of the next
@@ -834,6 +837,25 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 
   // ---- 6. epilogue ----------------------------------------------------------------------
   const float l_tot = sum_halves(l_part);
+  if constexpr (NATIVE) {
+    // Split partials for this library's own merge, in the accumulators' own layout: each
+    // store is one 1 KB run (register group k of block b, all 64 lanes), with no LDS stage
+    // and no normalization; beside them the head's reference max (log2 domain) and its
+    // probability sum, from which the merge forms the weights.
+    const size_t rs = (size_t)row * a.S + split;
+    const int nwh = (a.H + 31) >> 5;
+    float* base = a.part_o + (rs * nwh + wave) * (16 * 4 * 64 * 4) + 4 * lane_id;
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      const f32x16 ob = kO15V && b == 15 ? O15 : O[ob_index(b)];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        *reinterpret_cast<f32x4*>(base + (4 * b + k) * (64 * 4)) =
+            f32x4{ob[4 * k], ob[4 * k + 1], ob[4 * k + 2], ob[4 * k + 3]};
+    }
+    if (G == 0 && h_ok) *reinterpret_cast<f32x2*>(a.part_lse + (rs * a.H + h) * 2) = f32x2{m_used, l_tot};
+    return;
+  } else {
   float factor, lse_v;
   if (a.write_partials) {
     if (l_tot > 0.f) {
@@ -937,6 +959,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     }
     if (a.lse != nullptr && G == 0 && h_ok) a.lse[(size_t)row * a.H + h] = lse_v;
   }
+  }
 }
 
 template <int FMT>
@@ -962,7 +985,10 @@ __global__ void fill_u64_kernel(unsigned long long* p, unsigned long long v) {
 
 template <int NW, int FMT>
 hipError_t launch_nw(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<NW, FMT>), dim3(a.R, a.S), dim3(NW * 64), 0, st, a);
+  if (a.write_partials == 2)
+    hipLaunchKernelGGL((decode_kernel<NW, FMT, true>), dim3(a.R, a.S), dim3(NW * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<NW, FMT, false>), dim3(a.R, a.S), dim3(NW * 64), 0, st, a);
   return hipGetLastError();
 }
 

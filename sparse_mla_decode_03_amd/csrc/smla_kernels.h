@@ -20,7 +20,7 @@ struct DecodeArgs {
   unsigned long long* err;      // first bad (row << 32 | pos), or null
   int32_t R, H, K, S, chunk, B;
   int32_t ps_log2, num_pages, num_slots, max_pages, index_mode;
-  int32_t write_partials;
+  int32_t write_partials;       // 0 final output, 1 documented partials, 2 the merge's own format
   float scale_log2;             // softmax_scale * log2(e) (times the tensor scale, FMT 2)
   float out_scale;              // value scale applied to the output (the tensor scale, FMT 2; else 1)
 };
@@ -48,6 +48,13 @@ int max_chunk_positions();
 hipError_t launch_decode(const DecodeArgs& a, int kv_format, hipStream_t st);
 hipError_t launch_merge(const float* part_o, const float* part_lse, int R, int S, int H,
                         const float* sinks, uint16_t* out, float* lse, hipStream_t st);
+// Merge of the decode's own split format (DecodeArgs.write_partials == 2): part_o holds,
+// per (row, split) and 32-head group, 16 blocks x 4 runs of 64 lanes x 4 unnormalized
+// floats; part_ml holds (reference max in the log2 domain, probability sum) per head;
+// out_scale multiplies the merged output (the per-tensor FP8 value scale, else 1).
+hipError_t launch_merge_native(const float* part_o, const float* part_ml, int R, int S, int H,
+                               const float* sinks, float out_scale, uint16_t* out, float* lse,
+                               hipStream_t st);
 hipError_t launch_gather_debug(const uint8_t* kv, int kv_format, int ps_log2, int num_slots,
                                const int* slots, int n, uint16_t* out, hipStream_t st);
 hipError_t launch_fill_u64(unsigned long long* p, unsigned long long v, hipStream_t st);

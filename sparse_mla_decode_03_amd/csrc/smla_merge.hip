@@ -108,7 +108,104 @@ __global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ po,
   if (lse != nullptr && lane == 0) lse[(size_t)r * H + h] = lse_v;
 }
 
+// The same merge over the decode's own split format (write_partials == 2): per (row, split)
+// and group of 32 heads, 16 blocks of 32 dv as 4 runs of 64 lanes x 4 floats (lane l: head
+// 32g + l%32, dv 32b + 8k + 4(l/32) + 0..3), unnormalized, beside (m, l) per head: the
+// head's reference max in the log2 domain and its probability sum.  With sigma the sink in
+// the log2 domain:
+//   M = max(max_c m_c, sigma), w_c = 2^(m_c - M),
+//   out = sum_c w_c O_c / (sum_c w_c l_c + 2^(sigma - M)),  lse = (M + log2 z) ln 2,
+// the same result as normalizing each chunk first; out is then multiplied by out_scale (the
+// per-tensor FP8 value scale, 1 otherwise).  One 64-lane wave per (row, head group, block);
+// each lane owns 16 outputs of one head.
+constexpr int kNatBatch = 4;      // splits whose runs are loaded together
+
+__global__ __launch_bounds__(64) void merge_native_kernel(const float* __restrict__ po,
+                                                          const float* __restrict__ pml, int R, int S,
+                                                          int H, const float* __restrict__ sinks,
+                                                          float out_scale, uint16_t* __restrict__ out,
+                                                          float* __restrict__ lse) {
+  const int nwh = (H + 31) >> 5;
+  const long long id = blockIdx.x;
+  const int b = (int)(id % 16);
+  const int g = (int)((id / 16) % nwh);
+  const int r = (int)(id / (16 * nwh));
+  const int lane = threadIdx.x;
+  const int h = 32 * g + (lane & 31);
+  const bool h_ok = h < H;
+  const int hc = h_ok ? h : H - 1;                  // padded heads read a real head's pair
+  const float sink = (sinks != nullptr) ? sinks[hc] : -INFINITY;
+  const float sig2 = sink * kLog2e;
+  const f32x2* ml = reinterpret_cast<const f32x2*>(pml) + (size_t)r * S * H + hc;
+  // pass 1: the head's largest reference over the non-empty chunks
+  float M = sig2;
+  for (int c0 = 0; c0 < S; c0 += 16) {
+    f32x2 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (c0 + j < S) v[j] = ml[(size_t)(c0 + j) * H];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (c0 + j < S && v[j][1] > 0.f) M = fmaxf(M, v[j][0]);
+  }
+  const float* src0 = po + ((size_t)r * S * nwh + g) * (16 * 4 * 64 * 4) + b * (4 * 64 * 4) + 4 * lane;
+  const size_t cstride = (size_t)nwh * (16 * 4 * 64 * 4);
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  float z = 0.f;
+  if (M != -INFINITY) {
+    // pass 2: weights and the weighted sum, kNatBatch chunks' runs in flight at a time
+    for (int c0 = 0; c0 < S; c0 += kNatBatch) {
+      f32x4 x[kNatBatch][4];
+      f32x2 v[kNatBatch];
+#pragma unroll
+      for (int j = 0; j < kNatBatch; ++j) {
+        if (c0 + j < S) {
+          v[j] = ml[(size_t)(c0 + j) * H];
+          const float* src = src0 + (c0 + j) * cstride;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) x[j][k] = *reinterpret_cast<const f32x4*>(src + k * (64 * 4));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kNatBatch; ++j) {
+        if (c0 + j < S && v[j][1] > 0.f) {
+          const float w = __builtin_amdgcn_exp2f(v[j][0] - M);
+          z += w * v[j][1];
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[4 * k + i] += w * x[j][k][i];
+        }
+      }
+    }
+    z += sig2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sig2 - M);
+  }
+  // every chunk empty: out = 0 and the LSE is the sink (or -inf)
+  const float inv = z > 0.f ? out_scale / z : 0.f;
+  const float lse_v = z > 0.f ? (M + __log2f(z)) * kLn2 : sink;
+  if (h_ok) {
+    uint16_t* dst = out + ((size_t)r * H + h) * kV + 32 * b + 4 * (lane >> 5);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      *reinterpret_cast<u32x2*>(dst + 8 * k) =
+          u32x2{pack_bf16x2(acc[4 * k] * inv, acc[4 * k + 1] * inv),
+                pack_bf16x2(acc[4 * k + 2] * inv, acc[4 * k + 3] * inv)};
+    if (lse != nullptr && b == 0 && lane < 32) lse[(size_t)r * H + h] = lse_v;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_merge_native(const float* part_o, const float* part_ml, int R, int S, int H,
+                               const float* sinks, float out_scale, uint16_t* out, float* lse,
+                               hipStream_t st) {
+  const long long blocks = (long long)R * ((H + 31) / 32) * 16;
+  hipLaunchKernelGGL(merge_native_kernel, dim3((unsigned)blocks), dim3(64), 0, st, part_o, part_ml, R,
+                     S, H, sinks, out_scale, out, lse);
+  return hipGetLastError();
+}
 
 hipError_t launch_merge(const float* part_o, const float* part_lse, int R, int S, int H,
                         const float* sinks, uint16_t* out, float* lse, hipStream_t st) {

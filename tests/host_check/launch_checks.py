@@ -19,7 +19,7 @@ sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspa
 
 from sparse_mla_decode_03_amd import binding as B  # noqa: E402
 
-DECODE, MERGE, GATHER, FILL, STORE, LOGITS, TOPK, TRANSLATE = range(8)
+DECODE, MERGE, GATHER, FILL, STORE, LOGITS, TOPK, TRANSLATE, MERGE_NATIVE = range(9)
 LOG2E = 1.4426950408889634
 W = 0x100000          # fake workspace base (256-byte aligned); never dereferenced
 P = {n: 0x200000 + 0x10000 * i for i, n in enumerate(
@@ -36,10 +36,11 @@ def setup(lib):
                                                ctypes.POINTER(ctypes.c_uint64 * 11)]
     lib.smla_hostcheck_last_merge.argtypes = [ctypes.POINTER(ctypes.c_int32 * 3),
                                               ctypes.POINTER(ctypes.c_uint64 * 2)]
+    lib.smla_hostcheck_last_merge_scale.restype = ctypes.c_float
 
 
 def counts(lib):
-    return [lib.smla_hostcheck_launches(k) for k in range(8)]
+    return [lib.smla_hostcheck_launches(k) for k in range(9)]
 
 
 def last_decode(lib):
@@ -90,7 +91,7 @@ def check_unsplit(lib):
     pr = prob()
     pl, ws = plan(lib, pr)
     assert ws == 0 and run(lib, pl) == B.OK
-    assert counts(lib) == [1, 0, 0, 0, 0, 0, 0, 0]
+    assert counts(lib) == [1, 0, 0, 0, 0, 0, 0, 0, 0]
     d = last_decode(lib)
     assert (d["R"], d["H"], d["K"], d["S"], d["chunk"], d["B"]) == (512, 128, 2048, 1, 2048, 128)
     assert (d["ps_log2"], d["num_pages"], d["num_slots"], d["max_pages"]) == (6, 90000, 90000 * 64, 2048)
@@ -105,15 +106,20 @@ def check_split_merge(lib):
     lib.smla_hostcheck_reset()
     R, S, H = 2, 8, 128
     pl, ws = plan(lib, prob(num_rows=R, num_requests=2, num_splits=S, kv_format=B.KV_BF16))
+    # the decode's own format: O of whole 32-head groups, then (max, sum) per head
     po_bytes = R * S * H * 512 * 4
-    assert ws == round_up(po_bytes, 256) + round_up(R * S * H * 4, 256)
+    assert ws == round_up(po_bytes, 256) + round_up(R * S * H * 8, 256)
     assert run(lib, pl, ws=W, wsb=ws) == B.OK
-    assert counts(lib) == [1, 1, 0, 0, 0, 0, 0, 0]
+    assert counts(lib) == [1, 0, 0, 0, 0, 0, 0, 0, 1]
     d = last_decode(lib)
-    assert (d["S"], d["chunk"], d["write_partials"], d["kv_format"]) == (S, 256, 1, B.KV_BF16)
+    assert (d["S"], d["chunk"], d["write_partials"], d["kv_format"]) == (S, 256, 2, B.KV_BF16)
     assert d["po"] == W and d["pl"] == W + round_up(po_bytes, 256) and d["out"] == 0
     (mr, ms, mh), (mpo, mpl) = last_merge(lib)
     assert (mr, ms, mh) == (R, S, H) and (mpo, mpl) == (d["po"], d["pl"])
+    assert lib.smla_hostcheck_last_merge_scale() == 1.0
+    # 16 heads fill half of one 32-head group: the O blocks cover the whole group
+    pl, ws = plan(lib, prob(num_rows=3, num_requests=3, num_heads=16, num_splits=4))
+    assert ws == round_up(3 * 4 * 32 * 512 * 4, 256) + round_up(3 * 4 * 16 * 8, 256)
 
 
 def check_partials_only(lib):
@@ -121,7 +127,7 @@ def check_partials_only(lib):
     pl, ws = plan(lib, prob(num_rows=3, num_requests=3, num_splits=4, flags=B.F_PARTIALS_ONLY))
     assert ws == 0
     assert run(lib, pl, po=P["po"], pl_=P["pl"]) == B.OK
-    assert counts(lib) == [1, 0, 0, 0, 0, 0, 0, 0]
+    assert counts(lib) == [1, 0, 0, 0, 0, 0, 0, 0, 0]
     d = last_decode(lib)
     assert d["write_partials"] == 1 and (d["po"], d["pl"]) == (P["po"], P["pl"]) and d["out"] == 0
 
@@ -144,6 +150,11 @@ def check_tensor_fp8_scales(lib):
     d = last_decode(lib)
     assert math.isclose(d["scale_log2"], LOG2E / 24 / 64, rel_tol=1e-6)
     assert d["out_scale"] == 1 / 64 and d["kv_format"] == B.KV_FP8_TENSOR
+    # split: the merge of the decode's own format applies the value scale
+    pl, ws = plan(lib, prob(num_rows=2, num_requests=2, kv_format=B.KV_FP8_TENSOR, kv_scale=1 / 64,
+                            num_splits=4))
+    assert run(lib, pl, ws=W, wsb=ws) == B.OK
+    assert lib.smla_hostcheck_last_merge_scale() == 1 / 64
 
 
 def check_global_mode(lib):
@@ -167,16 +178,17 @@ def check_noalloc(lib):
         st = lib.sparse_mla_decode_run_noalloc(ctypes.byref(pl), v(P["q"]), v(P["kv"]), v(P["idx"]), v(P["rr"]),
                                                v(P["pt"]), None, v(P["out"]), v(P["lse"]), None)
         assert st == B.OK
-    assert counts(lib) == [2, 2, 0, 0, 0, 0, 0, 0]
+    assert counts(lib) == [2, 0, 0, 0, 0, 0, 0, 0, 2]
     d = last_decode(lib)
     base = lib.smla_hostcheck_fake_scratch()
     assert d["po"] == base and d["pl"] == base + round_up(R * S * H * 512 * 4, 256)
+    assert d["write_partials"] == 2
     # an unsplit plan needs no scratch and writes the output directly
     lib.smla_hostcheck_reset()
     pl, ws = plan(lib, prob())
     st = lib.sparse_mla_decode_run_noalloc(ctypes.byref(pl), v(P["q"]), v(P["kv"]), v(P["idx"]), v(P["rr"]),
                                            v(P["pt"]), None, v(P["out"]), v(P["lse"]), None)
-    assert st == B.OK and counts(lib) == [1, 0, 0, 0, 0, 0, 0, 0] and last_decode(lib)["out"] == P["out"]
+    assert st == B.OK and counts(lib) == [1, 0, 0, 0, 0, 0, 0, 0, 0] and last_decode(lib)["out"] == P["out"]
 
 
 def check_planner_cu_count(lib):
@@ -204,7 +216,7 @@ def check_other_entry_points(lib):
     assert lib.sparse_mla_indexer_topk(v(P["out"]), v(P["rr"]), 3, 64, 16, v(P["idx"]), None) == B.OK
     assert lib.sparse_mla_translate_indices(v(P["idx"]), v(P["rr"]), v(P["pt"]), 4, 16, 2, 8, 64, 100,
                                             v(P["out"]), None) == B.OK
-    assert counts(lib) == [0, 1, 1, 0, 1, 1, 1, 1]
+    assert counts(lib) == [0, 1, 1, 0, 1, 1, 1, 1, 0]
 
 
 def main(path):

@@ -19,7 +19,7 @@
 
 namespace {
 
-enum Kind { kDecode, kMerge, kGather, kFill, kStore, kLogits, kTopk, kTranslate, kKinds };
+enum Kind { kDecode, kMerge, kGather, kFill, kStore, kLogits, kTopk, kTranslate, kMergeNative, kKinds };
 
 int g_counts[kKinds];
 smla::DecodeArgs g_last_decode;
@@ -27,6 +27,7 @@ int g_last_decode_format = -1;
 int g_last_merge[3];             // R, S, H
 const void* g_last_merge_ptrs[2];  // part_o, part_lse
 int g_cus = 256;
+float g_last_merge_scale = 0.f;
 unsigned char g_fatbin_stand_in[16];
 
 // Where the stand-in hipGetSymbolAddress says the scratch array lives: an address that
@@ -53,6 +54,17 @@ hipError_t launch_merge(const float* part_o, const float* part_lse, int R, int S
   g_last_merge[2] = H;
   g_last_merge_ptrs[0] = part_o;
   g_last_merge_ptrs[1] = part_lse;
+  return hipSuccess;
+}
+hipError_t launch_merge_native(const float* part_o, const float* part_ml, int R, int S, int H,
+                               const float*, float out_scale, uint16_t*, float*, hipStream_t) {
+  ++g_counts[kMergeNative];
+  g_last_merge_scale = out_scale;
+  g_last_merge[0] = R;
+  g_last_merge[1] = S;
+  g_last_merge[2] = H;
+  g_last_merge_ptrs[0] = part_o;
+  g_last_merge_ptrs[1] = part_ml;
   return hipSuccess;
 }
 hipError_t launch_gather_debug(const uint8_t*, int, int, int, const int*, int, uint16_t*, hipStream_t) {
@@ -122,8 +134,9 @@ void smla_hostcheck_reset() {
   g_last_merge_ptrs[0] = g_last_merge_ptrs[1] = nullptr;
 }
 void smla_hostcheck_set_cus(int n) { g_cus = n; }
-// Launch counts by kind: 0 decode, 1 merge, 2 gather_debug, 3 fill, 4 store, 5 indexer
-// logits, 6 indexer top-k, 7 translate.
+float smla_hostcheck_last_merge_scale() { return g_last_merge_scale; }
+// Launch counts by kind: 0 decode, 1 merge (documented partials), 2 gather_debug, 3 fill,
+// 4 store, 5 indexer logits, 6 indexer top-k, 7 translate, 8 merge of the decode's own format.
 int smla_hostcheck_launches(int kind) { return kind >= 0 && kind < kKinds ? g_counts[kind] : -1; }
 uintptr_t smla_hostcheck_fake_scratch() { return kFakeScratch; }
 // The last decode launch: ints = R, H, K, S, chunk, B, ps_log2, num_pages, num_slots,
@@ -140,7 +153,7 @@ void smla_hostcheck_last_decode(int32_t* ints, float* floats, uintptr_t* ptrs) {
                         a.out, a.lse, a.part_o, a.part_lse, a.err};
   for (int i = 0; i < 11; ++i) ptrs[i] = reinterpret_cast<uintptr_t>(pv[i]);
 }
-// The last merge launch: ints = R, S, H; ptrs = part_o, part_lse.
+// The last merge launch (either kind): ints = R, S, H; ptrs = part_o, part_lse or part_ml.
 void smla_hostcheck_last_merge(int32_t* ints, uintptr_t* ptrs) {
   std::memcpy(ints, g_last_merge, sizeof(g_last_merge));
   ptrs[0] = reinterpret_cast<uintptr_t>(g_last_merge_ptrs[0]);
