@@ -293,7 +293,7 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kCandCap = 6144;                 // candidates of the first bin kept in LDS
-constexpr int kMergeCap = 2048;                // largest K whose selection is merged in LDS
+constexpr int kBitCap = 131072;                // longest row whose selection is a bitmap in LDS
 
 // Block-wide exclusive prefix sum of one value per thread; returns the prefix and the
 // total.  Uses `scratch` (kTopkWaves ints).
@@ -345,16 +345,6 @@ __device__ __forceinline__ void load_keys_run(const float* lg, int ip, int n, ui
 }
 constexpr int kRound = kPerThread * kTopkThreads;
 
-// Number of entries of the ascending list arr[0 .. len) below p.
-__device__ __forceinline__ int count_below(const int* arr, int len, int p) {
-  int lo = 0, hi = len;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (arr[mid] < p) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
-
 // The bin holding the need-th largest of a histogram counted from the top: thread i owns
 // bins nbins-1-per*i .. nbins-per*(i+1) (descending).  Writes (bin, count still needed
 // from it) to sel.  All threads call it.
@@ -381,11 +371,12 @@ __device__ __forceinline__ void find_bin(const int* hist, int nbins, int need, i
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kTopkThreads) void indexer_topk_kernel(IndexerTopkArgs a) {
+__global__ __launch_bounds__(kTopkThreads, 8) void indexer_topk_kernel(IndexerTopkArgs a) {
   __shared__ int sHist[2048];
   __shared__ uint32_t sCandKey[kCandCap];
   __shared__ int sCandPos[kCandCap];
-  __shared__ int sAbove[kMergeCap];
+  __shared__ uint32_t sBits[kBitCap / 32];
+  __shared__ int sCandN;
   __shared__ int sScan[kTopkWaves];
   __shared__ int sSel[2];
   const int r = blockIdx.x;
@@ -422,47 +413,84 @@ __global__ __launch_bounds__(kTopkThreads) void indexer_topk_kernel(IndexerTopkA
 
   uint32_t T;
   int ties_total = -1;                          // known only on the LDS path
-  // With K <= kMergeCap the row is read twice: pass 2 also keeps, in position order, the
-  // positions of the bins above b1 (fewer than K of them), and the selection from b1's
-  // candidates is merged with that list in LDS instead of a third pass over the row.
-  const bool merge = c1 <= kCandCap && K <= kMergeCap;   // block uniform
-  int n_above = 0;
+  // With a row of at most kBitCap positions the row is read twice: pass 2 marks the
+  // positions of the bins above b1 in an LDS bitmap and appends b1's keys and positions to
+  // an LDS list in any order (no scan, no barrier per round); the selection among them marks
+  // its positions too, ties by position, and the output is the bitmap read in order.
+  const bool bitmap = c1 <= kCandCap && n <= kBitCap;   // block uniform
   if (c1 <= kCandCap) {
-    // ---- pass 2: the first bin's keys and positions into LDS in position order (one block
-    // scan per round over packed counts: candidates in the low half, higher bins in the
-    // high half; each total is at most kRound), then select there ----
-    int cand_before = 0;
+    if (bitmap) {
+      // ---- pass 2 (bitmap) ----
+      const int nwords = (n + 31) >> 5;
+      for (int i = tid; i < nwords; i += kTopkThreads) sBits[i] = 0u;
+      if (tid == 0) sCandN = 0;
+      __syncthreads();
+      const int lane = tid & 63;
+      // the trip count is the same for every lane (the wave scan below needs all 64)
 #pragma unroll 1
-    for (int base = 0; base < n; base += kRound) {
-      const int ip = base + kPerThread * tid;
-      uint32_t k[kPerThread];
-      load_keys_run(lg, ip, n, k);
-      int nc = 0, na = 0;
+      for (int base = 0; base < n; base += kRound) {
+        const int ip = base + kPerThread * tid;
+        uint32_t k[kPerThread];
+        load_keys_run(lg, ip, n, k);
+        uint32_t bits = 0u;
+        int nc = 0;
 #pragma unroll
-      for (int e = 0; e < kPerThread; ++e)
-        if (ip + e < n) {
-          nc += (k[e] >> 21) == b1 ? 1 : 0;
-          na += (k[e] >> 21) > b1 ? 1 : 0;
+        for (int e = 0; e < kPerThread; ++e)
+          if (ip + e < n) {
+            const uint32_t b = k[e] >> 21;
+            bits |= (b > b1 ? 1u : 0u) << e;
+            nc += b == b1 ? 1 : 0;
+          }
+        // a thread's 8 positions sit in one word (ip is a multiple of 8); bits is 0 past n
+        if (bits) atomicOr(&sBits[ip >> 5], bits << (ip & 31));
+        // b1's entries: one slot reservation per wave, lanes in lane order
+        int incl = nc;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int y = __shfl_up(incl, d, 64);
+          if (lane >= d) incl += y;
         }
-      int tot;
-      const int pre = block_excl_scan(nc | (na << 16), sScan, tot);
-      int pc = cand_before + (pre & 0xFFFF), pa = n_above + (pre >> 16);
+        const int wave_total = __shfl(incl, 63, 64);
+        int slot0 = 0;
+        if (wave_total > 0) {
+          if (lane == 63) slot0 = atomicAdd(&sCandN, wave_total);
+          slot0 = __shfl(slot0, 63, 64);
+        }
+        int at = slot0 + incl - nc;
 #pragma unroll
-      for (int e = 0; e < kPerThread; ++e)
-        if (ip + e < n) {
-          const uint32_t b = k[e] >> 21;
-          if (b == b1) {
+        for (int e = 0; e < kPerThread; ++e)
+          if (ip + e < n && (k[e] >> 21) == b1) {
+            sCandKey[at] = k[e];
+            sCandPos[at] = ip + e;
+            ++at;
+          }
+      }
+    } else {
+      // ---- pass 2: the first bin's keys and positions into LDS in position order (one
+      // block scan per round over the candidate counts) ----
+      int cand_before = 0;
+#pragma unroll 1
+      for (int base = 0; base < n; base += kRound) {
+        const int ip = base + kPerThread * tid;
+        uint32_t k[kPerThread];
+        load_keys_run(lg, ip, n, k);
+        int nc = 0;
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e)
+          if (ip + e < n) nc += (k[e] >> 21) == b1 ? 1 : 0;
+        int tot;
+        int pc = cand_before + block_excl_scan(nc, sScan, tot);
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e)
+          if (ip + e < n && (k[e] >> 21) == b1) {
             sCandKey[pc] = k[e];
             sCandPos[pc] = ip + e;
             ++pc;
-          } else if (b > b1) {
-            if (merge) sAbove[pa] = ip + e;
-            ++pa;
           }
-        }
-      cand_before += tot & 0xFFFF;
-      n_above += tot >> 16;
+        cand_before += tot;
+      }
     }
+    // ---- the K-th largest key T among the candidates: two more histogram levels ----
     uint32_t prefix = b1 << 21, mask = 0x7FFu << 21;
 #pragma unroll 1
     for (int pass = 0; pass < 2; ++pass) {
@@ -483,42 +511,54 @@ __global__ __launch_bounds__(kTopkThreads) void indexer_topk_kernel(IndexerTopkA
       if (pass == 1) ties_total = sHist[sSel[0]];
     }
     T = prefix;
-    if (merge) {
-      // ---- selection from the candidates (position order): keys above T and the first
-      // `need` keys equal to T, compacted into sHist; then the two ascending lists are
-      // merged into the output by rank ----
-      int* sPick = sHist;
+    if (bitmap) {
+      // ---- selection: candidates above T, and the `need` ties at T with the smallest
+      // positions (all of them when every tie is taken) ----
       const bool all_ties = ties_total == need;
-      __syncthreads();                           // every thread has read ties_total
-      int ties_before = 0, n_pick = 0;
+      int last_tie = INT32_MAX;                  // ties at positions <= last_tie are taken
+      if (!all_ties) {
+        // the need-th smallest tie position, by two histogram levels over its bits
+        // (position / 64, then position % 64), counted from the top on reversed bins
+        int lvl_need = need, hi = 0;
 #pragma unroll 1
-      for (int c0 = 0; c0 < c1; c0 += kTopkThreads) {
-        const int c = c0 + tid;
-        const uint32_t kc = c < c1 ? sCandKey[c] : 0u;
-        const bool in = c < c1;
-        bool sel = in && kc > T;
-        if (all_ties) {
-          sel = sel || (in && kc == T);
-        } else {
-          const int tie = in && kc == T ? 1 : 0;
-          int tie_total;
-          const int rank = ties_before + block_excl_scan(tie, sScan, tie_total);
-          if (tie) sel = rank < need;
-          ties_before += tie_total;
+        for (int lvl = 0; lvl < 2; ++lvl) {
+          __syncthreads();
+          for (int i = tid; i < 2048; i += kTopkThreads) sHist[i] = 0;
+          __syncthreads();
+          for (int c = tid; c < c1; c += kTopkThreads) {
+            const int pos = sCandPos[c];
+            if (sCandKey[c] == T && (lvl == 0 || (pos >> 6) == hi))
+              atomicAdd(&sHist[2047 - (lvl == 0 ? (pos >> 6) : (pos & 63))], 1);
+          }
+          __syncthreads();
+          find_bin(sHist, 2048, lvl_need, sScan, sSel);
+          if (lvl == 0) hi = 2047 - sSel[0];
+          else last_tie = 64 * hi + (2047 - sSel[0]);
+          lvl_need = sSel[1];
         }
-        int pick_total;
-        const int at = n_pick + block_excl_scan(sel ? 1 : 0, sScan, pick_total);
-        if (sel) sPick[at] = sCandPos[c];
-        n_pick += pick_total;
+      }
+      for (int c = tid; c < c1; c += kTopkThreads) {
+        const uint32_t k = sCandKey[c];
+        const int pos = sCandPos[c];
+        if (k > T || (k == T && pos <= last_tie)) atomicOr(&sBits[pos >> 5], 1u << (pos & 31));
       }
       __syncthreads();
-      for (int i = tid; i < n_above; i += kTopkThreads) {
-        const int p = sAbove[i];
-        out[i + count_below(sPick, n_pick, p)] = p;
-      }
-      for (int j = tid; j < n_pick; j += kTopkThreads) {
-        const int p = sPick[j];
-        out[j + count_below(sAbove, n_above, p)] = p;
+      // ---- output: the bitmap in position order (each thread a run of words) ----
+      const int nwords = (n + 31) >> 5;
+      const int per = (nwords + kTopkThreads - 1) / kTopkThreads;
+      const int w0 = min(nwords, per * tid), w1 = min(nwords, w0 + per);
+      int cnt = 0;
+      for (int w = w0; w < w1; ++w) cnt += __popc(sBits[w]);
+      int tot;
+      int at = block_excl_scan(cnt, sScan, tot);
+      for (int w = w0; w < w1; ++w) {
+        uint32_t m = sBits[w];
+        while (m) {
+          const int bit = __ffs(m) - 1;
+          if (at < K) out[at] = 32 * w + bit;
+          ++at;
+          m &= m - 1u;
+        }
       }
       return;
     }
