@@ -209,6 +209,19 @@ def test_topk_edges():
     _topk_case(four, torch.tensor([20000, 19999], dtype=torch.int32), 2048, "four values, ties in LDS")
 
 
+def test_topk_rows_longer_than_the_bitmap():
+    """Rows past the kernel's in-LDS position bitmap (131072 positions) take the route that
+    keeps the boundary bin's entries in position order and writes the output in a last pass
+    over the row; one row just inside the bitmap for comparison, ties included."""
+    rng = np.random.default_rng(12)
+    width = 140032
+    lg = torch.from_numpy(rng.standard_normal((3, width)).astype(np.float32))
+    lg[2] = torch.from_numpy(rng.integers(0, 6, width).astype(np.float32))
+    lens = torch.tensor([140032, 131072, 139999], dtype=torch.int32)
+    announce("topk rows past the bitmap")
+    _topk_case(lg, lens, 2048, "rows of 131072 and 140000 positions")
+
+
 def test_indexer_then_decode():
     """The indexer's lists drive the decode path: logits -> top-k -> decode, compared with
     the decode oracle on the same lists."""
