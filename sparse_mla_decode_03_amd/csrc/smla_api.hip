@@ -431,6 +431,9 @@ smla_status sparse_mla_indexer_topk(const float* logits, const int32_t* row_len,
   a.out = indices;
   a.width = width;
   a.topk = topk;
+  int cus = 0;
+  if (cu_count(&cus) != 0) return SMLA_ERR_HIP;
+  a.cus = cus;
   if (smla::launch_indexer_topk(a, rows, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return SMLA_ERR_HIP;
   return SMLA_OK;

@@ -20,10 +20,17 @@
 // from the loop through a buffer descriptor of the row's length, so stores past it are
 // dropped and every page issues the same stores, which the loop's vmcnt waits count.
 //
-// Top-k: one workgroup per row.  Logits map to order-preserving 32-bit keys; three
-// histogram passes (11 + 11 + 10 bits) over the row find the K-th largest key T and how
-// many positions holding T are taken; a last pass writes every position with a key above
-// T and the first such ties in position order, compacted in ascending position order.
+// Top-k: one workgroup per row, two per CU, rows ordered by length so that a CU holds a
+// long row and a short one.  Logits map to order-preserving 32-bit keys.  A histogram of
+// the top 12 bits finds the bin of the K-th largest key; while it is built, every key at or
+// above a capture bin estimated from the row's first 8192 positions is kept in LDS with its
+// position, so a row is normally read once.  Two histogram levels (10 + 10 bits) over the
+// kept keys give the K-th largest key T and how many of its ties are taken (the smallest
+// positions), the selected positions are set in an LDS bitmap, and the output is the bitmap
+// read in order.  When the estimate fails the row is read again; rows past the bitmap's
+// 131072 positions, or with a crowded boundary bin, write the output in a last pass.
+#include <type_traits>
+
 #include "smla_device.h"
 #include "smla_kernels.h"
 
@@ -283,17 +290,23 @@ __global__ __launch_bounds__(256, 3) void indexer_logits_kernel(IndexerLogitsArg
 // ---- top-k ------------------------------------------------------------------------------
 
 // Order-preserving key of a float: larger floats give larger unsigned keys (-inf lowest
-// among non-NaN values); -0 and +0 get the same key, as they are equal.
+// among non-NaN values).  A non-negative float keeps its bits with the sign bit set; a
+// negative one becomes the two's complement negation of its bits, so -0 and +0 (equal
+// floats) share the key 0x80000000 and the more negative a float, the smaller its key.
+// Branch-free: m is 0 or all ones by the sign, and (u ^ (m | sign)) - m is u | sign or -u.
 __device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t m = (uint32_t)((int32_t)u >> 31);
+  return (u ^ (m | 0x80000000u)) - m;
 }
 
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
-constexpr int kCandCap = 6144;                 // candidates of the first bin kept in LDS
+constexpr int kBins1 = 4096;                   // first level: the top 12 bits of a key
+constexpr int kShift1 = 20;
+constexpr int kListCap = 6080;                 // keys and positions kept in LDS
 constexpr int kBitCap = 131072;                // longest row whose selection is a bitmap in LDS
+constexpr int kOrderBuckets = 32;              // length classes of the row order
 
 // Block-wide exclusive prefix sum of one value per thread; returns the prefix and the
 // total.  Uses `scratch` (kTopkWaves ints).
@@ -319,29 +332,27 @@ __device__ __forceinline__ int block_excl_scan(int v, int* scratch, int& total) 
   return before + x - v;
 }
 
-// Keys of positions 4i .. 4i+3 of the row (positions >= n give key 0, below every
-// real key but never counted: callers check the position).
-__device__ __forceinline__ void load_keys4(const float* lg, int i4, int n, uint32_t (&k)[4]) {
-  if (i4 + 3 < n) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(lg + i4);
+constexpr int kPerThread = 8;                  // consecutive positions per thread and round
+// Keys of positions ip .. ip + kPerThread - 1.  FULL: the whole round lies inside the row
+// (no checks); otherwise positions >= n give key 0, below every real key but never counted
+// (callers check the position).  The values are loaded first and the keys formed after
+// both paths join, so all of a thread's loads are in flight together.
+template <bool FULL>
+__device__ __forceinline__ void load_keys_run(const float* lg, int ip, int n, uint32_t (&k)[kPerThread]) {
+  float v[kPerThread];
+  if (FULL || ip + kPerThread <= n) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) k[e] = order_key(v[e]);
+    for (int g = 0; g < kPerThread / 4; ++g) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(lg + ip + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * g + e] = x[e];
+    }
   } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) k[e] = i4 + e < n ? order_key(lg[i4 + e]) : 0u;
+    for (int e = 0; e < kPerThread; ++e) v[e] = ip + e < n ? lg[ip + e] : 0.f;
   }
-}
-
-constexpr int kPerThread = 8;                  // consecutive positions per thread and round
-// Keys of positions i .. i + kPerThread - 1: all their loads issued before any key is formed.
-__device__ __forceinline__ void load_keys_run(const float* lg, int ip, int n, uint32_t (&k)[kPerThread]) {
-  uint32_t q[kPerThread / 4][4];
 #pragma unroll
-  for (int g = 0; g < kPerThread / 4; ++g) load_keys4(lg, ip + 4 * g, n, q[g]);
-#pragma unroll
-  for (int g = 0; g < kPerThread / 4; ++g)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) k[4 * g + e] = q[g][e];
+  for (int e = 0; e < kPerThread; ++e) k[e] = (FULL || ip + e < n) ? order_key(v[e]) : 0u;
 }
 constexpr int kRound = kPerThread * kTopkThreads;
 
@@ -372,15 +383,55 @@ __device__ __forceinline__ void find_bin(const int* hist, int nbins, int need, i
 }
 
 __global__ __launch_bounds__(kTopkThreads, 8) void indexer_topk_kernel(IndexerTopkArgs a) {
-  __shared__ int sHist[2048];
-  __shared__ uint32_t sCandKey[kCandCap];
-  __shared__ int sCandPos[kCandCap];
+  __shared__ int sHist[kBins1];
+  __shared__ uint32_t sKey[kListCap];
+  __shared__ int sPos[kListCap];
   __shared__ uint32_t sBits[kBitCap / 32];
-  __shared__ int sCandN;
+  __shared__ int sListN;
   __shared__ int sScan[kTopkWaves];
   __shared__ int sSel[2];
-  const int r = blockIdx.x;
+  __shared__ int sRow;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // ---- which row.  Two workgroups of this kernel share a CU, and a grid that fills the
+  // chip in order puts blocks b and b + cus on one CU, so the CU's time is the sum of its
+  // two rows'.  With cus < rows <= kTopkThreads every workgroup orders the rows the same
+  // way (by length class, longest first, ties by index: a bijection) and block b < cus
+  // takes rank b, block cus + j rank P - 1 - j (P = min(rows, 2 cus): a long row and a
+  // short one per CU), later blocks the ranks after P in order.
+  int r = blockIdx.x;
+  const int R = (int)gridDim.x;
+  if (R > a.cus && R <= kTopkThreads) {
+    int* table = sHist;                         // counts per (class desc, wave), then prefixes
+    const int wave = tid >> 6;
+    int cls = -1;
+    if (tid < R) {
+      const long long L = max(0, min(a.row_len[tid], a.width));
+      cls = (int)(L * kOrderBuckets / ((long long)a.width + 1));
+    }
+    int inr = 0, wc = 0;                        // rank among the wave's rows of its class
+#pragma unroll 1
+    for (int v = 0; v < kOrderBuckets; ++v) {
+      const uint64_t m = __ballot(cls == v);
+      if (cls == v)
+        inr = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (lane == v) wc = __popcll(m);
+    }
+    if (lane < kOrderBuckets) table[(kOrderBuckets - 1 - lane) * kTopkWaves + wave] = wc;
+    __syncthreads();
+    constexpr int kEntries = kOrderBuckets * kTopkWaves;
+    static_assert(kEntries <= kTopkThreads && kEntries <= kBins1, "row order table");
+    int total;
+    const int pre = block_excl_scan(tid < kEntries ? table[tid] : 0, sScan, total);
+    if (tid < kEntries) table[tid] = pre;
+    __syncthreads();
+    const int P = min(R, 2 * a.cus);
+    const int b = (int)blockIdx.x;
+    const int want = b < a.cus ? b : (b < P ? P - 1 - (b - a.cus) : b);
+    if (tid < R && table[(kOrderBuckets - 1 - cls) * kTopkWaves + wave] + inr == want) sRow = tid;
+    __syncthreads();
+    r = sRow;
+  }
   const int n = max(0, min(a.row_len[r], a.width));
   const int K = a.topk;
   const float* lg = a.logits + (size_t)r * a.width;
@@ -390,129 +441,191 @@ __global__ __launch_bounds__(kTopkThreads, 8) void indexer_topk_kernel(IndexerTo
     for (int j = tid; j < K; j += kTopkThreads) out[j] = j < n ? j : -1;
     return;
   }
-  // ---- pass 1: histogram of the top 11 bits ----
-  for (int i = tid; i < 2048; i += kTopkThreads) sHist[i] = 0;
+  // A row of at most kBitCap positions ends in an LDS bitmap of the selected positions,
+  // read in order for the output.
+  const bool bitmap = n <= kBitCap;             // block uniform
+  const int nwords = (n + 31) >> 5;
+  for (int i = tid; i < kBins1; i += kTopkThreads) sHist[i] = 0;
+  if (bitmap)
+    for (int i = tid; i < nwords; i += kTopkThreads) sBits[i] = 0u;
   if (tid == 0) {
     sSel[0] = 0;
     sSel[1] = K;
+    sListN = 0;
   }
   __syncthreads();
-  for (int ip = kPerThread * tid; ip < n; ip += kRound) {
-    uint32_t k[kPerThread];
-    load_keys_run(lg, ip, n, k);
+  // rounds wholly inside the row run without position checks; the ragged last round after
+  const int nfull = n - n % kRound;             // block uniform
+
+  // The round's keys k with lo <= k <= hi, and their positions, appended to the LDS list in
+  // any order: per element a ballot of the lanes holding one, a lane's slot the count in
+  // the earlier elements' ballots plus its rank in its own, one reservation per wave.
+  // Slots past kListCap are counted in sListN but not written.  Every lane calls it.
+  auto append = [&](auto full, int base, const uint32_t (&k)[kPerThread], uint32_t lo, uint32_t hi) {
+    constexpr bool F = decltype(full)::value;
+    const int ip = base + kPerThread * tid;
+    uint64_t sel[kPerThread];
+    int before[kPerThread], total = 0;            // wave uniform
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      sel[e] = __ballot((F || ip + e < n) && k[e] >= lo && k[e] <= hi);
+      before[e] = total;
+      total += __popcll(sel[e]);
+    }
+    if (total > 0) {
+      int slot0 = 0;
+      if (lane == 0) slot0 = atomicAdd(&sListN, total);
+      slot0 = __builtin_amdgcn_readfirstlane(slot0);
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e)
+        if (sel[e] != 0ull && ((sel[e] >> lane) & 1ull)) {
+          const int at = slot0 + before[e] +
+                         (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(sel[e] >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)sel[e], 0u));
+          if (at < kListCap) {
+            sKey[at] = k[e];
+            sPos[at] = ip + e;
+          }
+        }
+    }
+  };
+  auto hist_round = [&](auto full, int base, uint32_t (&k)[kPerThread]) {
+    constexpr bool F = decltype(full)::value;
+    const int ip = base + kPerThread * tid;
+    load_keys_run<F>(lg, ip, n, k);
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e)
-      if (ip + e < n) atomicAdd(&sHist[k[e] >> 21], 1);
+      if (F || ip + e < n) atomicAdd(&sHist[k[e] >> kShift1], 1);
+  };
+
+  // ---- pass 1: histogram of the top 12 bits.  On a bitmap row the first round (up to
+  // kRound positions) is a sample: the bin holding its ts-th largest key, ts the share of K
+  // expected in the sample plus three standard deviations, is the capture bin bt, and every
+  // key of bin bt or above is listed while the pass goes on.  When the K-th largest key of
+  // the row lies in bin bt or above and the list held every such key, the row is read once.
+  int bt = kBins1;                              // no capture
+  if (bitmap) {
+    uint32_t k0[kPerThread];
+    if (nfull > 0) hist_round(std::true_type{}, 0, k0);
+    else hist_round(std::false_type{}, 0, k0);
+    __syncthreads();
+    const int n0 = min(n, kRound);
+    int ts = K;
+    if (n0 < n) {
+      const float mu = (float)K * (float)n0 / (float)n;
+      ts = min(n0, (int)ceilf(mu + 3.0f * sqrtf(mu)) + 8);
+    }
+    find_bin(sHist, kBins1, ts, sScan, sSel);
+    bt = sSel[0];
+    const uint32_t lo = (uint32_t)bt << kShift1;
+    if (nfull > 0) append(std::true_type{}, 0, k0, lo, 0xFFFFFFFFu);
+    else append(std::false_type{}, 0, k0, lo, 0xFFFFFFFFu);
+#pragma unroll 1
+    for (int base = kRound; base < nfull; base += kRound) {
+      uint32_t k[kPerThread];
+      hist_round(std::true_type{}, base, k);
+      append(std::true_type{}, base, k, lo, 0xFFFFFFFFu);
+    }
+    if (nfull > 0 && nfull < n) {
+      uint32_t k[kPerThread];
+      hist_round(std::false_type{}, nfull, k);
+      append(std::false_type{}, nfull, k, lo, 0xFFFFFFFFu);
+    }
+  } else {
+#pragma unroll 1
+    for (int base = 0; base < nfull; base += kRound) {
+      uint32_t k[kPerThread];
+      hist_round(std::true_type{}, base, k);
+    }
+    if (nfull < n) {
+      uint32_t k[kPerThread];
+      hist_round(std::false_type{}, nfull, k);
+    }
   }
   __syncthreads();
-  find_bin(sHist, 2048, K, sScan, sSel);
-  const uint32_t b1 = (uint32_t)sSel[0];
-  int need = sSel[1];
+  find_bin(sHist, kBins1, K, sScan, sSel);
+  const int b1 = sSel[0];                       // the bin of the K-th largest key
+  int need = sSel[1];                           // how many of b1's keys are taken
   const int c1 = sHist[b1];
+  const int listed = sListN;
   __syncthreads();
 
   uint32_t T;
-  int ties_total = -1;                          // known only on the LDS path
-  // With a row of at most kBitCap positions the row is read twice: pass 2 marks the
-  // positions of the bins above b1 in an LDS bitmap and appends b1's keys and positions to
-  // an LDS list in any order (no scan, no barrier per round); the selection among them marks
-  // its positions too, ties by position, and the output is the bitmap read in order.
-  const bool bitmap = c1 <= kCandCap && n <= kBitCap;   // block uniform
-  if (c1 <= kCandCap) {
-    if (bitmap) {
-      // ---- pass 2 (bitmap) ----
-      const int nwords = (n + 31) >> 5;
-      for (int i = tid; i < nwords; i += kTopkThreads) sBits[i] = 0u;
-      if (tid == 0) sCandN = 0;
+  int ties_total = -1;                          // how many keys equal T (every route sets it)
+  const bool single = bitmap && bt <= b1 && listed <= kListCap;   // block uniform
+  if (single || c1 <= kListCap) {
+    int nlist = listed;
+    if (!single) {
+      nlist = c1;
+      if (tid == 0) sListN = 0;
       __syncthreads();
-      const int lane = tid & 63;
-      // the trip count is the same for every lane (the wave scan below needs all 64)
+      const uint32_t lo = (uint32_t)b1 << kShift1, hi = lo | ((1u << kShift1) - 1u);
+      if (bitmap) {
+        // ---- pass 2: the positions of the bins above b1 marked in the bitmap, b1's keys
+        // listed (any order) ----
+        auto pass2_round = [&](auto full, int base) {
+          constexpr bool F = decltype(full)::value;
+          const int ip = base + kPerThread * tid;
+          uint32_t k[kPerThread];
+          load_keys_run<F>(lg, ip, n, k);
+          uint32_t bits = 0u;
+#pragma unroll
+          for (int e = 0; e < kPerThread; ++e) bits |= ((F || ip + e < n) && k[e] > hi ? 1u : 0u) << e;
+          // a thread's 8 positions sit in one word (ip is a multiple of 8); bits is 0 past n
+          if (bits) atomicOr(&sBits[ip >> 5], bits << (ip & 31));
+          append(full, base, k, lo, hi);
+        };
 #pragma unroll 1
-      for (int base = 0; base < n; base += kRound) {
-        const int ip = base + kPerThread * tid;
-        uint32_t k[kPerThread];
-        load_keys_run(lg, ip, n, k);
-        uint32_t bits = 0u;
-        int nc = 0;
-#pragma unroll
-        for (int e = 0; e < kPerThread; ++e)
-          if (ip + e < n) {
-            const uint32_t b = k[e] >> 21;
-            bits |= (b > b1 ? 1u : 0u) << e;
-            nc += b == b1 ? 1 : 0;
-          }
-        // a thread's 8 positions sit in one word (ip is a multiple of 8); bits is 0 past n
-        if (bits) atomicOr(&sBits[ip >> 5], bits << (ip & 31));
-        // b1's entries: one slot reservation per wave, lanes in lane order
-        int incl = nc;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const int y = __shfl_up(incl, d, 64);
-          if (lane >= d) incl += y;
-        }
-        const int wave_total = __shfl(incl, 63, 64);
-        int slot0 = 0;
-        if (wave_total > 0) {
-          if (lane == 63) slot0 = atomicAdd(&sCandN, wave_total);
-          slot0 = __shfl(slot0, 63, 64);
-        }
-        int at = slot0 + incl - nc;
-#pragma unroll
-        for (int e = 0; e < kPerThread; ++e)
-          if (ip + e < n && (k[e] >> 21) == b1) {
-            sCandKey[at] = k[e];
-            sCandPos[at] = ip + e;
-            ++at;
-          }
-      }
-    } else {
-      // ---- pass 2: the first bin's keys and positions into LDS in position order (one
-      // block scan per round over the candidate counts) ----
-      int cand_before = 0;
+        for (int base = 0; base < nfull; base += kRound) pass2_round(std::true_type{}, base);
+        if (nfull < n) pass2_round(std::false_type{}, nfull);
+      } else {
+        // ---- pass 2: b1's keys and positions in position order (one block scan per
+        // round over the counts) ----
+        int cand_before = 0;
 #pragma unroll 1
-      for (int base = 0; base < n; base += kRound) {
-        const int ip = base + kPerThread * tid;
-        uint32_t k[kPerThread];
-        load_keys_run(lg, ip, n, k);
-        int nc = 0;
+        for (int base = 0; base < n; base += kRound) {
+          const int ip = base + kPerThread * tid;
+          uint32_t k[kPerThread];
+          load_keys_run<false>(lg, ip, n, k);
+          int nc = 0;
 #pragma unroll
-        for (int e = 0; e < kPerThread; ++e)
-          if (ip + e < n) nc += (k[e] >> 21) == b1 ? 1 : 0;
-        int tot;
-        int pc = cand_before + block_excl_scan(nc, sScan, tot);
+          for (int e = 0; e < kPerThread; ++e)
+            if (ip + e < n) nc += (k[e] >> kShift1) == (uint32_t)b1 ? 1 : 0;
+          int tot;
+          int pc = cand_before + block_excl_scan(nc, sScan, tot);
 #pragma unroll
-        for (int e = 0; e < kPerThread; ++e)
-          if (ip + e < n && (k[e] >> 21) == b1) {
-            sCandKey[pc] = k[e];
-            sCandPos[pc] = ip + e;
-            ++pc;
-          }
-        cand_before += tot;
+          for (int e = 0; e < kPerThread; ++e)
+            if (ip + e < n && (k[e] >> kShift1) == (uint32_t)b1) {
+              sKey[pc] = k[e];
+              sPos[pc] = ip + e;
+              ++pc;
+            }
+          cand_before += tot;
+        }
       }
     }
-    // ---- the K-th largest key T among the candidates: two more histogram levels ----
-    uint32_t prefix = b1 << 21, mask = 0x7FFu << 21;
+    // ---- the K-th largest key T among the listed keys of bin b1: bits 19..10, then 9..0 ----
+    uint32_t prefix = (uint32_t)b1 << kShift1, mask = 0xFFFu << kShift1;
 #pragma unroll 1
     for (int pass = 0; pass < 2; ++pass) {
       const int shift = pass == 0 ? 10 : 0;
-      const int nbins = pass == 0 ? 2048 : 1024;
       __syncthreads();
-      for (int i = tid; i < 2048; i += kTopkThreads) sHist[i] = 0;
+      for (int i = tid; i < 1024; i += kTopkThreads) sHist[i] = 0;
       __syncthreads();
-      for (int c = tid; c < c1; c += kTopkThreads) {
-        const uint32_t k = sCandKey[c];
-        if ((k & mask) == prefix) atomicAdd(&sHist[(k >> shift) & (nbins - 1)], 1);
+      for (int c = tid; c < nlist; c += kTopkThreads) {
+        const uint32_t k = sKey[c];
+        if ((k & mask) == prefix) atomicAdd(&sHist[(k >> shift) & 1023], 1);
       }
       __syncthreads();
-      find_bin(sHist, nbins, need, sScan, sSel);
+      find_bin(sHist, 1024, need, sScan, sSel);
       prefix |= (uint32_t)sSel[0] << shift;
-      mask |= (uint32_t)(nbins - 1) << shift;
+      mask |= 1023u << shift;
       need = sSel[1];
       if (pass == 1) ties_total = sHist[sSel[0]];
     }
     T = prefix;
     if (bitmap) {
-      // ---- selection: candidates above T, and the `need` ties at T with the smallest
+      // ---- selection: listed keys above T, and the `need` ties at T with the smallest
       // positions (all of them when every tie is taken) ----
       const bool all_ties = ties_total == need;
       int last_tie = INT32_MAX;                  // ties at positions <= last_tie are taken
@@ -525,9 +638,9 @@ __global__ __launch_bounds__(kTopkThreads, 8) void indexer_topk_kernel(IndexerTo
           __syncthreads();
           for (int i = tid; i < 2048; i += kTopkThreads) sHist[i] = 0;
           __syncthreads();
-          for (int c = tid; c < c1; c += kTopkThreads) {
-            const int pos = sCandPos[c];
-            if (sCandKey[c] == T && (lvl == 0 || (pos >> 6) == hi))
+          for (int c = tid; c < nlist; c += kTopkThreads) {
+            const int pos = sPos[c];
+            if (sKey[c] == T && (lvl == 0 || (pos >> 6) == hi))
               atomicAdd(&sHist[2047 - (lvl == 0 ? (pos >> 6) : (pos & 63))], 1);
           }
           __syncthreads();
@@ -537,14 +650,13 @@ __global__ __launch_bounds__(kTopkThreads, 8) void indexer_topk_kernel(IndexerTo
           lvl_need = sSel[1];
         }
       }
-      for (int c = tid; c < c1; c += kTopkThreads) {
-        const uint32_t k = sCandKey[c];
-        const int pos = sCandPos[c];
+      for (int c = tid; c < nlist; c += kTopkThreads) {
+        const uint32_t k = sKey[c];
+        const int pos = sPos[c];
         if (k > T || (k == T && pos <= last_tie)) atomicOr(&sBits[pos >> 5], 1u << (pos & 31));
       }
       __syncthreads();
       // ---- output: the bitmap in position order (each thread a run of words) ----
-      const int nwords = (n + 31) >> 5;
       const int per = (nwords + kTopkThreads - 1) / kTopkThreads;
       const int w0 = min(nwords, per * tid), w1 = min(nwords, w0 + per);
       int cnt = 0;
@@ -563,26 +675,26 @@ __global__ __launch_bounds__(kTopkThreads, 8) void indexer_topk_kernel(IndexerTo
       return;
     }
   } else {
-    // ---- passes 2 and 3 over the row (a crowded first bin) ----
-    uint32_t prefix = b1 << 21, mask = 0x7FFu << 21;
+    // ---- passes 2 and 3 over the row (a crowded first bin): bits 19..10, then 9..0 ----
+    uint32_t prefix = (uint32_t)b1 << kShift1, mask = 0xFFFu << kShift1;
 #pragma unroll 1
     for (int pass = 0; pass < 2; ++pass) {
       const int shift = pass == 0 ? 10 : 0;
-      const int nbins = pass == 0 ? 2048 : 1024;
-      for (int i = tid; i < 2048; i += kTopkThreads) sHist[i] = 0;
+      for (int i = tid; i < 1024; i += kTopkThreads) sHist[i] = 0;
       __syncthreads();
       for (int ip = kPerThread * tid; ip < n; ip += kRound) {
         uint32_t k[kPerThread];
-        load_keys_run(lg, ip, n, k);
+        load_keys_run<false>(lg, ip, n, k);
 #pragma unroll
         for (int e = 0; e < kPerThread; ++e)
-          if (ip + e < n && (k[e] & mask) == prefix) atomicAdd(&sHist[(k[e] >> shift) & (nbins - 1)], 1);
+          if (ip + e < n && (k[e] & mask) == prefix) atomicAdd(&sHist[(k[e] >> shift) & 1023], 1);
       }
       __syncthreads();
-      find_bin(sHist, nbins, need, sScan, sSel);
+      find_bin(sHist, 1024, need, sScan, sSel);
       prefix |= (uint32_t)sSel[0] << shift;
-      mask |= (uint32_t)(nbins - 1) << shift;
+      mask |= 1023u << shift;
       need = sSel[1];
+      if (pass == 1) ties_total = sHist[sSel[0]];   // every key of the last bin equals T
       __syncthreads();
     }
     T = prefix;
@@ -597,7 +709,7 @@ __global__ __launch_bounds__(kTopkThreads, 8) void indexer_topk_kernel(IndexerTo
   for (int base = 0; base < n; base += kRound) {
     const int ip = base + kPerThread * tid;
     uint32_t k[kPerThread];
-    load_keys_run(lg, ip, n, k);
+    load_keys_run<false>(lg, ip, n, k);
     int sel[kPerThread], cnt = 0;
     if (all_ties) {
 #pragma unroll

@@ -42,6 +42,7 @@ struct IndexerTopkArgs {
   const int32_t* row_len;       // [R]
   int32_t* out;                 // [R][topk]
   int32_t width, topk;
+  int32_t cus;                  // compute units of the device (row order across CUs)
 };
 
 int max_chunk_positions();

@@ -209,6 +209,54 @@ def test_topk_edges():
     _topk_case(four, torch.tensor([20000, 19999], dtype=torch.int32), 2048, "four values, ties in LDS")
 
 
+def test_topk_sample_misses_and_overflow():
+    """The kernel estimates a capture threshold from the first 8192 positions of a row and
+    keeps every key above it while it builds the histogram; rows where that estimate fails
+    (a sample of larger values than the rest: the K-th largest key lies below the capture
+    bin; a sample of smaller values: more keys above it than the list holds) take the route
+    that reads the row again, with the same result."""
+    rng = np.random.default_rng(21)
+    width = 60000
+    base = rng.standard_normal((4, width)).astype(np.float32)
+    lg = torch.from_numpy(base.copy())
+    lg[0, :8192] += 6.0                      # sample far above the rest
+    lg[1, 8192:] += 4.0                      # sample far below the rest
+    lg[2, 8192:] = torch.from_numpy(np.repeat(rng.standard_normal(13000).astype(np.float32), 4)[: width - 8192])
+    lens = torch.tensor([width, width, width, 30000], dtype=torch.int32)
+    announce("topk sample misses")
+    _topk_case(lg, lens, 2048, "biased samples")
+    _topk_case(lg, lens, 9000, "biased samples, K = 9000")
+
+
+@pytest.mark.parametrize("rows", [300, 700, 1100])
+def test_topk_row_order(rows):
+    """More rows than compute units: the workgroups order the rows by length and pair long
+    with short ones on a CU (up to 1024 rows; beyond, rows keep their order).  Every row's
+    output must match, so the order is a bijection: ragged and equal lengths, rows at or
+    under K, empty rows."""
+    rng = np.random.default_rng(100 + rows)
+    width = 16384
+    lg = torch.from_numpy(rng.standard_normal((rows, width)).astype(np.float32))
+    lens = rng.integers(0, width + 1, rows)
+    lens[::7] = 12000                        # runs of equal lengths
+    lens[3::11] = 2048
+    lens[5::13] = 0
+    announce(f"topk row order R={rows}")
+    _topk_case(lg, torch.from_numpy(lens.astype(np.int32)), 2048, f"{rows} rows")
+
+
+def test_topk_full_size():
+    """Top-k over the logits of the headline decode workload (128 requests x 4 rows over
+    8K..128K contexts, K = 2048) in the benchmark's launch configuration: every row
+    against the oracle, on the kernel's own logits."""
+    spec = W.INDEXER_WORKLOADS["idx_b128_mtp4_h64"]
+    inp = W.make_indexer_inputs(spec, 5, device=DEV, cache_device=DEV)
+    announce(f"topk full size R={inp.num_rows} width={inp.width}")
+    logits = B.indexer_logits(inp.q_codes, inp.weights, inp.key_cache, inp.row_len, inp.page_table,
+                              spec.next_n, inp.width)
+    _topk_case(logits, inp.row_len, spec.topk, "full size")
+
+
 def test_topk_rows_longer_than_the_bitmap():
     """Rows past the kernel's in-LDS position bitmap (131072 positions) take the route that
     keeps the boundary bin's entries in position order and writes the output in a last pass
