@@ -118,7 +118,8 @@ __global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ po,
 // the same result as normalizing each chunk first; out is then multiplied by out_scale (the
 // per-tensor FP8 value scale, 1 otherwise).  One 64-lane wave per (row, head group, block);
 // each lane owns 16 outputs of one head.
-constexpr int kNatBatch = 4;      // splits whose runs are loaded together
+constexpr int kNatBatch = 8;      // splits whose runs are loaded together
+constexpr int kNatMl = 16;        // splits whose (m, l) pairs are loaded together
 
 __global__ __launch_bounds__(64) void merge_native_kernel(const float* __restrict__ po,
                                                           const float* __restrict__ pml, int R, int S,
@@ -137,42 +138,63 @@ __global__ __launch_bounds__(64) void merge_native_kernel(const float* __restric
   const float sink = (sinks != nullptr) ? sinks[hc] : -INFINITY;
   const float sig2 = sink * kLog2e;
   const f32x2* ml = reinterpret_cast<const f32x2*>(pml) + (size_t)r * S * H + hc;
-  // pass 1: the head's largest reference over the non-empty chunks
-  float M = sig2;
-  for (int c0 = 0; c0 < S; c0 += 16) {
-    f32x2 v[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (c0 + j < S) v[j] = ml[(size_t)(c0 + j) * H];
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (c0 + j < S && v[j][1] > 0.f) M = fmaxf(M, v[j][0]);
-  }
   const float* src0 = po + ((size_t)r * S * nwh + g) * (16 * 4 * 64 * 4) + b * (4 * 64 * 4) + 4 * lane;
   const size_t cstride = (size_t)nwh * (16 * 4 * 64 * 4);
+  // one memory round trip for the pairs of the first kNatMl splits and the runs of the
+  // first kNatBatch (all issued before any use; the runs do not depend on the weights)
+  f32x2 v[kNatMl];
+  f32x4 x[kNatBatch][4];
+#pragma unroll
+  for (int j = 0; j < kNatMl; ++j)
+    if (j < S) v[j] = ml[(size_t)j * H];
+#pragma unroll
+  for (int j = 0; j < kNatBatch; ++j)
+    if (j < S) {
+      const float* src = src0 + j * cstride;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[j][k] = *reinterpret_cast<const f32x4*>(src + k * (64 * 4));
+    }
+  // pass 1: the head's largest reference over the non-empty chunks
+  float M = sig2;
+#pragma unroll
+  for (int j = 0; j < kNatMl; ++j)
+    if (j < S && v[j][1] > 0.f) M = fmaxf(M, v[j][0]);
+  for (int c0 = kNatMl; c0 < S; c0 += 16) {
+    f32x2 u[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (c0 + j < S) u[j] = ml[(size_t)(c0 + j) * H];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (c0 + j < S && u[j][1] > 0.f) M = fmaxf(M, u[j][0]);
+  }
   float acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
   float z = 0.f;
   if (M != -INFINITY) {
-    // pass 2: weights and the weighted sum, kNatBatch chunks' runs in flight at a time
+    // pass 2: weights and the weighted sum; the first batch is already in registers
     for (int c0 = 0; c0 < S; c0 += kNatBatch) {
-      f32x4 x[kNatBatch][4];
-      f32x2 v[kNatBatch];
+      f32x2 w2[kNatBatch];
+      if (c0 > 0) {
 #pragma unroll
-      for (int j = 0; j < kNatBatch; ++j) {
-        if (c0 + j < S) {
-          v[j] = ml[(size_t)(c0 + j) * H];
-          const float* src = src0 + (c0 + j) * cstride;
+        for (int j = 0; j < kNatBatch; ++j) {
+          if (c0 + j < S) {
+            w2[j] = ml[(size_t)(c0 + j) * H];
+            const float* src = src0 + (c0 + j) * cstride;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) x[j][k] = *reinterpret_cast<const f32x4*>(src + k * (64 * 4));
+            for (int k = 0; k < 4; ++k) x[j][k] = *reinterpret_cast<const f32x4*>(src + k * (64 * 4));
+          }
         }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kNatBatch; ++j) w2[j] = v[j];
       }
 #pragma unroll
       for (int j = 0; j < kNatBatch; ++j) {
-        if (c0 + j < S && v[j][1] > 0.f) {
-          const float w = __builtin_amdgcn_exp2f(v[j][0] - M);
-          z += w * v[j][1];
+        if (c0 + j < S && w2[j][1] > 0.f) {
+          const float w = __builtin_amdgcn_exp2f(w2[j][0] - M);
+          z += w * w2[j][1];
 #pragma unroll
           for (int k = 0; k < 4; ++k)
 #pragma unroll
