@@ -128,7 +128,11 @@ int choose_splits(const smla_problem* p, int num_cus) {
   const int64_t rows = p->num_rows > 0 ? p->num_rows : 1;
   if (rows < num_cus) {
     int want = (int)((num_cus + rows - 1) / rows);
-    const int by_len = p->topk / 128 > 0 ? p->topk / 128 : 1;
+    // chunks of at least 128 positions, but a list of two tiles or more still splits in two
+    // (two one-tile chunks and the merge beat one two-tile pass when rows are few)
+    int by_len = p->topk / 128;
+    const int short_split = p->topk >= 64 ? 2 : 1;
+    if (by_len < short_split) by_len = short_split;
     if (want > by_len) want = by_len;
     if (want > s) s = want;
   } else {

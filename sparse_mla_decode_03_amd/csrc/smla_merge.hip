@@ -154,11 +154,15 @@ __global__ __launch_bounds__(64) void merge_native_kernel(const float* __restric
 #pragma unroll
       for (int k = 0; k < 4; ++k) x[j][k] = *reinterpret_cast<const f32x4*>(src + k * (64 * 4));
     }
-  // pass 1: the head's largest reference over the non-empty chunks
+  // pass 1: the head's largest reference over the non-empty chunks (and the sink)
   float M = sig2;
+  bool any = false;                                  // a non-empty chunk
 #pragma unroll
   for (int j = 0; j < kNatMl; ++j)
-    if (j < S && v[j][1] > 0.f) M = fmaxf(M, v[j][0]);
+    if (j < S && v[j][1] > 0.f) {
+      M = fmaxf(M, v[j][0]);
+      any = true;
+    }
   for (int c0 = kNatMl; c0 < S; c0 += 16) {
     f32x2 u[16];
 #pragma unroll
@@ -166,13 +170,16 @@ __global__ __launch_bounds__(64) void merge_native_kernel(const float* __restric
       if (c0 + j < S) u[j] = ml[(size_t)(c0 + j) * H];
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      if (c0 + j < S && u[j][1] > 0.f) M = fmaxf(M, u[j][0]);
+      if (c0 + j < S && u[j][1] > 0.f) {
+        M = fmaxf(M, u[j][0]);
+        any = true;
+      }
   }
   float acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
   float z = 0.f;
-  if (M != -INFINITY) {
+  if (any) {
     // pass 2: weights and the weighted sum; the first batch is already in registers
     for (int c0 = 0; c0 < S; c0 += kNatBatch) {
       f32x2 w2[kNatBatch];
@@ -204,7 +211,7 @@ __global__ __launch_bounds__(64) void merge_native_kernel(const float* __restric
     }
     z += sig2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sig2 - M);
   }
-  // every chunk empty: out = 0 and the LSE is the sink (or -inf)
+  // every chunk empty: z = 0, so out = 0 and the LSE is the sink itself (or -inf)
   const float inv = z > 0.f ? out_scale / z : 0.f;
   const float lse_v = z > 0.f ? (M + __log2f(z)) * kLn2 : sink;
   if (h_ok) {

@@ -119,6 +119,11 @@ def test_plan_splits_and_workspace(lib):
     st, p, ws = _plan_status(lib, _prob(num_rows=32))
     s = lib.sparse_mla_plan_num_splits(ctypes.byref(p))
     assert st == B.OK and 1 < s <= 2048 // 128
+    # a short list of two tiles over few rows splits in two; one tile does not split
+    st, p, ws = _plan_status(lib, _prob(num_rows=1, topk=64))
+    assert st == B.OK and lib.sparse_mla_plan_num_splits(ctypes.byref(p)) == 2
+    st, p, ws = _plan_status(lib, _prob(num_rows=1, topk=32))
+    assert st == B.OK and lib.sparse_mla_plan_num_splits(ctypes.byref(p)) == 1 and ws == 0
     # partials-only keeps the partials out of the workspace
     st, p, ws = _plan_status(lib, _prob(num_rows=2, num_splits=4, flags=B.F_PARTIALS_ONLY))
     assert st == B.OK and ws == 0

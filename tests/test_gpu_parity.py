@@ -258,17 +258,19 @@ def test_merge_kernel_matches_oracle_merge(R, S, H):
 
 # ------------------------------------------------------------------ edge cases
 
-def test_empty_rows_and_zero_rows():
+@pytest.mark.parametrize("splits", [0, 1, 2, 3])
+def test_empty_rows_and_zero_rows(splits):
+    # an empty row gives out = 0 and LSE = the sink exactly, unsplit and through the merge
     inp = _small(heads=16, topk=64, nreq=3, rows=(1,), seed=31)
     idx = inp.indices.clone()
     idx[1] = -1
-    announce("empty row")
-    out, lse = gpu_decode(inp, indices=idx)
+    announce(f"empty row, splits {splits}")
+    out, lse = gpu_decode(inp, indices=idx, num_splits=splits)
     o, l = oracle_decode(inp, indices=idx)
     compare(out, lse, o, l, what="empty row")
     assert torch.all(out[1] == 0)
     assert torch.equal(lse[1].cpu(), inp.sinks)
-    out, lse = gpu_decode(inp, indices=idx, sinks=None)
+    out, lse = gpu_decode(inp, indices=idx, sinks=None, num_splits=splits)
     assert torch.all(out[1] == 0) and torch.isneginf(lse[1]).all()
     # zero rows: nothing launched, empty results
     z = W.Inputs(inp.spec, inp.q[:0], inp.kv_cache, inp.indices[:0], inp.row_req[:0],
