@@ -15,7 +15,8 @@
 // the request on its share of each page's two 32-token blocks, so a page is read from HBM
 // once for all rows.  Scores come from the FP8 MFMA 32x32x64 (rows = 32 heads, columns =
 // 32 tokens); each lane then holds one token and 16 heads of a block, so the weighted ReLU
-// sum over heads is 32 FMAs and one swap between lane halves.  The key scale multiplies
+// sum over heads is 32 FMAs, and one swap between lane halves finishes both token blocks of a
+// page (block 0 in lanes 0..31, block 1 in lanes 32..63), stored together.  The key scale multiplies
 // the head sum (the ReLU is positively homogeneous; scales are >= 0).  Logits are stored
 // from the loop through a buffer descriptor of the row's length, so stores past it are
 // dropped and every page issues the same stores, which the loop's vmcnt waits count.
@@ -48,6 +49,18 @@ constexpr int kKeyPageBytes = kKeyPageCodes + 4 * kKeyPage;
 constexpr int kSegPages = 256;                   // page ids staged per segment
 constexpr int kRing = 4;
 constexpr int kSlotBytes = kKeyPageBytes;          // one LDS ring slot
+
+// Copies (global -> LDS, 16 or 4 bytes per lane) from a wave-uniform base address in SGPRs
+// plus a 32-bit per-lane byte offset, so the page loop keeps no 64-bit per-lane address
+// arithmetic; lds_addr is the wave's LDS destination (m0).
+__device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory");
+}
+__device__ __forceinline__ void dma4_sv(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory");
+}
 
 __device__ __forceinline__ float halves_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -117,8 +130,9 @@ template <int NN>
 __global__ __launch_bounds__(256, 3) void indexer_logits_kernel(IndexerLogitsArgs a) {
   // G groups of next_n waves split each page's two 32-token blocks
   constexpr int G = NN <= 2 ? 2 : 1;
-  // logit stores per page of an active wave (one per 32-token block it serves)
-  constexpr int ST = 2 / G;
+  // logit stores per page of an active wave: one (a wave serving both 32-token blocks
+  // stores them together, block 0 from lanes 0..31 and block 1 from lanes 32..63)
+  constexpr int ST = 1;
   __shared__ __attribute__((aligned(16))) uint8_t sRing[kRing * kSlotBytes];
   __shared__ int sPage[kSegPages];
   __shared__ int sOk[kSegPages];
@@ -162,19 +176,41 @@ __global__ __launch_bounds__(256, 3) void indexer_logits_kernel(IndexerLogitsArg
 
   const bool active = wave < NN * G;
   const int ri = wave % NN, grp = wave / NN;
+  // byte offset of this lane's token in a page's logits, per token block; lanes 32..63
+  // start at 2^31, past any row's length in bytes
+  int st_base[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) st_base[nb] = lane < 32 ? 4 * (32 * nb + lane) : (int)0x80000000u;
+  // byte offsets in a ring slot of this lane's B-operand chunks of token block 0 (k-step ks,
+  // half hh); token block 1 is 32 tokens (4096 bytes) further with the same swizzle, since
+  // the swizzle depends on token bits 1..3 only
+  int koff[2][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int tn0 = lane & 31;
+      const int lc = 4 * ks + 2 * (lane >> 5) + hh;
+      koff[ks][hh] = tn0 * kIdxDim + 16 * (lc ^ key_swz(tn0));
+    }
+  static_assert(((32 >> 1) & 7) == 0, "token block 1 shares block 0's swizzle");
 
   // Page copies: wave w's instruction j fills 1 KB of codes (tokens 8(4j + w) .. +7, lane
   // = physical chunk); wave 0 also copies the 64 scales.
-  auto issue_page = [&](int it) {
-    uint8_t* slot = sRing + (it % kRing) * kSlotBytes;
-    const uint8_t* src = a.keys + (size_t)sPage[it] * kKeyPageBytes;
+  // this lane's source offsets in a key page (fixed), and the ring's LDS address
+  uint32_t src_off[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int t = 8 * (4 * j + wave) + (lane >> 3);
-      const int lc = (lane & 7) ^ key_swz(t);
-      dma16(src + t * kIdxDim + 16 * lc, slot + 1024 * (4 * j + wave));
-    }
-    if (wave == 0) dma4(src + kKeyPageCodes + 4 * lane, slot + kKeyPageCodes);
+  for (int j = 0; j < 2; ++j) {
+    const int t = 8 * (4 * j + wave) + (lane >> 3);
+    src_off[j] = t * kIdxDim + 16 * ((lane & 7) ^ key_swz(t));
+  }
+  const uint32_t ring_lds = lds_offset(sRing);
+  auto issue_page = [&](int it, int u) {             // u = it % kRing
+    const uint8_t* src = a.keys + (size_t)__builtin_amdgcn_readfirstlane(sPage[it]) * kKeyPageBytes;
+    const uint32_t slot = ring_lds + u * kSlotBytes;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16_sv(src, src_off[j], slot + 1024 * (4 * j + wave));
+    if (wave == 0) dma4_sv(src, kKeyPageCodes + 4 * lane, slot + kKeyPageCodes);
   };
 
   while (g < g1) {
@@ -226,13 +262,19 @@ __global__ __launch_bounds__(256, 3) void indexer_logits_kernel(IndexerLogitsArg
         a.logits + (size_t)row * a.width, (short)0, active ? row_len * 4 : 0, 0x00020000);
     __syncthreads();                                // page ids visible
 
-    for (int it = 0; it < min(n, kRing); ++it) issue_page(it);
+    for (int it = 0; it < min(n, kRing); ++it) issue_page(it, it);
     // The compiler does not see the page copies (inline asm): one full wait here, which it
     // does see, lets it count the query, weight and page-id loads as done, so it puts no
     // waits of its own inside the page loop.  It costs the spread of the first copies.
     wait_vm();
 
-    for (int it = 0; it < n; ++it) {
+    // the page loop unrolled by the ring: each page's slot is a constant LDS offset
+    // (folded into the reads' immediate offsets)
+    for (int it0 = 0; it0 < n; it0 += kRing)
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      const int it = it0 + u;
+      if (it >= n) break;                             // uniform
       {
         const int lc = min(kRing - 1, n - 1 - it), ls = min(it, kRing - 1);
         if (wave == 0) wait_page_sched<3, ST>(lc, ls);
@@ -241,19 +283,20 @@ __global__ __launch_bounds__(256, 3) void indexer_logits_kernel(IndexerLogitsArg
       }
       __syncthreads();
       if (active) {
-        const uint8_t* slot = sRing + (it % kRing) * kSlotBytes;
+        const uint8_t* slot = sRing + u * kSlotBytes;
         const float* scl = reinterpret_cast<const float*>(slot + kKeyPageCodes);
         const bool page_ok = sOk[it] != 0;
+        // per token block served: the head sum of each lane's 32 scores, its two head-block
+        // halves kept apart (halves the dependent FMA chain)
+        float xs[2 / G];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          if (nb % G != grp) continue;
-          const int tn = 32 * nb + (lane & 31);      // this lane's token in the page
+        for (int q = 0; q < 2 / G; ++q) {
+          const int nb = G == 1 ? q : grp;
           f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            const int lc = 4 * ks + 2 * (lane >> 5);
-            const u32x4 lo = *reinterpret_cast<const u32x4*>(slot + tn * kIdxDim + 16 * (lc ^ key_swz(tn)));
-            const u32x4 hi = *reinterpret_cast<const u32x4*>(slot + tn * kIdxDim + 16 * ((lc + 1) ^ key_swz(tn)));
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(slot + 32 * kIdxDim * nb + koff[ks][0]);
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(slot + 32 * kIdxDim * nb + koff[ks][1]);
             const i32x8 kb = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
@@ -261,8 +304,7 @@ __global__ __launch_bounds__(256, 3) void indexer_logits_kernel(IndexerLogitsArg
           }
           // ReLU as a signed-integer max on the bits (a negative float is a negative
           // integer, so it becomes +0; a non-negative one is unchanged): one instruction,
-          // where fmaxf costs two (its NaN-quieting canonicalization, then the max).  Two
-          // partial sums, one per head block, halve the dependent FMA chain.
+          // where fmaxf costs two (its NaN-quieting canonicalization, then the max)
           float part[2] = {0.f, 0.f};
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
@@ -271,15 +313,29 @@ __global__ __launch_bounds__(256, 3) void indexer_logits_kernel(IndexerLogitsArg
               const float r = __int_as_float(max(__float_as_int(acc[mb][j]), 0));
               part[mb] = __builtin_fmaf(wj[mb][j], r, part[mb]);
             }
-          const float logit = page_ok ? halves_sum(part[0] + part[1]) * scl[tn] : -INFINITY;
-          // lanes 32..63 hold the same sums: their offset is past any row, so they store nothing
-          const int t_rel = (p + it) * kKeyPage + tn;
-          const int off = lane < 32 ? 4 * t_rel : INT32_MAX - 3;
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(logit), out_rsrc, off, 0, 0);
+          xs[q] = part[0] + part[1];
         }
+        // The lane halves hold the other half of each token's heads.  Serving both blocks,
+        // one swap of block 0's upper lanes with block 1's lower lanes and one add leave
+        // block 0's logits in lanes 0..31 and block 1's in lanes 32..63: lane = token.
+        float tot;
+        int tok;
+        if constexpr (G == 1) {
+          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(xs[0]), __float_as_uint(xs[1]), false, false);
+          tot = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+          tok = lane;
+        } else {
+          tot = halves_sum(xs[0]);
+          tok = 32 * grp + (lane & 31);
+        }
+        const float logit = page_ok ? tot * scl[tok] : -INFINITY;
+        // with one block served, lanes 32..63 repeat lanes 0..31: their offset is past any
+        // row (2^31 and up), so they store nothing
+        const int off = (G == 1 ? 4 * lane : st_base[grp]) + 4 * kKeyPage * (p + it);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(logit), out_rsrc, off, 0, 0);
       }
       __syncthreads();
-      if (it + kRing < n) issue_page(it + kRing);
+      if (it + kRing < n) issue_page(it + kRing, u);
     }
     g += n;
     p += n;
