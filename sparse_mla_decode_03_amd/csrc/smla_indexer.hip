@@ -719,14 +719,25 @@ __global__ __launch_bounds__(kTopkThreads, 8) void indexer_topk_kernel(IndexerTo
       for (int w = w0; w < w1; ++w) cnt += __popc(sBits[w]);
       int tot;
       int at = block_excl_scan(cnt, sScan, tot);
+      // with K within the list's capacity the positions are staged in the list (no longer
+      // read) and leave in contiguous runs; otherwise each goes straight out
+      const bool stage = K <= kListCap + 1;         // block uniform
+      int* stg = reinterpret_cast<int*>(sKey);
       for (int w = w0; w < w1; ++w) {
         uint32_t m = sBits[w];
         while (m) {
           const int bit = __ffs(m) - 1;
-          if (at < K) out[at] = 32 * w + bit;
+          if (at < K) {
+            if (stage) stg[at] = 32 * w + bit;
+            else out[at] = 32 * w + bit;
+          }
           ++at;
           m &= m - 1u;
         }
+      }
+      if (stage) {
+        __syncthreads();
+        for (int j = tid; j < K; j += kTopkThreads) out[j] = stg[j];
       }
       return;
     }
