@@ -721,7 +721,7 @@ __global__ __launch_bounds__(kTopkThreads, 8) void indexer_topk_kernel(IndexerTo
       int at = block_excl_scan(cnt, sScan, tot);
       // with K within the list's capacity the positions are staged in the list (no longer
       // read) and leave in contiguous runs; otherwise each goes straight out
-      const bool stage = K <= kListCap + 1;         // block uniform
+      const bool stage = K <= kListCap;             // block uniform
       int* stg = reinterpret_cast<int*>(sKey);
       for (int w = w0; w < w1; ++w) {
         uint32_t m = sBits[w];

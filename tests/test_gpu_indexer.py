@@ -207,6 +207,11 @@ def test_topk_edges():
     four = torch.from_numpy(rng.integers(0, 4, (2, 20000)).astype(np.float32))
     four[1, ::50] = torch.from_numpy(10.0 + rng.standard_normal(400).astype(np.float32))
     _topk_case(four, torch.tensor([20000, 19999], dtype=torch.int32), 2048, "four values, ties in LDS")
+    # K at the kernel's staging capacity (6080 positions staged in LDS) and one past it
+    wide = torch.from_numpy(rng.standard_normal((2, 20000)).astype(np.float32))
+    wl = torch.tensor([20000, 13000], dtype=torch.int32)
+    _topk_case(wide, wl, 6080, "K = 6080")
+    _topk_case(wide, wl, 6081, "K = 6081")
 
 
 def test_topk_sample_misses_and_overflow():
