@@ -268,8 +268,8 @@ smla_status sparse_mla_cache_store(const void* latent, const void* rope, const i
  *   key_cache num_pages pages of 132*page_size bytes: codes e4m3fn [page_size][128], then
  *             fp32 scales [page_size]; scales must be >= 0 (quantization scales)
  *   row_len   int32 [R]; page_table int32 [num_requests][max_pages]
- *   logits    fp32 [R][width] (caller-owned, 16 B aligned); width a multiple of 64 and
- *             max_pages * 64 >= width
+ *   logits    fp32 [R][width] (caller-owned, 16 B aligned); width a multiple of 64,
+ *             at most 2^28 (a row's bytes stay below 2^31), and max_pages * 64 >= width
  * Supported: num_heads = 64, page_size = 64, next_n 1..4.  No allocation; asynchronous.
  * Errors: UNSUPPORTED, BAD_SHAPE, NULL_ARG, MISALIGNED, HIP. */
 smla_status sparse_mla_indexer_logits(const void* q_codes, const float* weights, const void* key_cache,

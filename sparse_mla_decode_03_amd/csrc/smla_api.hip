@@ -392,7 +392,8 @@ smla_status sparse_mla_indexer_logits(const void* q_codes, const float* weights,
                                       int32_t page_size, int32_t num_pages, int32_t max_pages,
                                       int32_t width, float* logits, void* stream) {
   if (num_heads != 64 || page_size != 64 || next_n < 1 || next_n > 4) return SMLA_ERR_UNSUPPORTED;
-  if (num_requests < 0 || num_pages < 1 || width < 64 || width % 64 != 0 || max_pages < width / 64 ||
+  if (num_requests < 0 || num_pages < 1 || width < 64 || width % 64 != 0 || width > (1 << 28) ||
+      max_pages < width / 64 ||
       (int64_t)num_requests * next_n > INT32_MAX / 64 || (int64_t)num_pages * page_size > INT32_MAX)
     return SMLA_ERR_BAD_SHAPE;
   if (num_requests == 0) return SMLA_OK;

@@ -238,6 +238,8 @@ def test_indexer_validation(lib):
     assert call(nn=5) == B.ERR_UNSUPPORTED and call(nn=0) == B.ERR_UNSUPPORTED
     assert call(width=500) == B.ERR_BAD_SHAPE and call(width=0) == B.ERR_BAD_SHAPE
     assert call(mp=7) == B.ERR_BAD_SHAPE            # the table must cover the width
+    # a row's bytes stay below 2^31: width at most 2^28 positions
+    assert call(width=(1 << 28) + 64, mp=(1 << 22) + 1) == B.ERR_BAD_SHAPE
     assert call(np=0) == B.ERR_BAD_SHAPE and call(B=-1) == B.ERR_BAD_SHAPE
     assert call(q=None) == B.ERR_NULL_ARG and call(out=None) == B.ERR_NULL_ARG
     assert call(w=v(FAKE + 4)) == B.ERR_MISALIGNED and call(len=v(FAKE + 2)) == B.ERR_MISALIGNED
