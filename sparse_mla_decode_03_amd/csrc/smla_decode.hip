@@ -841,10 +841,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     // Split partials for this library's own merge, in the accumulators' own layout: each
     // store is one 1 KB run (register group k of block b, all 64 lanes), with no LDS stage
     // and no normalization; beside them the head's reference max (log2 domain) and its
-    // probability sum, from which the merge forms the weights.
+    // probability sum, from which the merge forms the weights.  A split with no valid entry
+    // writes only its pairs (sum 0): the merge gives it no weight and never uses its runs.
     const size_t rs = (size_t)row * a.S + split;
     const int nwh = (a.H + 31) >> 5;
     float* base = a.part_o + (rs * nwh + wave) * (16 * 4 * 64 * 4) + 4 * lane_id;
+    if (n_valid > 0)   // block uniform
 #pragma unroll
     for (int b = 0; b < 16; ++b) {
       const f32x16 ob = kO15V && b == 15 ? O15 : O[ob_index(b)];

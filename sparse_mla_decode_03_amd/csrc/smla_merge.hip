@@ -116,22 +116,33 @@ __global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ po,
 //   M = max(max_c m_c, sigma), w_c = 2^(m_c - M),
 //   out = sum_c w_c O_c / (sum_c w_c l_c + 2^(sigma - M)),  lse = (M + log2 z) ln 2,
 // the same result as normalizing each chunk first; out is then multiplied by out_scale (the
-// per-tensor FP8 value scale, 1 otherwise).  One 64-lane wave per (row, head group, block);
-// each lane owns 16 outputs of one head.
-constexpr int kNatBatch = 8;      // splits whose runs are loaded together
-constexpr int kNatMl = 16;        // splits whose (m, l) pairs are loaded together
+// per-tensor FP8 value scale, 1 otherwise).  One wave merges one (row, head group, block),
+// each lane 16 outputs of one head.  NB splits' runs and NM splits' (m, l) pairs are loaded
+// together; the launch takes the smallest NB that covers S (up to 8), so a merge of few
+// splits holds few registers, and below 8 splits the runs of a split that is empty for all
+// of the wave's heads are not read.  STAGE (grids of many rows): one workgroup of four waves
+// per (row, head group, quarter of dv), whose bf16 results pass through LDS so that every
+// store writes whole 256-byte pieces of head rows (a wave's own 32 dv of 32 heads are
+// 64-byte pieces, half a cache line each); otherwise one single-wave workgroup per block,
+// which spreads a merge of few rows over more CUs.
+constexpr int kStagePitch = 272;   // bytes per head row of the stage: 128 dv + 16 bytes of pad
+constexpr int kStageMinGroups = 128;   // (row, head group) pairs from which the stage is used
 
-__global__ __launch_bounds__(64) void merge_native_kernel(const float* __restrict__ po,
-                                                          const float* __restrict__ pml, int R, int S,
-                                                          int H, const float* __restrict__ sinks,
-                                                          float out_scale, uint16_t* __restrict__ out,
-                                                          float* __restrict__ lse) {
+template <int NB, int NM, bool STAGE>
+__global__ __launch_bounds__(STAGE ? 256 : 64) void merge_native_kernel(
+    const float* __restrict__ po, const float* __restrict__ pml, int R, int S, int H,
+    const float* __restrict__ sinks, float out_scale, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(16))) uint8_t sStage[STAGE ? 32 * kStagePitch : 16];
   const int nwh = (H + 31) >> 5;
   const long long id = blockIdx.x;
-  const int b = (int)(id % 16);
-  const int g = (int)((id / 16) % nwh);
-  const int r = (int)(id / (16 * nwh));
-  const int lane = threadIdx.x;
+  constexpr int kPer = STAGE ? 4 : 16;               // workgroups per (row, head group)
+  const int part = (int)(id % kPer);
+  const int g = (int)((id / kPer) % nwh);
+  const int r = (int)(id / (kPer * nwh));
+  const int wave = STAGE ? (int)(threadIdx.x >> 6) : 0;
+  const int b = STAGE ? 4 * part + wave : part;
+  const int lane = threadIdx.x & 63;
   const int h = 32 * g + (lane & 31);
   const bool h_ok = h < H;
   const int hc = h_ok ? h : H - 1;                  // padded heads read a real head's pair
@@ -140,16 +151,17 @@ __global__ __launch_bounds__(64) void merge_native_kernel(const float* __restric
   const f32x2* ml = reinterpret_cast<const f32x2*>(pml) + (size_t)r * S * H + hc;
   const float* src0 = po + ((size_t)r * S * nwh + g) * (16 * 4 * 64 * 4) + b * (4 * 64 * 4) + 4 * lane;
   const size_t cstride = (size_t)nwh * (16 * 4 * 64 * 4);
-  // one memory round trip for the pairs of the first kNatMl splits and the runs of the
-  // first kNatBatch (all issued before any use; the runs do not depend on the weights)
-  f32x2 v[kNatMl];
-  f32x4 x[kNatBatch][4];
+  // one memory round trip for the pairs of the first NM splits and the runs of the first NB
+  // (all issued before any use; the runs do not depend on the weights)
+  static_assert(NM >= NB, "the first batch's weights come from the pairs loaded with it");
+  f32x2 v[NM];
+  f32x4 x[NB][4];
 #pragma unroll
-  for (int j = 0; j < kNatMl; ++j)
+  for (int j = 0; j < NM; ++j)
     if (j < S) v[j] = ml[(size_t)j * H];
 #pragma unroll
-  for (int j = 0; j < kNatBatch; ++j)
-    if (j < S) {
+  for (int j = 0; j < NB; ++j)
+    if (j < S && (NB > 4 || __ballot(v[j][1] > 0.f) != 0)) {
       const float* src = src0 + j * cstride;
 #pragma unroll
       for (int k = 0; k < 4; ++k) x[j][k] = *reinterpret_cast<const f32x4*>(src + k * (64 * 4));
@@ -158,12 +170,12 @@ __global__ __launch_bounds__(64) void merge_native_kernel(const float* __restric
   float M = sig2;
   bool any = false;                                  // a non-empty chunk
 #pragma unroll
-  for (int j = 0; j < kNatMl; ++j)
+  for (int j = 0; j < NM; ++j)
     if (j < S && v[j][1] > 0.f) {
       M = fmaxf(M, v[j][0]);
       any = true;
     }
-  for (int c0 = kNatMl; c0 < S; c0 += 16) {
+  for (int c0 = NM; c0 < S; c0 += 16) {
     f32x2 u[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j)
@@ -181,11 +193,11 @@ __global__ __launch_bounds__(64) void merge_native_kernel(const float* __restric
   float z = 0.f;
   if (any) {
     // pass 2: weights and the weighted sum; the first batch is already in registers
-    for (int c0 = 0; c0 < S; c0 += kNatBatch) {
-      f32x2 w2[kNatBatch];
+    for (int c0 = 0; c0 < S; c0 += NB) {
+      f32x2 w2[NB];
       if (c0 > 0) {
 #pragma unroll
-        for (int j = 0; j < kNatBatch; ++j) {
+        for (int j = 0; j < NB; ++j) {
           if (c0 + j < S) {
             w2[j] = ml[(size_t)(c0 + j) * H];
             const float* src = src0 + (c0 + j) * cstride;
@@ -195,10 +207,10 @@ __global__ __launch_bounds__(64) void merge_native_kernel(const float* __restric
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < kNatBatch; ++j) w2[j] = v[j];
+        for (int j = 0; j < NB; ++j) w2[j] = v[j];
       }
 #pragma unroll
-      for (int j = 0; j < kNatBatch; ++j) {
+      for (int j = 0; j < NB; ++j) {
         if (c0 + j < S && w2[j][1] > 0.f) {
           const float w = __builtin_amdgcn_exp2f(w2[j][0] - M);
           z += w * w2[j][1];
@@ -214,14 +226,36 @@ __global__ __launch_bounds__(64) void merge_native_kernel(const float* __restric
   // every chunk empty: z = 0, so out = 0 and the LSE is the sink itself (or -inf)
   const float inv = z > 0.f ? out_scale / z : 0.f;
   const float lse_v = z > 0.f ? (M + __log2f(z)) * kLn2 : sink;
-  if (h_ok) {
-    uint16_t* dst = out + ((size_t)r * H + h) * kV + 32 * b + 4 * (lane >> 5);
+  if constexpr (!STAGE) {
+    if (h_ok) {
+      uint16_t* dst = out + ((size_t)r * H + h) * kV + 32 * b + 4 * (lane >> 5);
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      *reinterpret_cast<u32x2*>(dst + 8 * k) =
-          u32x2{pack_bf16x2(acc[4 * k] * inv, acc[4 * k + 1] * inv),
-                pack_bf16x2(acc[4 * k + 2] * inv, acc[4 * k + 3] * inv)};
-    if (lse != nullptr && b == 0 && lane < 32) lse[(size_t)r * H + h] = lse_v;
+      for (int k = 0; k < 4; ++k)
+        *reinterpret_cast<u32x2*>(dst + 8 * k) =
+            u32x2{pack_bf16x2(acc[4 * k] * inv, acc[4 * k + 1] * inv),
+                  pack_bf16x2(acc[4 * k + 2] * inv, acc[4 * k + 3] * inv)};
+      if (lse != nullptr && b == 0 && lane < 32) lse[(size_t)r * H + h] = lse_v;
+    }
+    return;
+  }
+  // lane: head row lane % 32 of the stage, dv 32 * wave + 8k + 4 (lane / 32) + 0..3
+  uint8_t* srow = sStage + (lane & 31) * kStagePitch + 64 * wave + 8 * (lane >> 5);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    *reinterpret_cast<u32x2*>(srow + 16 * k) =
+        u32x2{pack_bf16x2(acc[4 * k] * inv, acc[4 * k + 1] * inv),
+              pack_bf16x2(acc[4 * k + 2] * inv, acc[4 * k + 3] * inv)};
+  if (h_ok && lse != nullptr && b == 0 && lane < 32) lse[(size_t)r * H + h] = lse_v;
+  __syncthreads();
+  // 32 heads x 256 bytes: thread t stores 16-byte pieces t and t + 256 (head piece / 16)
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    const int hr = c >> 4;
+    const int piece = c & 15;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(sStage + hr * kStagePitch + 16 * piece);
+    if (32 * g + hr < H)
+      *reinterpret_cast<u32x4*>(out + ((size_t)r * H + 32 * g + hr) * kV + 128 * part + 8 * piece) = v;
   }
 }
 
@@ -230,9 +264,28 @@ __global__ __launch_bounds__(64) void merge_native_kernel(const float* __restric
 hipError_t launch_merge_native(const float* part_o, const float* part_ml, int R, int S, int H,
                                const float* sinks, float out_scale, uint16_t* out, float* lse,
                                hipStream_t st) {
-  const long long blocks = (long long)R * ((H + 31) / 32) * 16;
-  hipLaunchKernelGGL(merge_native_kernel, dim3((unsigned)blocks), dim3(64), 0, st, part_o, part_ml, R,
-                     S, H, sinks, out_scale, out, lse);
+  // the staged layout once there are enough (row, head group) pairs to fill the chip with
+  // four-wave workgroups
+  const long long groups = (long long)R * ((H + 31) / 32);
+  const bool stage = groups >= kStageMinGroups;
+  const dim3 grid((unsigned)(groups * (stage ? 4 : 16)));
+  const dim3 block(stage ? 256 : 64);
+#define SMLA_MERGE_NATIVE(NB, NM)                                                                 \
+  do {                                                                                            \
+    if (stage)                                                                                    \
+      hipLaunchKernelGGL((merge_native_kernel<NB, NM, true>), grid, block, 0, st, part_o, part_ml, \
+                         R, S, H, sinks, out_scale, out, lse);                                    \
+    else                                                                                          \
+      hipLaunchKernelGGL((merge_native_kernel<NB, NM, false>), grid, block, 0, st, part_o,         \
+                         part_ml, R, S, H, sinks, out_scale, out, lse);                           \
+  } while (0)
+  if (S <= 2)
+    SMLA_MERGE_NATIVE(2, 2);
+  else if (S <= 4)
+    SMLA_MERGE_NATIVE(4, 4);
+  else
+    SMLA_MERGE_NATIVE(8, 16);
+#undef SMLA_MERGE_NATIVE
   return hipGetLastError();
 }
 

@@ -256,6 +256,24 @@ def test_merge_kernel_matches_oracle_merge(R, S, H):
     assert np.all(d <= np.abs(o) * 2.0 ** -8 + 1e-5), "merge: beyond one bf16 rounding of the oracle"
 
 
+# At least 128 (row, group of 32 heads) pairs: the merge of the decode's own split format
+# stages its bf16 results through LDS (four-wave workgroups); 16 and 48 heads pad the last
+# group.  Valid prefixes of 1..K entries leave the later chunks of short rows empty (their
+# runs are neither written nor read), and one row is empty altogether.
+@pytest.mark.parametrize("heads,splits", [(16, 2), (48, 3), (64, 5), (64, 2)])
+def test_merge_of_many_rows_with_empty_chunks(heads, splits):
+    inp = _small(heads=heads, topk=128, nreq=140, rows=(1,), ctx=(200, 600), valid="uniform",
+                 seed=41 + heads + splits)
+    assert inp.num_rows * ((heads + 31) // 32) >= 128
+    idx = inp.indices.clone()
+    idx[3] = -1
+    o, l = oracle_decode(inp, indices=idx)
+    announce(f"merge of many rows H={heads} S={splits}")
+    out, lse = gpu_decode(inp, indices=idx, num_splits=splits)
+    compare(out, lse, o, l, what=f"many rows H={heads} S={splits}")
+    assert torch.all(out[3] == 0) and torch.equal(lse[3].cpu(), inp.sinks)
+
+
 # ------------------------------------------------------------------ edge cases
 
 @pytest.mark.parametrize("splits", [0, 1, 2, 3])
