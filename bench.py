@@ -151,7 +151,7 @@ def workload_measure(B, W, torch, dev, name: str, seed: int, reps: int):
     R, H = inp.num_rows, inp.num_heads
     prob = B.make_problem(R, spec.num_requests, H, spec.topk, spec.page_size, inp.num_pages,
                           inp.page_table.shape[1], kv_code(B, spec.kv_format), B.IDX_LOGICAL,
-                          spec.num_splits, 0, spec.softmax_scale, spec.kv_scale)
+                          spec.num_splits, spec.flags, spec.softmax_scale, spec.kv_scale)
     info = B.plan(prob)
     out = torch.empty((R, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((R, H), dtype=torch.float32, device=dev)
@@ -498,7 +498,7 @@ def main() -> int:
     R, H, K = inp.num_rows, inp.num_heads, spec.topk
     kvf = kv_code(B, spec.kv_format)
     prob = B.make_problem(R, spec.num_requests, H, K, spec.page_size, inp.num_pages,
-                          inp.page_table.shape[1], kvf, B.IDX_LOGICAL, spec.num_splits, 0,
+                          inp.page_table.shape[1], kvf, B.IDX_LOGICAL, spec.num_splits, spec.flags,
                           spec.softmax_scale, spec.kv_scale)
     info = B.plan(prob)
     out = torch.empty((R, H, 512), dtype=torch.bfloat16, device=dev)
@@ -599,7 +599,7 @@ def main() -> int:
     slots = B.translate_indices(inp.indices, inp.row_req, inp.page_table, spec.page_size, inp.num_pages,
                                 stream=stream)
     gprob = B.make_problem(R, spec.num_requests, H, K, spec.page_size, inp.num_pages,
-                           inp.page_table.shape[1], kvf, B.IDX_GLOBAL, spec.num_splits, 0,
+                           inp.page_table.shape[1], kvf, B.IDX_GLOBAL, spec.num_splits, spec.flags,
                            spec.softmax_scale, spec.kv_scale)
     ginfo = B.plan(gprob)
 

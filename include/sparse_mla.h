@@ -123,7 +123,16 @@ enum {
    * output; out/lse are not written.  For callers that merge elsewhere. */
   SMLA_F_PARTIALS_ONLY = 1,
   /* Record the first out-of-range index in the workspace (see sparse_mla_read_index_error). */
-  SMLA_F_CHECK_INDICES = 2
+  SMLA_F_CHECK_INDICES = 2,
+  /* For batches whose rows hold very different numbers of entries (short contexts padded
+   * with -1): the run first counts each row's valid entries (those the decode keeps) and
+   * orders the rows by that count, longest first (two small launches, 8 bytes of workspace
+   * per row), then takes the rows in that order, and a split row's chunks hold equal
+   * numbers of its valid entries instead of equal ranges of positions.  The result is the
+   * same attention; the rounding of a split row may differ from the positional split
+   * (LOGICAL and GLOBAL mode over the same entries still agree bit for bit).  Not with
+   * SMLA_F_PARTIALS_ONLY (UNSUPPORTED): the documented partials are ranges of positions. */
+  SMLA_F_BALANCE_ROWS = 4
 };
 
 typedef struct {

@@ -36,6 +36,7 @@ IDX_LOGICAL = 0
 IDX_GLOBAL = 1
 F_PARTIALS_ONLY = 1
 F_CHECK_INDICES = 2
+F_BALANCE_ROWS = 4
 
 EXPORTED = [
     "sparse_mla_decode_plan", "sparse_mla_plan_num_splits", "sparse_mla_decode_run",

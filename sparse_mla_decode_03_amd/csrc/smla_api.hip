@@ -23,6 +23,7 @@ struct PlanImpl {
   uint64_t off_part_o;
   uint64_t off_part_lse;
   uint64_t off_err;
+  uint64_t off_balance;   // row counts [R], then the row order [R] (SMLA_F_BALANCE_ROWS)
   uint64_t ws_bytes;
 };
 static_assert(sizeof(PlanImpl) <= sizeof(smla_plan), "plan does not fit its opaque storage");
@@ -94,7 +95,10 @@ smla_status check_problem(const smla_problem* p) {
   if (p->kv_format != SMLA_KV_BF16 && p->kv_format != SMLA_KV_FP8_UE8M0 && p->kv_format != SMLA_KV_FP8_TENSOR)
     return SMLA_ERR_UNSUPPORTED;
   if (p->index_mode != SMLA_IDX_LOGICAL && p->index_mode != SMLA_IDX_GLOBAL) return SMLA_ERR_UNSUPPORTED;
-  if (p->flags & ~(SMLA_F_PARTIALS_ONLY | SMLA_F_CHECK_INDICES)) return SMLA_ERR_UNSUPPORTED;
+  if (p->flags & ~(SMLA_F_PARTIALS_ONLY | SMLA_F_CHECK_INDICES | SMLA_F_BALANCE_ROWS))
+    return SMLA_ERR_UNSUPPORTED;
+  // the documented partials are chunks of positions, which balancing would change
+  if ((p->flags & SMLA_F_BALANCE_ROWS) && (p->flags & SMLA_F_PARTIALS_ONLY)) return SMLA_ERR_UNSUPPORTED;
   const int l = log2_exact(p->page_size);
   if (p->page_size < 1 || p->page_size > 1024 || l < 0) return SMLA_ERR_BAD_SHAPE;
   // FP8 pages are 648 * page_size bytes; the 16-byte copies need an even page size
@@ -186,6 +190,10 @@ smla_status sparse_mla_decode_plan(const smla_problem* p, int32_t num_cus, smla_
   if (p->flags & SMLA_F_CHECK_INDICES) {
     pi.off_err = off;
     off = round_up(off + sizeof(unsigned long long), 256);
+  }
+  if (p->flags & SMLA_F_BALANCE_ROWS) {
+    pi.off_balance = off;
+    off = round_up(off + 2 * (uint64_t)p->num_rows * sizeof(int32_t), 256);
   }
   pi.ws_bytes = off;
   memset(plan, 0, sizeof(*plan));
@@ -279,6 +287,13 @@ smla_status run_impl(const PlanImpl* pi, const void* q, const void* kv_cache, co
     a.write_partials = 0;
     a.out = reinterpret_cast<uint16_t*>(out);
     a.lse = lse;
+  }
+  if (p.flags & SMLA_F_BALANCE_ROWS) {
+    int32_t* counts = reinterpret_cast<int32_t*>(ws + pi->off_balance);
+    int32_t* order = counts + p.num_rows;
+    if (smla::launch_balance(a, counts, order, st) != hipSuccess) return SMLA_ERR_HIP;
+    a.row_count = counts;
+    a.row_order = order;
   }
   if (smla::launch_decode(a, p.kv_format, st) != hipSuccess) return SMLA_ERR_HIP;
   if (merge) {

@@ -120,9 +120,10 @@ struct Cfg {
 };
 
 // NATIVE: the epilogue writes split partials in the merge's own format (write_partials 2)
-// and nothing else; otherwise it writes the output or the documented partials.  Two
-// instantiations, so neither epilogue changes the other's register allocation.
-template <int NW, int FMT, bool NATIVE>
+// and nothing else; otherwise it writes the output or the documented partials.  BAL: the
+// balanced order and rank-window splits (row_order set).  Separate instantiations, so that
+// neither epilogue nor the balanced set-up changes another variant's register allocation.
+template <int NW, int FMT, bool NATIVE, bool BAL>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   using C = Cfg<NW, FMT>;
   // load_slots(tile) reads up to index (tile + 1) * kT + kT - 1 (the scale copy of the next
@@ -142,10 +143,38 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // wave-uniform, in an SGPR; the clamp tells the compiler its range
   const int wave = NW == 4 ? (int)((unsigned)__builtin_amdgcn_readfirstlane(tid >> 6) & 3u)
                            : __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int row = blockIdx.x;
-  const int split = blockIdx.y;
-  const int p0 = split * a.chunk;
-  const int p1 = min(p0 + a.chunk, a.K);
+  // Work item.  Positional splits: row blockIdx.x, positions [split * chunk, +chunk).
+  // Balanced (row_order set): the dispatch index picks a (job, split) pair, jobs being rows
+  // longest first, so the longest rows start first and short ones fill the tail; the splits
+  // of a job take equal shares of the row's entries by rank (the last one takes the rest),
+  // and a group of eight jobs sends all its splits to the same eight dispatch slots mod 8
+  // (the same XCDs, whose L2s then serve the row's q and index list to its other splits).
+  int row, split, p0, p1;
+  int lo = 0, hi = INT_MAX;   // ranks of the valid entries this split keeps
+  if constexpr (BAL) {
+    const int L = blockIdx.x + blockIdx.y * gridDim.x;
+    const int full = (a.R >> 3) * 8 * a.S;
+    int j;
+    if (L < full) {
+      const int rem = L % (8 * a.S);
+      j = 8 * (L / (8 * a.S)) + (rem & 7);
+      split = rem >> 3;
+    } else {
+      j = 8 * (a.R >> 3) + (L - full) / a.S;
+      split = (L - full) % a.S;
+    }
+    row = min(max(a.row_order[j], 0), a.R - 1);   // the clamps keep any count or order in bounds
+    const int n = min(max(a.row_count[row], 0), a.K);
+    lo = (int)((long long)split * n / a.S);
+    if (split < a.S - 1) hi = (int)((long long)(split + 1) * n / a.S);
+    p0 = 0;
+    p1 = a.K;
+  } else {
+    row = blockIdx.x;
+    split = blockIdx.y;
+    p0 = split * a.chunk;
+    p1 = min(p0 + a.chunk, a.K);
+  }
   const int ps_mask = (1 << a.ps_log2) - 1;
   if (tid == 0) sRestart = 0;
 
@@ -271,12 +300,20 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       }
       const int before = __builtin_amdgcn_mbcnt_hi((unsigned)(m[i] >> 32),
                                                    __builtin_amdgcn_mbcnt_lo((unsigned)m[i], 0u));
-      if (ok[i]) sSlots[off + before_w + before] = slot[i];
+      if constexpr (BAL) {
+        // the split's rank window; the slot list bound holds whatever the counts say
+        const int at = off + before_w + before - lo;
+        if (ok[i] && at >= 0 && at < hi - lo && at < kCMax) sSlots[at] = slot[i];
+      } else {
+        if (ok[i]) sSlots[off + before_w + before] = slot[i];
+      }
       off += tot;
     }
     n_valid = off;
     __syncthreads();
+    if (BAL && off >= hi) break;     // block uniform: the split's share is complete
   }
+  if constexpr (BAL) n_valid = min(max(n_valid - lo, 0), min(hi - lo, kCMax));
   // Positions past the valid count repeat the split's first valid slot, so the copies of
   // the last tile and of the tiles past the end need no per-lane selection and bring in
   // finite data (a valid entry of this very split) that meets a masked score, P = 0.
@@ -981,16 +1018,97 @@ __global__ __launch_bounds__(256) void gather_debug_kernel(const uint8_t* __rest
   *reinterpret_cast<u32x4*>(out + e * kQK + 8 * c) = v;
 }
 
+// ---- balanced splits: entry counts per row and a longest-first row order ------------------
+constexpr int kOrderBins = 1024;   // classes of the order: 32 entries (one tile) each, the last open
+
+// One wave per row: the number of entries the decode keeps, by the same test as its
+// translation (an id >= 0 that names a slot of the pool, through the page table in LOGICAL
+// mode), so that the ranks of a balanced split are those of the decode's own list.
+__global__ __launch_bounds__(256) void count_rows_kernel(DecodeArgs a, int32_t* __restrict__ counts) {
+  const int lane = threadIdx.x & 63;
+  const int row = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (row >= a.R) return;
+  const int* pt = nullptr;
+  bool req_ok = true;
+  if (a.index_mode == 0) {
+    const int req = a.row_req[row];
+    req_ok = req >= 0 && req < a.B;
+    pt = a.page_table + (size_t)(req_ok ? req : 0) * a.max_pages;
+  }
+  const u32x4* p = reinterpret_cast<const u32x4*>(a.indices + (size_t)row * a.K);
+  const int n4 = a.K >> 2;
+  int c = 0;
+#pragma unroll 4
+  for (int i = lane; i < n4; i += 64) {
+    const u32x4 v = p[i];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int t = (int)v[k];
+      bool ok;
+      if (a.index_mode == 0) {
+        ok = req_ok && t >= 0 && (t >> a.ps_log2) < a.max_pages;
+        const int pg = ok ? pt[t >> a.ps_log2] : -1;
+        ok = ok && pg >= 0 && pg < a.num_pages;
+      } else {
+        ok = t >= 0 && t < a.num_slots;
+      }
+      c += ok ? 1 : 0;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
+  if (lane == 0) counts[row] = c;
+}
+
+// One workgroup: a counting sort of the rows by tiles of entries, most first (rows of one
+// class in no particular order; the decode's results do not depend on it).
+__global__ __launch_bounds__(1024) void order_rows_kernel(const int32_t* __restrict__ counts, int R,
+                                                          int32_t* __restrict__ order) {
+  __shared__ int sStart[kOrderBins];
+  __shared__ int sWave[16];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  sStart[tid] = 0;
+  __syncthreads();
+  auto cls = [](int c) { return min((max(c, 0) + 31) >> 5, kOrderBins - 1); };
+  for (int r = tid; r < R; r += 1024) atomicAdd(&sStart[cls(counts[r])], 1);
+  __syncthreads();
+  // exclusive prefix over the classes in descending order: thread t takes class 1023 - t
+  const int v = sStart[kOrderBins - 1 - tid];
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(inc, off);
+    if (lane >= off) inc += u;
+  }
+  if (lane == 63) sWave[wave] = inc;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += sWave[w];
+  sStart[kOrderBins - 1 - tid] = before + inc - v;
+  __syncthreads();
+  for (int r = tid; r < R; r += 1024) order[atomicAdd(&sStart[cls(counts[r])], 1)] = r;
+}
+
 __global__ void fill_u64_kernel(unsigned long long* p, unsigned long long v) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *p = v;
 }
 
 template <int NW, int FMT>
 hipError_t launch_nw(const DecodeArgs& a, hipStream_t st) {
-  if (a.write_partials == 2)
-    hipLaunchKernelGGL((decode_kernel<NW, FMT, true>), dim3(a.R, a.S), dim3(NW * 64), 0, st, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<NW, FMT, false>), dim3(a.R, a.S), dim3(NW * 64), 0, st, a);
+  const dim3 grid(a.R, a.S), block(NW * 64);
+  if (a.row_order != nullptr) {
+    if (a.write_partials == 2)
+      hipLaunchKernelGGL((decode_kernel<NW, FMT, true, true>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<NW, FMT, false, true>), grid, block, 0, st, a);
+  } else {
+    if (a.write_partials == 2)
+      hipLaunchKernelGGL((decode_kernel<NW, FMT, true, false>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<NW, FMT, false, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 
@@ -1031,6 +1149,12 @@ hipError_t launch_gather_debug(const uint8_t* kv, int kv_format, int ps_log2, in
   else
     hipLaunchKernelGGL(gather_debug_kernel<0>, dim3(blocks), dim3(256), 0, st, kv, ps_log2, num_slots,
                        slots, n, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_balance(const DecodeArgs& a, int32_t* counts, int32_t* order, hipStream_t st) {
+  hipLaunchKernelGGL(count_rows_kernel, dim3((unsigned)((a.R + 3) / 4)), dim3(256), 0, st, a, counts);
+  hipLaunchKernelGGL(order_rows_kernel, dim3(1), dim3(1024), 0, st, counts, a.R, order);
   return hipGetLastError();
 }
 

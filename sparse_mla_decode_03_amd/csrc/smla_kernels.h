@@ -18,6 +18,8 @@ struct DecodeArgs {
   float* part_o;                // [R][S][H][512]        (partial mode)
   float* part_lse;              // [R][S][H]             (partial mode)
   unsigned long long* err;      // first bad (row << 32 | pos), or null
+  const int32_t* row_order;     // [R] rows longest first (balanced splits), or null
+  const int32_t* row_count;     // [R] entries the decode keeps per row (balanced splits)
   int32_t R, H, K, S, chunk, B;
   int32_t ps_log2, num_pages, num_slots, max_pages, index_mode;
   int32_t write_partials;       // 0 final output, 1 documented partials, 2 the merge's own format
@@ -47,6 +49,9 @@ struct IndexerTopkArgs {
 
 int max_chunk_positions();
 hipError_t launch_decode(const DecodeArgs& a, int kv_format, hipStream_t st);
+// Balanced splits: count each row's entries that the decode with these arguments keeps into
+// counts[R] and order the rows by their count, longest first, into order[R].
+hipError_t launch_balance(const DecodeArgs& a, int32_t* counts, int32_t* order, hipStream_t st);
 hipError_t launch_merge(const float* part_o, const float* part_lse, int R, int S, int H,
                         const float* sinks, uint16_t* out, float* lse, hipStream_t st);
 // Merge of the decode's own split format (DecodeArgs.write_partials == 2): part_o holds,

@@ -73,6 +73,7 @@ class WorkloadSpec:
     softmax_scale: float = 1.0 / math.sqrt(576.0)
     causal: bool = False             # row i of n rows draws from positions < ctx - n + 1 + i
     kv_scale: float = 1.0            # per-tensor FP8: the cache's one scale
+    flags: int = 0                   # run flags that suit the batch (4: balanced rows)
 
     def scaled(self, **kw) -> "WorkloadSpec":
         return dataclasses.replace(self, **kw)
@@ -88,7 +89,7 @@ WORKLOADS = {
                                          131072, KV_BF16, num_splits=16),
     "ragged_b256_h64_fp8": WorkloadSpec("ragged_b256_h64_fp8", 256, (1, 2, 4), 64, 2048, 4096,
                                         4096, KV_FP8, valid="uniform", sinks="half_neg_inf",
-                                        shared_frac=0.1),
+                                        shared_frac=0.1, flags=4),
     # prefill chunks and decode rows in one launch: requests with 1, 4 or 256 query rows,
     # each row with its own causal top-k list
     # the headline shape over the contiguous per-tensor FP8 cache

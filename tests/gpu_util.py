@@ -29,7 +29,7 @@ def q_bits(q: torch.Tensor) -> np.ndarray:
     return q.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-def gpu_decode(inp: W.Inputs, num_splits=None, flags=0, index_mode=B.IDX_LOGICAL, indices=None,
+def gpu_decode(inp: W.Inputs, num_splits=None, flags=None, index_mode=B.IDX_LOGICAL, indices=None,
                sinks="same", page_table=None, kv_cache=None, return_info=False):
     dev = torch.device("cuda")
     g = lambda t: None if t is None else t.to(dev).contiguous()  # noqa: E731
@@ -39,7 +39,8 @@ def gpu_decode(inp: W.Inputs, num_splits=None, flags=0, index_mode=B.IDX_LOGICAL
         g(inp.indices if indices is None else indices), g(inp.row_req),
         g(inp.page_table if page_table is None else page_table), g(s), inp.spec.kv_format,
         inp.spec.page_size, inp.spec.softmax_scale, index_mode=index_mode,
-        num_splits=inp.spec.num_splits if num_splits is None else num_splits, flags=flags,
+        num_splits=inp.spec.num_splits if num_splits is None else num_splits,
+        flags=inp.spec.flags if flags is None else flags,
         return_info=return_info, kv_scale=inp.spec.kv_scale)
 
 

@@ -37,6 +37,8 @@ def setup(lib):
     lib.smla_hostcheck_last_merge.argtypes = [ctypes.POINTER(ctypes.c_int32 * 3),
                                               ctypes.POINTER(ctypes.c_uint64 * 2)]
     lib.smla_hostcheck_last_merge_scale.restype = ctypes.c_float
+    lib.smla_hostcheck_last_balance.argtypes = [ctypes.POINTER(ctypes.c_int32 * 2),
+                                                ctypes.POINTER(ctypes.c_uint64 * 5)]
 
 
 def counts(lib):
@@ -52,6 +54,12 @@ def last_decode(lib):
     d["scale_log2"], d["out_scale"] = f[0], f[1]
     d.update(zip(["q", "kv", "idx", "rr", "pt", "sinks", "out", "lse", "po", "pl", "err"], list(p)))
     return d
+
+
+def last_balance(lib):
+    i, p = (ctypes.c_int32 * 2)(), (ctypes.c_uint64 * 5)()
+    lib.smla_hostcheck_last_balance(ctypes.byref(i), ctypes.byref(p))
+    return list(i), list(p)
 
 
 def last_merge(lib):
@@ -191,6 +199,36 @@ def check_noalloc(lib):
     assert st == B.OK and counts(lib) == [1, 0, 0, 0, 0, 0, 0, 0, 0] and last_decode(lib)["out"] == P["out"]
 
 
+def check_balance_rows(lib):
+    lib.smla_hostcheck_reset()
+    R, S, H = 600, 2, 64
+    # the row counts and the order follow the split partials in the workspace
+    pl, ws = plan(lib, prob(num_rows=R, num_requests=R, num_heads=H, num_splits=S, flags=B.F_BALANCE_ROWS))
+    parts = round_up(R * S * H * 512 * 4, 256) + round_up(R * S * H * 8, 256)
+    assert ws == parts + round_up(2 * R * 4, 256)
+    assert run(lib, pl, ws=W, wsb=ws) == B.OK
+    assert lib.smla_hostcheck_launches(9) == 1 and counts(lib) == [1, 0, 0, 0, 0, 0, 0, 0, 1]
+    (br, bk), (bidx, bc, bo, dc, do) = last_balance(lib)
+    assert (br, bk) == (R, 2048) and bidx == P["idx"]
+    assert bc == W + parts and bo == bc + 4 * R and (dc, do) == (bc, bo)
+    # unsplit: the order alone, in a workspace of its own
+    lib.smla_hostcheck_reset()
+    pl, ws = plan(lib, prob(num_rows=R, num_requests=R, num_splits=1, flags=B.F_BALANCE_ROWS))
+    assert ws == round_up(2 * R * 4, 256)
+    assert run(lib, pl, ws=W, wsb=ws) == B.OK
+    assert lib.smla_hostcheck_launches(9) == 1 and last_decode(lib)["out"] == P["out"]
+    assert last_balance(lib)[1][3:] == [W, W + 4 * R]
+    # without the flag the decode gets no order
+    lib.smla_hostcheck_reset()
+    pl, ws = plan(lib, prob(num_rows=R, num_requests=R, num_splits=1))
+    assert run(lib, pl) == B.OK and lib.smla_hostcheck_launches(9) == 0
+    assert last_balance(lib)[1][3:] == [0, 0]
+    # balancing changes the positional chunks the documented partials are defined by
+    pr = prob(num_rows=4, num_requests=4, num_splits=2, flags=B.F_BALANCE_ROWS | B.F_PARTIALS_ONLY)
+    pl_, wsb = B.Plan(), ctypes.c_size_t(0)
+    assert lib.sparse_mla_decode_plan(ctypes.byref(pr), 256, ctypes.byref(pl_), ctypes.byref(wsb)) == B.ERR_UNSUPPORTED
+
+
 def check_planner_cu_count(lib):
     # num_cus <= 0 asks the runtime (the stand-in reports 304 CUs): 32 rows -> ceil(304 / 32)
     lib.smla_hostcheck_set_cus(304)
@@ -223,8 +261,8 @@ def main(path):
     lib = B.load_library(path)
     setup(lib)
     checks = [check_unsplit, check_split_merge, check_partials_only, check_index_check,
-              check_tensor_fp8_scales, check_global_mode, check_noalloc, check_planner_cu_count,
-              check_other_entry_points]
+              check_tensor_fp8_scales, check_global_mode, check_noalloc, check_balance_rows,
+              check_planner_cu_count, check_other_entry_points]
     for c in checks:
         c(lib)
         print("ok", c.__name__, flush=True)

@@ -19,7 +19,8 @@
 
 namespace {
 
-enum Kind { kDecode, kMerge, kGather, kFill, kStore, kLogits, kTopk, kTranslate, kMergeNative, kKinds };
+enum Kind { kDecode, kMerge, kGather, kFill, kStore, kLogits, kTopk, kTranslate, kMergeNative, kBalance,
+            kKinds };
 
 int g_counts[kKinds];
 smla::DecodeArgs g_last_decode;
@@ -28,6 +29,8 @@ int g_last_merge[3];             // R, S, H
 const void* g_last_merge_ptrs[2];  // part_o, part_lse
 int g_cus = 256;
 float g_last_merge_scale = 0.f;
+int g_last_balance[2];               // R, K
+const void* g_last_balance_ptrs[3];  // indices, counts, order
 unsigned char g_fatbin_stand_in[16];
 
 // Where the stand-in hipGetSymbolAddress says the scratch array lives: an address that
@@ -65,6 +68,15 @@ hipError_t launch_merge_native(const float* part_o, const float* part_ml, int R,
   g_last_merge[2] = H;
   g_last_merge_ptrs[0] = part_o;
   g_last_merge_ptrs[1] = part_ml;
+  return hipSuccess;
+}
+hipError_t launch_balance(const DecodeArgs& a, int32_t* counts, int32_t* order, hipStream_t) {
+  ++g_counts[kBalance];
+  g_last_balance[0] = a.R;
+  g_last_balance[1] = a.K;
+  g_last_balance_ptrs[0] = a.indices;
+  g_last_balance_ptrs[1] = counts;
+  g_last_balance_ptrs[2] = order;
   return hipSuccess;
 }
 hipError_t launch_gather_debug(const uint8_t*, int, int, int, const int*, int, uint16_t*, hipStream_t) {
@@ -132,11 +144,14 @@ void smla_hostcheck_reset() {
   g_last_decode_format = -1;
   std::memset(g_last_merge, 0, sizeof(g_last_merge));
   g_last_merge_ptrs[0] = g_last_merge_ptrs[1] = nullptr;
+  std::memset(g_last_balance, 0, sizeof(g_last_balance));
+  g_last_balance_ptrs[0] = g_last_balance_ptrs[1] = g_last_balance_ptrs[2] = nullptr;
 }
 void smla_hostcheck_set_cus(int n) { g_cus = n; }
 float smla_hostcheck_last_merge_scale() { return g_last_merge_scale; }
 // Launch counts by kind: 0 decode, 1 merge (documented partials), 2 gather_debug, 3 fill,
-// 4 store, 5 indexer logits, 6 indexer top-k, 7 translate, 8 merge of the decode's own format.
+// 4 store, 5 indexer logits, 6 indexer top-k, 7 translate, 8 merge of the decode's own format,
+// 9 row count and order (balanced splits).
 int smla_hostcheck_launches(int kind) { return kind >= 0 && kind < kKinds ? g_counts[kind] : -1; }
 uintptr_t smla_hostcheck_fake_scratch() { return kFakeScratch; }
 // The last decode launch: ints = R, H, K, S, chunk, B, ps_log2, num_pages, num_slots,
@@ -152,6 +167,14 @@ void smla_hostcheck_last_decode(int32_t* ints, float* floats, uintptr_t* ptrs) {
   const void* pv[11] = {a.q, a.kv, a.indices, a.row_req, a.page_table, a.sinks,
                         a.out, a.lse, a.part_o, a.part_lse, a.err};
   for (int i = 0; i < 11; ++i) ptrs[i] = reinterpret_cast<uintptr_t>(pv[i]);
+}
+// The last balance launch: ints = R, K; ptrs = indices, counts, order, then the last decode
+// launch's row_count and row_order.
+void smla_hostcheck_last_balance(int32_t* ints, uintptr_t* ptrs) {
+  std::memcpy(ints, g_last_balance, sizeof(g_last_balance));
+  for (int i = 0; i < 3; ++i) ptrs[i] = reinterpret_cast<uintptr_t>(g_last_balance_ptrs[i]);
+  ptrs[3] = reinterpret_cast<uintptr_t>(g_last_decode.row_count);
+  ptrs[4] = reinterpret_cast<uintptr_t>(g_last_decode.row_order);
 }
 // The last merge launch (either kind): ints = R, S, H; ptrs = part_o, part_lse or part_ml.
 void smla_hostcheck_last_merge(int32_t* ints, uintptr_t* ptrs) {

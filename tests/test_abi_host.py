@@ -84,6 +84,7 @@ def _plan_status(lib, prob, cus=256):
     (dict(kv_format=7), B.ERR_UNSUPPORTED),
     (dict(index_mode=3), B.ERR_UNSUPPORTED),
     (dict(flags=8), B.ERR_UNSUPPORTED),
+    (dict(flags=B.F_BALANCE_ROWS | B.F_PARTIALS_ONLY, num_splits=2), B.ERR_UNSUPPORTED),
     (dict(num_requests=0), B.ERR_BAD_SHAPE),
     (dict(max_pages_per_req=0), B.ERR_BAD_SHAPE),
     (dict(num_splits=-2), B.ERR_BAD_SHAPE),
@@ -130,6 +131,10 @@ def test_plan_splits_and_workspace(lib):
     # index checking needs one word
     st, p, ws = _plan_status(lib, _prob(num_rows=512, flags=B.F_CHECK_INDICES))
     assert st == B.OK and ws == 256
+    # balanced rows: a count and an order slot per row (the header's flag value is the binding's)
+    st, p, ws = _plan_status(lib, _prob(num_rows=600, num_splits=1, flags=B.F_BALANCE_ROWS))
+    assert st == B.OK and ws == 4864
+    assert "SMLA_F_BALANCE_ROWS = 4" in open(HEADER).read() and B.F_BALANCE_ROWS == 4
     # plans are data independent and deterministic
     a = _plan_status(lib, _prob(num_rows=32))
     b = _plan_status(lib, _prob(num_rows=32))

@@ -274,6 +274,58 @@ def test_merge_of_many_rows_with_empty_chunks(heads, splits):
     assert torch.all(out[3] == 0) and torch.equal(lse[3].cpu(), inp.sinks)
 
 
+# Balanced rows: the rows are counted and ordered on the device, and a split row's chunks
+# take equal numbers of its entries.  Ragged valid prefixes, an empty row, a row whose first
+# half is -1, and out-of-range indices (not counted: the count applies the translation's own
+# test, so the shares partition exactly the entries the decode keeps).
+@pytest.mark.parametrize("heads,splits", [(64, 1), (64, 2), (128, 3), (16, 5)])
+def test_balanced_rows_match_oracle(heads, splits):
+    inp = _small(heads=heads, topk=256, nreq=140, rows=(1,), ctx=(200, 600), valid="uniform",
+                 seed=61 + heads + splits)
+    idx = inp.indices.clone()
+    idx[5] = -1
+    idx[6, :128] = -1
+    ctx = inp.context_lens.long()
+    rng = np.random.default_rng(3)
+    for r in rng.choice(inp.num_rows, size=20, replace=False):
+        n = int((idx[r] >= 0).sum())
+        if n > 2:
+            pos = rng.choice(n, size=min(3, n), replace=False)
+            idx[r, pos] = int(inp.page_table.shape[1]) * inp.spec.page_size + 7 + int(ctx[r])
+    o, l = oracle_decode(inp, indices=idx)
+    announce(f"balanced rows H={heads} S={splits}")
+    out, lse, info, _ = gpu_decode(inp, indices=idx, num_splits=splits, flags=B.F_BALANCE_ROWS,
+                                   return_info=True)
+    assert info.num_splits == splits
+    compare(out, lse, o, l, what=f"balanced H={heads} S={splits}")
+    assert torch.all(out[5] == 0) and torch.equal(lse[5].cpu(), inp.sinks)
+    # the same attention as the positional split
+    out2, lse2 = gpu_decode(inp, indices=idx, num_splits=splits)
+    assert (out.float() - out2.float()).abs().max().item() <= 2e-2
+
+
+def test_balanced_rows_above_one_workgroup_and_global_slots():
+    # K = 5000 needs at least three splits; GLOBAL mode takes the slots as they are
+    inp = _small(heads=64, topk=5000, nreq=3, rows=(1, 2), ctx=(6000, 9000), valid="uniform", seed=67)
+    idx = inp.indices.clone()
+    idx[0, :2600] = -1
+    o, l = oracle_decode(inp, indices=idx)
+    announce("balanced rows K=5000")
+    out, lse, info, _ = gpu_decode(inp, indices=idx, num_splits=0, flags=B.F_BALANCE_ROWS,
+                                   return_info=True)
+    assert info.num_splits >= 3
+    compare(out, lse, o, l, what="balanced K=5000")
+    ps = inp.spec.page_size
+    pt = inp.page_table.long()
+    valid = idx >= 0
+    req = inp.row_req.long()[:, None].expand_as(idx)
+    slots = pt[req, (idx.clamp(min=0) // ps).long()] * ps + idx.clamp(min=0) % ps
+    gidx = torch.where(valid, slots, torch.full_like(idx, -1)).int()
+    out_g, lse_g = gpu_decode(inp, indices=gidx, index_mode=B.IDX_GLOBAL, num_splits=0,
+                              flags=B.F_BALANCE_ROWS)
+    assert torch.equal(out_g, out) and torch.equal(lse_g, lse)
+
+
 # ------------------------------------------------------------------ edge cases
 
 @pytest.mark.parametrize("splits", [0, 1, 2, 3])
