@@ -141,6 +141,10 @@ int choose_splits(const smla_problem* p, int num_cus) {
     if (want > s) s = want;
   } else {
     const int64_t slots = (int64_t)num_cus * ((p->num_heads + 31) / 32 <= 2 ? 2 : 1);
+    // balanced rows with a row per workgroup slot: the longest-first order already evens out
+    // the slots, so a split would only add its partials and merge (627 ragged rows of 64
+    // heads: 0.213 ms unsplit against 0.217 ms at two splits)
+    if ((p->flags & SMLA_F_BALANCE_ROWS) && rows >= slots) return s;
     auto cost = [&](int c) {
       const int64_t rounds = (rows * c + slots - 1) / slots;
       return rounds * ((p->topk + c - 1) / c + kSplitOverhead);
