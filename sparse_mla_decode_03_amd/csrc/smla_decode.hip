@@ -152,16 +152,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   int row, split, p0, p1;
   int lo = 0, hi = INT_MAX;   // ranks of the valid entries this split keeps
   if constexpr (BAL) {
-    const int L = blockIdx.x + blockIdx.y * gridDim.x;
-    const int full = (a.R >> 3) * 8 * a.S;
+    const long long L = blockIdx.x + (long long)blockIdx.y * gridDim.x;
+    const long long full = (long long)(a.R >> 3) * 8 * a.S;
     int j;
     if (L < full) {
-      const int rem = L % (8 * a.S);
-      j = 8 * (L / (8 * a.S)) + (rem & 7);
+      const int rem = (int)(L % (8 * a.S));
+      j = (int)(8 * (L / (8 * a.S))) + (rem & 7);
       split = rem >> 3;
     } else {
-      j = 8 * (a.R >> 3) + (L - full) / a.S;
-      split = (L - full) % a.S;
+      j = 8 * (a.R >> 3) + (int)((L - full) / a.S);
+      split = (int)((L - full) % a.S);
     }
     row = min(max(a.row_order[j], 0), a.R - 1);   // the clamps keep any count or order in bounds
     const int n = min(max(a.row_count[row], 0), a.K);
