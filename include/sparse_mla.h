@@ -212,7 +212,8 @@ smla_status sparse_mla_decode_run(const smla_plan* plan, const void* q, const vo
 
 /* The same decode as sparse_mla_decode_run, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): it
- * takes no workspace.  A split plan's fp32 partials go to scratch the library holds, one
+ * takes no workspace.  A split plan's fp32 partials (and a balanced plan's row counts and
+ * order, SMLA_F_BALANCE_ROWS) go to scratch the library holds, one
  * SMLA_NOALLOC_SCRATCH_BYTES array per GPU in the library's own device memory, reserved
  * when the library is loaded and kept until the process ends; no call allocates or frees
  * anything.  Arguments as for sparse_mla_decode_run, without partial_o, partial_lse and

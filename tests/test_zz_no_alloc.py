@@ -1,7 +1,7 @@
 """The allocation-free entry point (sparse_mla_decode_run_noalloc) against sparse_mla_decode_run
-on the GPU: split plans (partials in the library's per-GPU scratch) and an unsplit one, two
-calls in a row with the second smaller, the first call again after the second, and every
-result also against the float64 oracle at the usual tolerance."""
+on the GPU: split plans (partials in the library's per-GPU scratch), an unsplit one and
+balanced rows, two calls in a row with the second smaller, the first call again after the
+second, and every result also against the float64 oracle at the usual tolerance."""
 
 from __future__ import annotations
 
@@ -18,14 +18,14 @@ pytestmark = [pytest.mark.gpu,
 DEV = torch.device("cuda")
 
 
-def _case(fmt, heads, topk, nreq, rows, splits, seed):
+def _case(fmt, heads, topk, nreq, rows, splits, seed, flags=0):
     spec = W.WorkloadSpec("noalloc", nreq, rows, heads, topk, topk + 100, 3 * topk, fmt,
                           num_splits=splits, valid="uniform")
     inp = W.make_inputs(spec, seed)
     g = inp.to(DEV)
     kvf = {"fp8": B.KV_FP8_UE8M0, "bf16": B.KV_BF16}[fmt]
     prob = B.make_problem(inp.num_rows, nreq, heads, topk, spec.page_size, inp.num_pages,
-                          inp.page_table.shape[1], kvf, B.IDX_LOGICAL, splits, 0, spec.softmax_scale)
+                          inp.page_table.shape[1], kvf, B.IDX_LOGICAL, splits, flags, spec.softmax_scale)
     info = B.plan(prob)
     return inp, g, info
 
@@ -69,3 +69,19 @@ def test_noalloc_unsplit_plan_needs_no_scratch():
     out_ws, lse_ws, out_na, lse_na = _both(inp, g, info)
     assert torch.equal(out_na.view(torch.int16), out_ws.view(torch.int16))
     assert torch.equal(lse_na, lse_ws)
+
+
+def test_noalloc_balanced_rows_two_calls():
+    # balanced rows keep their row counts and order in the scratch too (beside the partials of
+    # a split plan); the second call is smaller and unsplit
+    big = _case("fp8", 64, 512, 20, (1, 2, 4), 2, 704, flags=B.F_BALANCE_ROWS)
+    small = _case("bf16", 32, 256, 5, (1,), 1, 705, flags=B.F_BALANCE_ROWS)
+    assert big[2].num_splits == 2 and small[2].num_splits == 1
+    assert 0 < small[2].workspace_bytes < big[2].workspace_bytes <= B.NOALLOC_SCRATCH_BYTES
+    for name, (inp, g, info) in (("balanced first", big), ("balanced second (smaller)", small)):
+        announce(f"noalloc {name} R={inp.num_rows} H={inp.num_heads} S={info.num_splits}")
+        out_ws, lse_ws, out_na, lse_na = _both(inp, g, info)
+        assert torch.equal(out_na.view(torch.int16), out_ws.view(torch.int16)), name
+        assert torch.equal(lse_na, lse_ws), name
+        o, l = oracle_decode(inp)
+        compare(out_na, lse_na, o, l, what=f"noalloc {name}")
