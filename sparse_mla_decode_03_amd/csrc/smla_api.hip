@@ -23,8 +23,9 @@ struct PlanImpl {
   uint64_t off_part_o;
   uint64_t off_part_lse;
   uint64_t off_err;
-  uint64_t off_balance;   // row counts [R], then the row order [R] (SMLA_F_BALANCE_ROWS)
+  uint64_t off_balance;   // SMLA_F_BALANCE_ROWS: row counts [R], split counts [R], jobs [R * S], job count
   uint64_t ws_bytes;
+  int32_t slots;          // workgroup slots of the device (balanced rows' target job length)
 };
 static_assert(sizeof(PlanImpl) <= sizeof(smla_plan), "plan does not fit its opaque storage");
 
@@ -99,6 +100,8 @@ smla_status check_problem(const smla_problem* p) {
     return SMLA_ERR_UNSUPPORTED;
   // the documented partials are chunks of positions, which balancing would change
   if ((p->flags & SMLA_F_BALANCE_ROWS) && (p->flags & SMLA_F_PARTIALS_ONLY)) return SMLA_ERR_UNSUPPORTED;
+  // balanced jobs are coded as row | split << 24
+  if ((p->flags & SMLA_F_BALANCE_ROWS) && p->num_rows >= (1 << 24)) return SMLA_ERR_BAD_SHAPE;
   const int l = log2_exact(p->page_size);
   if (p->page_size < 1 || p->page_size > 1024 || l < 0) return SMLA_ERR_BAD_SHAPE;
   // FP8 pages are 648 * page_size bytes; the 16-byte copies need an even page size
@@ -141,10 +144,13 @@ int choose_splits(const smla_problem* p, int num_cus) {
     if (want > s) s = want;
   } else {
     const int64_t slots = (int64_t)num_cus * ((p->num_heads + 31) / 32 <= 2 ? 2 : 1);
-    // balanced rows with a row per workgroup slot: the longest-first order already evens out
-    // the slots, so a split would only add its partials and merge (627 ragged rows of 64
-    // heads: 0.213 ms unsplit against 0.217 ms at two splits)
-    if ((p->flags & SMLA_F_BALANCE_ROWS) && rows >= slots) return s;
+    // balanced rows with a row per workgroup slot: the device gives each row its own split
+    // count, up to one more than the least, so that only the longest rows split (chunks of
+    // at least 128 positions)
+    if (p->flags & SMLA_F_BALANCE_ROWS) {
+      if (p->topk / (s + 1) >= 128 && s < SMLA_MAX_SPLITS) ++s;
+      return s;
+    }
     auto cost = [&](int c) {
       const int64_t rounds = (rows * c + slots - 1) / slots;
       return rounds * ((p->topk + c - 1) / c + kSplitOverhead);
@@ -197,8 +203,9 @@ smla_status sparse_mla_decode_plan(const smla_problem* p, int32_t num_cus, smla_
   }
   if (p->flags & SMLA_F_BALANCE_ROWS) {
     pi.off_balance = off;
-    off = round_up(off + 2 * (uint64_t)p->num_rows * sizeof(int32_t), 256);
+    off = round_up(off + ((2 + (uint64_t)s) * p->num_rows + 1) * sizeof(int32_t), 256);
   }
+  pi.slots = cus * ((p->num_heads + 31) / 32 <= 2 ? 2 : 1);
   pi.ws_bytes = off;
   memset(plan, 0, sizeof(*plan));
   memcpy(plan->opaque, &pi, sizeof(pi));
@@ -279,6 +286,7 @@ smla_status run_impl(const PlanImpl* pi, const void* q, const void* kv_cache, co
     if (smla::launch_fill_u64(a.err, ~0ull, st) != hipSuccess) return SMLA_ERR_HIP;
   }
   const bool merge = pi->num_splits > 1 && !partials_only;
+  const bool balance = (p.flags & SMLA_F_BALANCE_ROWS) != 0;
   if (partials_only) {
     a.write_partials = 1;
     a.part_o = partial_o;
@@ -287,22 +295,31 @@ smla_status run_impl(const PlanImpl* pi, const void* q, const void* kv_cache, co
     a.write_partials = 2;
     a.part_o = reinterpret_cast<float*>(ws + pi->off_part_o);
     a.part_lse = reinterpret_cast<float*>(ws + pi->off_part_lse);
+    if (balance) {   // rows of one split write their output directly
+      a.out = reinterpret_cast<uint16_t*>(out);
+      a.lse = lse;
+    }
   } else {
     a.write_partials = 0;
     a.out = reinterpret_cast<uint16_t*>(out);
     a.lse = lse;
   }
-  if (p.flags & SMLA_F_BALANCE_ROWS) {
+  if (balance) {
     int32_t* counts = reinterpret_cast<int32_t*>(ws + pi->off_balance);
-    int32_t* order = counts + p.num_rows;
-    if (smla::launch_balance(a, counts, order, st) != hipSuccess) return SMLA_ERR_HIP;
+    int32_t* row_splits = counts + p.num_rows;
+    int32_t* jobs = row_splits + p.num_rows;
+    int32_t* job_count = jobs + (size_t)p.num_rows * pi->num_splits;
+    if (smla::launch_balance(a, pi->slots, counts, row_splits, jobs, job_count, st) != hipSuccess)
+      return SMLA_ERR_HIP;
     a.row_count = counts;
-    a.row_order = order;
+    a.row_splits = row_splits;
+    a.jobs = jobs;
+    a.job_count = job_count;
   }
   if (smla::launch_decode(a, p.kv_format, st) != hipSuccess) return SMLA_ERR_HIP;
   if (merge) {
     if (smla::launch_merge_native(a.part_o, a.part_lse, a.R, a.S, a.H, sinks, a.out_scale,
-                                  reinterpret_cast<uint16_t*>(out), lse, st) != hipSuccess)
+                                  reinterpret_cast<uint16_t*>(out), lse, a.row_splits, st) != hipSuccess)
       return SMLA_ERR_HIP;
   }
   return SMLA_OK;

@@ -120,9 +120,10 @@ struct Cfg {
 };
 
 // NATIVE: the epilogue writes split partials in the merge's own format (write_partials 2)
-// and nothing else; otherwise it writes the output or the documented partials.  BAL: the
-// balanced order and rank-window splits (row_order set).  Separate instantiations, so that
-// neither epilogue nor the balanced set-up changes another variant's register allocation.
+// and nothing else; otherwise it writes the output or the documented partials.  BAL (with
+// NATIVE): the balanced job list and rank-window splits (jobs set); a row of one split
+// writes its output directly.  Separate instantiations, so that neither epilogue nor the
+// balanced set-up changes another variant's register allocation.
 template <int NW, int FMT, bool NATIVE, bool BAL>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   using C = Cfg<NW, FMT>;
@@ -136,6 +137,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   __shared__ int sSlots[kSlotLen];
   __shared__ int sWcnt[8 * NW];
   __shared__ int sRestart;
+  // Balanced rows: what the direct output of a one-split row needs, kept in LDS from the
+  // set-up to the epilogue so that it holds no registers through the tile loop
+  struct EpiArgs {
+    uint16_t* out;
+    float* lse;
+    const float* sinks;
+    float out_scale;
+    int one_split;
+  };
+  __shared__ EpiArgs sEpi;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -144,31 +155,28 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int wave = NW == 4 ? (int)((unsigned)__builtin_amdgcn_readfirstlane(tid >> 6) & 3u)
                            : __builtin_amdgcn_readfirstlane(tid >> 6);
   // Work item.  Positional splits: row blockIdx.x, positions [split * chunk, +chunk).
-  // Balanced (row_order set): the dispatch index picks a (job, split) pair, jobs being rows
-  // longest first, so the longest rows start first and short ones fill the tail; the splits
-  // of a job take equal shares of the row's entries by rank (the last one takes the rest),
-  // and a group of eight jobs sends all its splits to the same eight dispatch slots mod 8
-  // (the same XCDs, whose L2s then serve the row's q and index list to its other splits).
+  // Balanced (jobs set): the dispatch index picks the next (row, split) job of a list ordered
+  // longest first, so the longest work starts first and short jobs fill the tail; a row of
+  // S_r splits gives each an equal share of its entries by rank (the last one takes the
+  // rest), and a row of one split writes its output directly.  Dispatch slots past the job
+  // count leave at once.
   int row, split, p0, p1;
   int lo = 0, hi = INT_MAX;   // ranks of the valid entries this split keeps
+  int s_row = a.S;            // the row's split count
   if constexpr (BAL) {
     const long long L = blockIdx.x + (long long)blockIdx.y * gridDim.x;
-    const long long full = (long long)(a.R >> 3) * 8 * a.S;
-    int j;
-    if (L < full) {
-      const int rem = (int)(L % (8 * a.S));
-      j = (int)(8 * (L / (8 * a.S))) + (rem & 7);
-      split = rem >> 3;
-    } else {
-      j = 8 * (a.R >> 3) + (int)((L - full) / a.S);
-      split = (int)((L - full) % a.S);
-    }
-    row = min(max(a.row_order[j], 0), a.R - 1);   // the clamps keep any count or order in bounds
+    if (L >= (long long)*a.job_count) return;      // uniform: the whole workgroup leaves
+    const int job = a.jobs[L];
+    // the clamps keep any count, split count or job in bounds
+    row = min(max(job & 0xFFFFFF, 0), a.R - 1);
+    s_row = min(max(a.row_splits[row], 1), a.S);
+    split = min((int)((unsigned)job >> 24), s_row - 1);
     const int n = min(max(a.row_count[row], 0), a.K);
-    lo = (int)((long long)split * n / a.S);
-    if (split < a.S - 1) hi = (int)((long long)(split + 1) * n / a.S);
+    lo = (int)((long long)split * n / s_row);
+    if (split < s_row - 1) hi = (int)((long long)(split + 1) * n / s_row);
     p0 = 0;
     p1 = a.K;
+    if (tid == 0) sEpi = EpiArgs{a.out, a.lse, a.sinks, a.out_scale, s_row == 1};
   } else {
     row = blockIdx.x;
     split = blockIdx.y;
@@ -875,6 +883,41 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // ---- 6. epilogue ----------------------------------------------------------------------
   const float l_tot = sum_halves(l_part);
   if constexpr (NATIVE) {
+    if (BAL && sEpi.one_split) {
+      // A balanced row of one split: the output itself, sink folded in, straight from the
+      // accumulators (lane: head h, dv 32b + 8k + 4G + 0..3 as one 8-byte bf16 piece; the
+      // wave's two lane halves complete each 16-byte piece, and its stores whole head rows)
+      const EpiArgs e = sEpi;
+      const float sink = (e.sinks != nullptr && h_ok) ? e.sinks[h] : -INFINITY;
+      const float sig2 = sink * kLog2e;
+      const float M = fmaxf(m_used, sig2);
+      float factor, lse_v;
+      if (m_used == -INFINITY) {
+        factor = 0.f;   // no valid entry: out = 0 and the LSE is the sink itself
+        lse_v = sink;
+      } else {
+        const float al = __builtin_amdgcn_exp2f(m_used - M);
+        const float z = l_tot * al + __builtin_amdgcn_exp2f(sig2 - M);
+        factor = al / z;
+        lse_v = (M + __log2f(z)) * kLn2;
+      }
+      factor *= e.out_scale;
+      if (h_ok) {
+        uint16_t* dst = e.out + ((size_t)row * a.H + h) * kV + 4 * G;
+#pragma unroll
+        for (int b = 0; b < 16; ++b) {
+          const f32x16 ob = kO15V && b == 15 ? O15 : O[ob_index(b)];
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            *reinterpret_cast<u32x2*>(dst + 32 * b + 8 * k) =
+                u32x2{pack_bf16x2(ob[4 * k] * factor, ob[4 * k + 1] * factor),
+                      pack_bf16x2(ob[4 * k + 2] * factor, ob[4 * k + 3] * factor)};
+          __builtin_amdgcn_sched_barrier(0);   // one block's values live at a time
+        }
+        if (e.lse != nullptr && G == 0) e.lse[(size_t)row * a.H + h] = lse_v;
+      }
+      return;
+    }
     // Split partials for this library's own merge, in the accumulators' own layout: each
     // store is one 1 KB run (register group k of block b, all 64 lanes), with no LDS stage
     // and no normalization; beside them the head's reference max (log2 domain) and its
@@ -895,8 +938,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     if (G == 0 && h_ok) *reinterpret_cast<f32x2*>(a.part_lse + (rs * a.H + h) * 2) = f32x2{m_used, l_tot};
     return;
   } else {
+  const bool documented = a.write_partials != 0;
   float factor, lse_v;
-  if (a.write_partials) {
+  if (documented) {
     if (l_tot > 0.f) {
       factor = 1.0f / l_tot;
       lse_v = (m_used + __log2f(l_tot)) * kLn2;
@@ -924,7 +968,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // Accumulator register r of block b holds head h (this lane's) at dv 32b + acc_row(r, G):
   // registers 4k..4k+3 are four consecutive dv, stored as one 8-byte (bf16) or 16-byte
   // (fp32 partial) piece.
-  if (a.write_partials) {
+  if (documented) {
     // fp32 partials through a per-wave LDS stage, in four quarters of 128 dv: each lane
     // writes its 16-byte runs into rows of 528 bytes (one per head; the 16-byte pad keeps the
     // 32 rows' writes on different banks), then reads back 16-byte chunks along dv, so every
@@ -1018,8 +1062,9 @@ __global__ __launch_bounds__(256) void gather_debug_kernel(const uint8_t* __rest
   *reinterpret_cast<u32x4*>(out + e * kQK + 8 * c) = v;
 }
 
-// ---- balanced splits: entry counts per row and a longest-first row order ------------------
+// ---- balanced rows: entry counts per row, per-row split counts and a longest-first job order
 constexpr int kOrderBins = 1024;   // classes of the order: 32 entries (one tile) each, the last open
+constexpr int kMinJobTiles = 4;    // the shortest target job (128 entries, the planner's least chunk)
 
 // One wave per row: the number of entries the decode keeps, by the same test as its
 // translation (an id >= 0 that names a slot of the pool, through the page table in LOGICAL
@@ -1060,19 +1105,50 @@ __global__ __launch_bounds__(256) void count_rows_kernel(DecodeArgs a, int32_t* 
   if (lane == 0) counts[row] = c;
 }
 
-// One workgroup: a counting sort of the rows by tiles of entries, most first (rows of one
-// class in no particular order; the decode's results do not depend on it).
-__global__ __launch_bounds__(1024) void order_rows_kernel(const int32_t* __restrict__ counts, int R,
-                                                          int32_t* __restrict__ order) {
+// One workgroup: each row's split count and the (row, split) jobs, longest first.  The target
+// job length is three quarters of an even share of the slots' work (at least kMinJobTiles
+// tiles); a row whose tiles exceed it splits into ceil(tiles / target) chunks, at most S (and
+// at least what keeps each chunk within kCMax entries), so that only long rows pay for
+// partials and a merge.  The jobs are counting-sorted by their
+// tiles (jobs of one class in no particular order: no result depends on it); job_count holds
+// their number.
+__global__ __launch_bounds__(1024) void schedule_rows_kernel(const int32_t* __restrict__ counts, int R,
+                                                             int S, int slots,
+                                                             int32_t* __restrict__ row_splits,
+                                                             int32_t* __restrict__ jobs,
+                                                             int32_t* __restrict__ job_count) {
   __shared__ int sStart[kOrderBins];
   __shared__ int sWave[16];
+  __shared__ unsigned long long sTotal;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   sStart[tid] = 0;
+  if (tid == 0) sTotal = 0;
   __syncthreads();
-  auto cls = [](int c) { return min((max(c, 0) + 31) >> 5, kOrderBins - 1); };
-  for (int r = tid; r < R; r += 1024) atomicAdd(&sStart[cls(counts[r])], 1);
+  auto tiles = [](int n) { return (n + 31) >> 5; };
+  auto cls = [&](int n) { return min(tiles(n), kOrderBins - 1); };
+  unsigned long long t = 0;
+  for (int r = tid; r < R; r += 1024) t += (unsigned)tiles(max(counts[r], 0));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+  if (lane == 0) atomicAdd(&sTotal, t);
+  __syncthreads();
+  const unsigned long long share = (3ull * sTotal + 4ull * slots - 1) / (4ull * slots);
+  const int target = (int)min(max(share, (unsigned long long)kMinJobTiles), (unsigned long long)INT_MAX);
+  // at least the splits that keep every chunk within a workgroup's kCMax positions
+  auto splits_of = [&](int n) {
+    return S > 1 ? min(S, max((n + kCMax - 1) / kCMax, max(1, (tiles(n) + target - 1) / target))) : 1;
+  };
+  auto job_len = [](int n, int sr, int s) {
+    return (int)((long long)(s + 1) * n / sr - (long long)s * n / sr);
+  };
+  for (int r = tid; r < R; r += 1024) {
+    const int n = max(counts[r], 0);
+    const int sr = splits_of(n);
+    row_splits[r] = sr;
+    for (int s = 0; s < sr; ++s) atomicAdd(&sStart[cls(job_len(n, sr, s))], 1);
+  }
   __syncthreads();
   // exclusive prefix over the classes in descending order: thread t takes class 1023 - t
   const int v = sStart[kOrderBins - 1 - tid];
@@ -1087,8 +1163,13 @@ __global__ __launch_bounds__(1024) void order_rows_kernel(const int32_t* __restr
   int before = 0;
   for (int w = 0; w < wave; ++w) before += sWave[w];
   sStart[kOrderBins - 1 - tid] = before + inc - v;
+  if (tid == 1023) *job_count = before + inc;   // the last class closes the count
   __syncthreads();
-  for (int r = tid; r < R; r += 1024) order[atomicAdd(&sStart[cls(counts[r])], 1)] = r;
+  for (int r = tid; r < R; r += 1024) {
+    const int n = max(counts[r], 0);
+    const int sr = splits_of(n);
+    for (int s = 0; s < sr; ++s) jobs[atomicAdd(&sStart[cls(job_len(n, sr, s))], 1)] = r | (s << 24);
+  }
 }
 
 __global__ void fill_u64_kernel(unsigned long long* p, unsigned long long v) {
@@ -1098,11 +1179,10 @@ __global__ void fill_u64_kernel(unsigned long long* p, unsigned long long v) {
 template <int NW, int FMT>
 hipError_t launch_nw(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.R, a.S), block(NW * 64);
-  if (a.row_order != nullptr) {
-    if (a.write_partials == 2)
-      hipLaunchKernelGGL((decode_kernel<NW, FMT, true, true>), grid, block, 0, st, a);
-    else
-      hipLaunchKernelGGL((decode_kernel<NW, FMT, false, true>), grid, block, 0, st, a);
+  if (a.jobs != nullptr) {
+    // balanced rows: the split-format instantiation, whose rows of one split write the
+    // output directly
+    hipLaunchKernelGGL((decode_kernel<NW, FMT, true, true>), grid, block, 0, st, a);
   } else {
     if (a.write_partials == 2)
       hipLaunchKernelGGL((decode_kernel<NW, FMT, true, false>), grid, block, 0, st, a);
@@ -1152,9 +1232,11 @@ hipError_t launch_gather_debug(const uint8_t* kv, int kv_format, int ps_log2, in
   return hipGetLastError();
 }
 
-hipError_t launch_balance(const DecodeArgs& a, int32_t* counts, int32_t* order, hipStream_t st) {
+hipError_t launch_balance(const DecodeArgs& a, int slots, int32_t* counts, int32_t* row_splits,
+                          int32_t* jobs, int32_t* job_count, hipStream_t st) {
   hipLaunchKernelGGL(count_rows_kernel, dim3((unsigned)((a.R + 3) / 4)), dim3(256), 0, st, a, counts);
-  hipLaunchKernelGGL(order_rows_kernel, dim3(1), dim3(1024), 0, st, counts, a.R, order);
+  hipLaunchKernelGGL(schedule_rows_kernel, dim3(1), dim3(1024), 0, st, counts, a.R, a.S, slots,
+                     row_splits, jobs, job_count);
   return hipGetLastError();
 }
 

@@ -18,8 +18,12 @@ struct DecodeArgs {
   float* part_o;                // [R][S][H][512]        (partial mode)
   float* part_lse;              // [R][S][H]             (partial mode)
   unsigned long long* err;      // first bad (row << 32 | pos), or null
-  const int32_t* row_order;     // [R] rows longest first (balanced splits), or null
-  const int32_t* row_count;     // [R] entries the decode keeps per row (balanced splits)
+  // balanced rows (jobs set, else null): entries the decode keeps per row, each row's split
+  // count (1..S), the (row | split << 24) jobs longest first, and their number
+  const int32_t* row_count;     // [R]
+  const int32_t* row_splits;    // [R]
+  const int32_t* jobs;          // [R * S]
+  const int32_t* job_count;     // [1]
   int32_t R, H, K, S, chunk, B;
   int32_t ps_log2, num_pages, num_slots, max_pages, index_mode;
   int32_t write_partials;       // 0 final output, 1 documented partials, 2 the merge's own format
@@ -49,18 +53,23 @@ struct IndexerTopkArgs {
 
 int max_chunk_positions();
 hipError_t launch_decode(const DecodeArgs& a, int kv_format, hipStream_t st);
-// Balanced splits: count each row's entries that the decode with these arguments keeps into
-// counts[R] and order the rows by their count, longest first, into order[R].
-hipError_t launch_balance(const DecodeArgs& a, int32_t* counts, int32_t* order, hipStream_t st);
+// Balanced rows: count each row's entries that the decode with these arguments keeps into
+// counts[R], give each row its split count (row_splits[R], 1..a.S, from its share of the work
+// of `slots` workgroup slots) and list the (row, split) jobs longest first (jobs[R * a.S],
+// job_count[1]).
+hipError_t launch_balance(const DecodeArgs& a, int slots, int32_t* counts, int32_t* row_splits,
+                          int32_t* jobs, int32_t* job_count, hipStream_t st);
 hipError_t launch_merge(const float* part_o, const float* part_lse, int R, int S, int H,
                         const float* sinks, uint16_t* out, float* lse, hipStream_t st);
 // Merge of the decode's own split format (DecodeArgs.write_partials == 2): part_o holds,
 // per (row, split) and 32-head group, 16 blocks x 4 runs of 64 lanes x 4 unnormalized
 // floats; part_ml holds (reference max in the log2 domain, probability sum) per head;
 // out_scale multiplies the merged output (the per-tensor FP8 value scale, else 1).
+// With row_splits (balanced rows) a row merges its first row_splits[r] chunks, and a row of
+// one chunk is skipped (the decode wrote its output).
 hipError_t launch_merge_native(const float* part_o, const float* part_ml, int R, int S, int H,
                                const float* sinks, float out_scale, uint16_t* out, float* lse,
-                               hipStream_t st);
+                               const int32_t* row_splits, hipStream_t st);
 hipError_t launch_gather_debug(const uint8_t* kv, int kv_format, int ps_log2, int num_slots,
                                const int* slots, int n, uint16_t* out, hipStream_t st);
 hipError_t launch_fill_u64(unsigned long long* p, unsigned long long v, hipStream_t st);

@@ -132,7 +132,7 @@ template <int NB, int NM, bool STAGE>
 __global__ __launch_bounds__(STAGE ? 256 : 64) void merge_native_kernel(
     const float* __restrict__ po, const float* __restrict__ pml, int R, int S, int H,
     const float* __restrict__ sinks, float out_scale, uint16_t* __restrict__ out,
-    float* __restrict__ lse) {
+    float* __restrict__ lse, const int32_t* __restrict__ row_splits) {
   __shared__ __attribute__((aligned(16))) uint8_t sStage[STAGE ? 32 * kStagePitch : 16];
   const int nwh = (H + 31) >> 5;
   const long long id = blockIdx.x;
@@ -143,6 +143,13 @@ __global__ __launch_bounds__(STAGE ? 256 : 64) void merge_native_kernel(
   const int wave = STAGE ? (int)(threadIdx.x >> 6) : 0;
   const int b = STAGE ? 4 * part + wave : part;
   const int lane = threadIdx.x & 63;
+  // chunks of this row: all S, or (balanced rows) the row's own count; a row of one chunk
+  // was written by the decode itself (uniform over the workgroup: one row)
+  int Sr = S;
+  if (row_splits != nullptr) {
+    Sr = min(max(row_splits[r], 1), S);
+    if (Sr == 1) return;
+  }
   const int h = 32 * g + (lane & 31);
   const bool h_ok = h < H;
   const int hc = h_ok ? h : H - 1;                  // padded heads read a real head's pair
@@ -158,10 +165,10 @@ __global__ __launch_bounds__(STAGE ? 256 : 64) void merge_native_kernel(
   f32x4 x[NB][4];
 #pragma unroll
   for (int j = 0; j < NM; ++j)
-    if (j < S) v[j] = ml[(size_t)j * H];
+    if (j < Sr) v[j] = ml[(size_t)j * H];
 #pragma unroll
   for (int j = 0; j < NB; ++j)
-    if (j < S && (NB > 4 || __ballot(v[j][1] > 0.f) != 0)) {
+    if (j < Sr && (NB > 4 || __ballot(v[j][1] > 0.f) != 0)) {
       const float* src = src0 + j * cstride;
 #pragma unroll
       for (int k = 0; k < 4; ++k) x[j][k] = *reinterpret_cast<const f32x4*>(src + k * (64 * 4));
@@ -171,18 +178,18 @@ __global__ __launch_bounds__(STAGE ? 256 : 64) void merge_native_kernel(
   bool any = false;                                  // a non-empty chunk
 #pragma unroll
   for (int j = 0; j < NM; ++j)
-    if (j < S && v[j][1] > 0.f) {
+    if (j < Sr && v[j][1] > 0.f) {
       M = fmaxf(M, v[j][0]);
       any = true;
     }
-  for (int c0 = NM; c0 < S; c0 += 16) {
+  for (int c0 = NM; c0 < Sr; c0 += 16) {
     f32x2 u[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      if (c0 + j < S) u[j] = ml[(size_t)(c0 + j) * H];
+      if (c0 + j < Sr) u[j] = ml[(size_t)(c0 + j) * H];
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      if (c0 + j < S && u[j][1] > 0.f) {
+      if (c0 + j < Sr && u[j][1] > 0.f) {
         M = fmaxf(M, u[j][0]);
         any = true;
       }
@@ -193,12 +200,12 @@ __global__ __launch_bounds__(STAGE ? 256 : 64) void merge_native_kernel(
   float z = 0.f;
   if (any) {
     // pass 2: weights and the weighted sum; the first batch is already in registers
-    for (int c0 = 0; c0 < S; c0 += NB) {
+    for (int c0 = 0; c0 < Sr; c0 += NB) {
       f32x2 w2[NB];
       if (c0 > 0) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-          if (c0 + j < S) {
+          if (c0 + j < Sr) {
             w2[j] = ml[(size_t)(c0 + j) * H];
             const float* src = src0 + (c0 + j) * cstride;
 #pragma unroll
@@ -211,7 +218,7 @@ __global__ __launch_bounds__(STAGE ? 256 : 64) void merge_native_kernel(
       }
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        if (c0 + j < S && w2[j][1] > 0.f) {
+        if (c0 + j < Sr && w2[j][1] > 0.f) {
           const float w = __builtin_amdgcn_exp2f(w2[j][0] - M);
           z += w * w2[j][1];
 #pragma unroll
@@ -263,7 +270,7 @@ __global__ __launch_bounds__(STAGE ? 256 : 64) void merge_native_kernel(
 
 hipError_t launch_merge_native(const float* part_o, const float* part_ml, int R, int S, int H,
                                const float* sinks, float out_scale, uint16_t* out, float* lse,
-                               hipStream_t st) {
+                               const int32_t* row_splits, hipStream_t st) {
   // the staged layout once there are enough (row, head group) pairs to fill the chip with
   // four-wave workgroups
   const long long groups = (long long)R * ((H + 31) / 32);
@@ -274,10 +281,10 @@ hipError_t launch_merge_native(const float* part_o, const float* part_ml, int R,
   do {                                                                                            \
     if (stage)                                                                                    \
       hipLaunchKernelGGL((merge_native_kernel<NB, NM, true>), grid, block, 0, st, part_o, part_ml, \
-                         R, S, H, sinks, out_scale, out, lse);                                    \
+                         R, S, H, sinks, out_scale, out, lse, row_splits);                        \
     else                                                                                          \
       hipLaunchKernelGGL((merge_native_kernel<NB, NM, false>), grid, block, 0, st, part_o,         \
-                         part_ml, R, S, H, sinks, out_scale, out, lse);                           \
+                         part_ml, R, S, H, sinks, out_scale, out, lse, row_splits);               \
   } while (0)
   if (S <= 2)
     SMLA_MERGE_NATIVE(2, 2);

@@ -37,8 +37,8 @@ def setup(lib):
     lib.smla_hostcheck_last_merge.argtypes = [ctypes.POINTER(ctypes.c_int32 * 3),
                                               ctypes.POINTER(ctypes.c_uint64 * 2)]
     lib.smla_hostcheck_last_merge_scale.restype = ctypes.c_float
-    lib.smla_hostcheck_last_balance.argtypes = [ctypes.POINTER(ctypes.c_int32 * 2),
-                                                ctypes.POINTER(ctypes.c_uint64 * 5)]
+    lib.smla_hostcheck_last_balance.argtypes = [ctypes.POINTER(ctypes.c_int32 * 4),
+                                                ctypes.POINTER(ctypes.c_uint64 * 10)]
 
 
 def counts(lib):
@@ -57,7 +57,7 @@ def last_decode(lib):
 
 
 def last_balance(lib):
-    i, p = (ctypes.c_int32 * 2)(), (ctypes.c_uint64 * 5)()
+    i, p = (ctypes.c_int32 * 4)(), (ctypes.c_uint64 * 10)()
     lib.smla_hostcheck_last_balance(ctypes.byref(i), ctypes.byref(p))
     return list(i), list(p)
 
@@ -202,31 +202,40 @@ def check_noalloc(lib):
 def check_balance_rows(lib):
     lib.smla_hostcheck_reset()
     R, S, H = 600, 2, 64
-    # the row counts and the order follow the split partials in the workspace
+    # counts [R], split counts [R], jobs [R * S] and the job count follow the split partials
     pl, ws = plan(lib, prob(num_rows=R, num_requests=R, num_heads=H, num_splits=S, flags=B.F_BALANCE_ROWS))
     parts = round_up(R * S * H * 512 * 4, 256) + round_up(R * S * H * 8, 256)
-    assert ws == parts + round_up(2 * R * 4, 256)
+    assert ws == parts + round_up((2 * R + R * S + 1) * 4, 256)
     assert run(lib, pl, ws=W, wsb=ws) == B.OK
     assert lib.smla_hostcheck_launches(9) == 1 and counts(lib) == [1, 0, 0, 0, 0, 0, 0, 0, 1]
-    (br, bk), (bidx, bc, bo, dc, do) = last_balance(lib)
-    assert (br, bk) == (R, 2048) and bidx == P["idx"]
-    assert bc == W + parts and bo == bc + 4 * R and (dc, do) == (bc, bo)
-    # unsplit: the order alone, in a workspace of its own
+    (br, bk, bs, slots), p = last_balance(lib)
+    assert (br, bk, bs, slots) == (R, 2048, S, 2 * 256) and p[0] == P["idx"]
+    bc = W + parts
+    assert p[1:5] == [bc, bc + 4 * R, bc + 8 * R, bc + 8 * R + 4 * R * S]
+    assert p[5:9] == p[1:5] and p[9] == p[2]          # the decode and the merge see the same lists
+    d = last_decode(lib)
+    assert d["write_partials"] == 2 and d["po"] == W and d["out"] == P["out"] and d["lse"] == P["lse"]
+    # unsplit: the lists alone, in a workspace of their own; four-wave rows take one slot per CU
     lib.smla_hostcheck_reset()
     pl, ws = plan(lib, prob(num_rows=R, num_requests=R, num_splits=1, flags=B.F_BALANCE_ROWS))
-    assert ws == round_up(2 * R * 4, 256)
+    assert ws == round_up((3 * R + 1) * 4, 256)
     assert run(lib, pl, ws=W, wsb=ws) == B.OK
     assert lib.smla_hostcheck_launches(9) == 1 and last_decode(lib)["out"] == P["out"]
-    assert last_balance(lib)[1][3:] == [W, W + 4 * R]
-    # without the flag the decode gets no order
+    (_, _, bs, slots), p = last_balance(lib)
+    assert (bs, slots) == (1, 256) and p[5:9] == [W, W + 4 * R, W + 8 * R, W + 12 * R]
+    assert counts(lib)[8] == 0
+    # without the flag the decode gets no lists and the merge no split counts
     lib.smla_hostcheck_reset()
-    pl, ws = plan(lib, prob(num_rows=R, num_requests=R, num_splits=1))
-    assert run(lib, pl) == B.OK and lib.smla_hostcheck_launches(9) == 0
-    assert last_balance(lib)[1][3:] == [0, 0]
+    pl, ws = plan(lib, prob(num_rows=R, num_requests=R, num_heads=H, num_splits=S))
+    assert run(lib, pl, ws=W, wsb=ws) == B.OK and lib.smla_hostcheck_launches(9) == 0
+    assert last_balance(lib)[1][5:] == [0, 0, 0, 0, 0] and last_decode(lib)["out"] == 0
     # balancing changes the positional chunks the documented partials are defined by
     pr = prob(num_rows=4, num_requests=4, num_splits=2, flags=B.F_BALANCE_ROWS | B.F_PARTIALS_ONLY)
     pl_, wsb = B.Plan(), ctypes.c_size_t(0)
     assert lib.sparse_mla_decode_plan(ctypes.byref(pr), 256, ctypes.byref(pl_), ctypes.byref(wsb)) == B.ERR_UNSUPPORTED
+    # jobs are coded as row | split << 24
+    pr = prob(num_rows=1 << 24, num_requests=4, num_splits=1, flags=B.F_BALANCE_ROWS)
+    assert lib.sparse_mla_decode_plan(ctypes.byref(pr), 256, ctypes.byref(pl_), ctypes.byref(wsb)) == B.ERR_BAD_SHAPE
 
 
 def check_planner_cu_count(lib):

@@ -29,8 +29,9 @@ int g_last_merge[3];             // R, S, H
 const void* g_last_merge_ptrs[2];  // part_o, part_lse
 int g_cus = 256;
 float g_last_merge_scale = 0.f;
-int g_last_balance[2];               // R, K
-const void* g_last_balance_ptrs[3];  // indices, counts, order
+const int32_t* g_last_merge_splits = nullptr;
+int g_last_balance[4];               // R, K, S, slots
+const void* g_last_balance_ptrs[5];  // indices, counts, row_splits, jobs, job_count
 unsigned char g_fatbin_stand_in[16];
 
 // Where the stand-in hipGetSymbolAddress says the scratch array lives: an address that
@@ -60,8 +61,10 @@ hipError_t launch_merge(const float* part_o, const float* part_lse, int R, int S
   return hipSuccess;
 }
 hipError_t launch_merge_native(const float* part_o, const float* part_ml, int R, int S, int H,
-                               const float*, float out_scale, uint16_t*, float*, hipStream_t) {
+                               const float*, float out_scale, uint16_t*, float*, const int32_t* row_splits,
+                               hipStream_t) {
   ++g_counts[kMergeNative];
+  g_last_merge_splits = row_splits;
   g_last_merge_scale = out_scale;
   g_last_merge[0] = R;
   g_last_merge[1] = S;
@@ -70,13 +73,18 @@ hipError_t launch_merge_native(const float* part_o, const float* part_ml, int R,
   g_last_merge_ptrs[1] = part_ml;
   return hipSuccess;
 }
-hipError_t launch_balance(const DecodeArgs& a, int32_t* counts, int32_t* order, hipStream_t) {
+hipError_t launch_balance(const DecodeArgs& a, int slots, int32_t* counts, int32_t* row_splits,
+                          int32_t* jobs, int32_t* job_count, hipStream_t) {
   ++g_counts[kBalance];
   g_last_balance[0] = a.R;
   g_last_balance[1] = a.K;
+  g_last_balance[2] = a.S;
+  g_last_balance[3] = slots;
   g_last_balance_ptrs[0] = a.indices;
   g_last_balance_ptrs[1] = counts;
-  g_last_balance_ptrs[2] = order;
+  g_last_balance_ptrs[2] = row_splits;
+  g_last_balance_ptrs[3] = jobs;
+  g_last_balance_ptrs[4] = job_count;
   return hipSuccess;
 }
 hipError_t launch_gather_debug(const uint8_t*, int, int, int, const int*, int, uint16_t*, hipStream_t) {
@@ -145,7 +153,8 @@ void smla_hostcheck_reset() {
   std::memset(g_last_merge, 0, sizeof(g_last_merge));
   g_last_merge_ptrs[0] = g_last_merge_ptrs[1] = nullptr;
   std::memset(g_last_balance, 0, sizeof(g_last_balance));
-  g_last_balance_ptrs[0] = g_last_balance_ptrs[1] = g_last_balance_ptrs[2] = nullptr;
+  std::memset(g_last_balance_ptrs, 0, sizeof(g_last_balance_ptrs));
+  g_last_merge_splits = nullptr;
 }
 void smla_hostcheck_set_cus(int n) { g_cus = n; }
 float smla_hostcheck_last_merge_scale() { return g_last_merge_scale; }
@@ -168,13 +177,17 @@ void smla_hostcheck_last_decode(int32_t* ints, float* floats, uintptr_t* ptrs) {
                         a.out, a.lse, a.part_o, a.part_lse, a.err};
   for (int i = 0; i < 11; ++i) ptrs[i] = reinterpret_cast<uintptr_t>(pv[i]);
 }
-// The last balance launch: ints = R, K; ptrs = indices, counts, order, then the last decode
-// launch's row_count and row_order.
+// The last balance launch: ints = R, K, S, slots; ptrs = indices, counts, row_splits, jobs,
+// job_count, then the last decode launch's row_count, row_splits, jobs and job_count, then the
+// last native merge's row_splits.
 void smla_hostcheck_last_balance(int32_t* ints, uintptr_t* ptrs) {
   std::memcpy(ints, g_last_balance, sizeof(g_last_balance));
-  for (int i = 0; i < 3; ++i) ptrs[i] = reinterpret_cast<uintptr_t>(g_last_balance_ptrs[i]);
-  ptrs[3] = reinterpret_cast<uintptr_t>(g_last_decode.row_count);
-  ptrs[4] = reinterpret_cast<uintptr_t>(g_last_decode.row_order);
+  for (int i = 0; i < 5; ++i) ptrs[i] = reinterpret_cast<uintptr_t>(g_last_balance_ptrs[i]);
+  ptrs[5] = reinterpret_cast<uintptr_t>(g_last_decode.row_count);
+  ptrs[6] = reinterpret_cast<uintptr_t>(g_last_decode.row_splits);
+  ptrs[7] = reinterpret_cast<uintptr_t>(g_last_decode.jobs);
+  ptrs[8] = reinterpret_cast<uintptr_t>(g_last_decode.job_count);
+  ptrs[9] = reinterpret_cast<uintptr_t>(g_last_merge_splits);
 }
 // The last merge launch (either kind): ints = R, S, H; ptrs = part_o, part_lse or part_ml.
 void smla_hostcheck_last_merge(int32_t* ints, uintptr_t* ptrs) {

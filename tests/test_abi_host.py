@@ -131,14 +131,16 @@ def test_plan_splits_and_workspace(lib):
     # index checking needs one word
     st, p, ws = _plan_status(lib, _prob(num_rows=512, flags=B.F_CHECK_INDICES))
     assert st == B.OK and ws == 256
-    # many ragged rows: two splits by the round rule, none when the rows are balanced
+    # many ragged rows: two splits by the round rule; balanced rows may split in two, each
+    # row by its own count
     st, p, ws = _plan_status(lib, _prob(num_rows=627, num_heads=64))
     assert st == B.OK and lib.sparse_mla_plan_num_splits(ctypes.byref(p)) == 2
     st, p, ws = _plan_status(lib, _prob(num_rows=627, num_heads=64, flags=B.F_BALANCE_ROWS))
-    assert st == B.OK and lib.sparse_mla_plan_num_splits(ctypes.byref(p)) == 1
-    # balanced rows: a count and an order slot per row (the header's flag value is the binding's)
+    assert st == B.OK and lib.sparse_mla_plan_num_splits(ctypes.byref(p)) == 2
+    # balanced rows: a count, a split count and a job per row, and the job count (the
+    # header's flag value is the binding's)
     st, p, ws = _plan_status(lib, _prob(num_rows=600, num_splits=1, flags=B.F_BALANCE_ROWS))
-    assert st == B.OK and ws == 4864
+    assert st == B.OK and ws == 7424
     assert "SMLA_F_BALANCE_ROWS = 4" in open(HEADER).read() and B.F_BALANCE_ROWS == 4
     # plans are data independent and deterministic
     a = _plan_status(lib, _prob(num_rows=32))
