@@ -125,13 +125,17 @@ enum {
   /* Record the first out-of-range index in the workspace (see sparse_mla_read_index_error). */
   SMLA_F_CHECK_INDICES = 2,
   /* For batches whose rows hold very different numbers of entries (short contexts padded
-   * with -1): the run first counts each row's valid entries (those the decode keeps) and
-   * orders the rows by that count, longest first (two small launches, 8 bytes of workspace
-   * per row), then takes the rows in that order, and a split row's chunks hold equal
-   * numbers of its valid entries instead of equal ranges of positions.  The result is the
-   * same attention; the rounding of a split row may differ from the positional split
-   * (LOGICAL and GLOBAL mode over the same entries still agree bit for bit).  Not with
-   * SMLA_F_PARTIALS_ONLY (UNSUPPORTED): the documented partials are ranges of positions. */
+   * with -1).  The run first counts each row's valid entries (those the decode keeps), gives
+   * each row its own split count (one for most rows; up to the plan's S for rows far longer
+   * than an even share of the work) and orders the (row, split) jobs longest first (two
+   * small launches; workspace for 3 + S int32 per row); the decode then takes the jobs in
+   * that order, a split row's chunks hold equal numbers of its valid entries instead of
+   * equal ranges of positions, rows of one split write their output directly and only split
+   * rows are merged.  The result is the same attention; the rounding of a split row may
+   * differ from the positional split (LOGICAL and GLOBAL mode over the same entries still
+   * agree bit for bit).  On rows of equal length it only adds cost.  Not with
+   * SMLA_F_PARTIALS_ONLY (UNSUPPORTED): the documented partials are ranges of positions;
+   * num_rows must be below 2^24 (BAD_SHAPE). */
   SMLA_F_BALANCE_ROWS = 4
 };
 
