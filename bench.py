@@ -188,6 +188,7 @@ def workload_measure(B, W, torch, dev, name: str, seed: int, reps: int):
     mfma_frac = flops / t / 1e12 / PEAK_BF16_TFLOPS
     del inp, scratch
     return {"kv_format": spec.kv_format, "rows": R, "heads": H, "num_splits": info.num_splits,
+            "balanced_rows": bool(spec.flags & B.F_BALANCE_ROWS),
             "attended_entries": n, "launch_ms_p50": times["warm"], "cold_cache_launch_ms_p50": times["cold"],
             "entries_per_s": n / t, "tokens_per_s": R / t,
             "hbm_tb_s": cbytes / t / 1e12, "hbm_frac": hbm_frac,
