@@ -304,6 +304,45 @@ def test_balanced_rows_match_oracle(heads, splits):
     assert (out.float() - out2.float()).abs().max().item() <= 2e-2
 
 
+def test_balanced_schedule_lists():
+    """The scheduling launch's own lists, read back from the workspace: each row's count is
+    the number of entries the oracle's translation keeps; each row's split count follows the
+    rule (tiles over a target of three quarters of an even share of the slots' work, at
+    least 4 tiles; at most S; at least what keeps a chunk within 2048 entries); the jobs are
+    exactly the (row, split) pairs, longest first by tiles (1024 classes)."""
+    inp = _small(heads=64, topk=512, nreq=300, rows=(1,), ctx=(300, 1500), valid="uniform", seed=71)
+    idx = inp.indices.clone()
+    idx[4] = -1
+    idx[7, :20] = int(inp.page_table.shape[1]) * inp.spec.page_size + 1   # past the table
+    announce("balanced schedule lists")
+    S = 2
+    out, lse, info, ws = gpu_decode(inp, indices=idx, num_splits=S, flags=B.F_BALANCE_ROWS,
+                                    return_info=True)
+    torch.cuda.synchronize()
+    R, H, K = inp.num_rows, inp.num_heads, inp.spec.topk
+    rup = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    parts = rup(R * S * ((H + 31) // 32) * 32 * 512 * 4) + rup(R * S * H * 8)
+    w = ws.cpu().numpy()[parts:].view(np.int32)
+    counts, splits, jobs, njobs = w[:R], w[R:2 * R], w[2 * R:2 * R + R * S], int(w[2 * R + R * S])
+    pt, rr = inp.page_table.numpy(), inp.row_req.numpy()
+    want = np.array([len(orc.translate(idx[r].numpy(), orc.IDX_LOGICAL, int(rr[r]), pt,
+                                       inp.spec.page_size, inp.num_pages)[0]) for r in range(R)])
+    assert np.array_equal(counts, want)
+    tiles = (want + 31) // 32
+    slots = 2 * torch.cuda.get_device_properties(0).multi_processor_count   # two-wave workgroups
+    target = max(-(-3 * int(tiles.sum()) // (4 * slots)), 4)
+    rule = np.minimum(S, np.maximum(-(-want // 2048), np.maximum(1, -(-tiles // target))))
+    assert np.array_equal(splits, rule) and 1 < rule.max()
+    assert njobs == int(rule.sum())
+    got = [(int(j) & 0xFFFFFF, int(np.uint32(j)) >> 24) for j in jobs[:njobs]]
+    assert sorted(got) == sorted((r, s) for r in range(R) for s in range(int(rule[r])))
+    share = lambda n, sr, s: (s + 1) * n // sr - s * n // sr  # noqa: E731
+    cls = [min((share(int(want[r]), int(rule[r]), s) + 31) // 32, 1023) for r, s in got]
+    assert all(a >= b for a, b in zip(cls, cls[1:])), "jobs not longest first"
+    o, l = oracle_decode(inp, indices=idx)
+    compare(out, lse, o, l, what="balanced schedule")
+
+
 def test_balanced_rows_above_one_workgroup_and_global_slots():
     # K = 5000 needs at least three splits; GLOBAL mode takes the slots as they are
     inp = _small(heads=64, topk=5000, nreq=3, rows=(1, 2), ctx=(6000, 9000), valid="uniform", seed=67)
