@@ -1068,11 +1068,26 @@ constexpr int kMinJobTiles = 4;    // the shortest target job (128 entries, the 
 
 // One wave per row: the number of entries the decode keeps, by the same test as its
 // translation (an id >= 0 that names a slot of the pool, through the page table in LOGICAL
-// mode), so that the ranks of a balanced split are those of the decode's own list.
+// mode), so that the ranks of a balanced split are those of the decode's own list.  A lane
+// takes up to eight 16-byte groups of ids per round, all loaded before any is used, then all
+// their page-table entries, so a row of 2048 ids costs two memory round trips.
+constexpr int kCountUnroll = 8;
 __global__ __launch_bounds__(256) void count_rows_kernel(DecodeArgs a, int32_t* __restrict__ counts) {
   const int lane = threadIdx.x & 63;
-  const int row = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  // wave-uniform, so the request lookup is a scalar load beside the vector loads of the ids
+  const int row = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
   if (row >= a.R) return;
+  const u32x4* p = reinterpret_cast<const u32x4*>(a.indices + (size_t)row * a.K);
+  const int n4 = a.K >> 2;
+  u32x4 v[kCountUnroll];
+  auto load_round = [&](int i0) {
+#pragma unroll
+    for (int u = 0; u < kCountUnroll; ++u) {
+      const int i = i0 + 64 * u;
+      v[u] = i < n4 ? p[i] : u32x4{~0u, ~0u, ~0u, ~0u};   // past the row: -1
+    }
+  };
+  load_round(lane);   // the first round's ids are in flight during the request lookup
   const int* pt = nullptr;
   bool req_ok = true;
   if (a.index_mode == 0) {
@@ -1080,24 +1095,31 @@ __global__ __launch_bounds__(256) void count_rows_kernel(DecodeArgs a, int32_t* 
     req_ok = req >= 0 && req < a.B;
     pt = a.page_table + (size_t)(req_ok ? req : 0) * a.max_pages;
   }
-  const u32x4* p = reinterpret_cast<const u32x4*>(a.indices + (size_t)row * a.K);
-  const int n4 = a.K >> 2;
   int c = 0;
-#pragma unroll 4
-  for (int i = lane; i < n4; i += 64) {
-    const u32x4 v = p[i];
+  for (int i0 = lane; i0 < n4; i0 += 64 * kCountUnroll) {
+    if (i0 != lane) load_round(i0);
+    if (a.index_mode == 0) {
+      int pg[kCountUnroll][4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int t = (int)v[k];
-      bool ok;
-      if (a.index_mode == 0) {
-        ok = req_ok && t >= 0 && (t >> a.ps_log2) < a.max_pages;
-        const int pg = ok ? pt[t >> a.ps_log2] : -1;
-        ok = ok && pg >= 0 && pg < a.num_pages;
-      } else {
-        ok = t >= 0 && t < a.num_slots;
-      }
-      c += ok ? 1 : 0;
+      for (int u = 0; u < kCountUnroll; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int t = (int)v[u][k];
+          const bool ok = req_ok && t >= 0 && (t >> a.ps_log2) < a.max_pages;
+          pg[u][k] = ok ? pt[t >> a.ps_log2] : -1;
+        }
+#pragma unroll
+      for (int u = 0; u < kCountUnroll; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) c += (pg[u][k] >= 0 && pg[u][k] < a.num_pages) ? 1 : 0;
+    } else {
+#pragma unroll
+      for (int u = 0; u < kCountUnroll; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int t = (int)v[u][k];
+          c += (t >= 0 && t < a.num_slots) ? 1 : 0;
+        }
     }
   }
 #pragma unroll
