@@ -71,3 +71,56 @@ def test_graph_replays_match_eager(name):
         assert torch.isfinite(x).all()
         assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16)), f"{name}: replay {i}"
         assert torch.equal(lse, ref_l), f"{name}: replay {i}"
+
+
+def test_graph_of_a_whole_step():
+    """One decode step as one graph: indexer logits -> top-k -> the once-per-step slot build ->
+    decode in GLOBAL mode over those slots.  Every intermediate buffer is scrambled before
+    each replay; the lists and the outputs come back bit-identical to the eager step."""
+    ispec = W.INDEXER_WORKLOADS["idx_small"].scaled(next_n=2, num_requests=3, ctx_lo=300, ctx_hi=900)
+    iinp = W.make_indexer_inputs(ispec, 41)
+    dspec = W.WorkloadSpec("step", 3, (2,), 64, 256, 300, 900, W.KV_FP8)
+    d = W.make_inputs(dspec, 41).to(DEV)
+    assert torch.equal(d.context_lens.cpu(), iinp.context_lens)
+    R, H, K = d.num_rows, d.num_heads, 256
+    q_codes, weights = iinp.q_codes.to(DEV).contiguous(), iinp.weights.to(DEV).contiguous()
+    key_cache, row_len = iinp.key_cache.to(DEV), iinp.row_len.to(DEV).contiguous()
+    ipt = iinp.page_table.to(DEV).contiguous()
+    logits = torch.empty((R, iinp.width), dtype=torch.float32, device=DEV)
+    idx = torch.empty((R, K), dtype=torch.int32, device=DEV)
+    slots = torch.empty((R, K), dtype=torch.int32, device=DEV)
+    out = torch.empty((R, H, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((R, H), dtype=torch.float32, device=DEV)
+    info = B.plan(B.make_problem(R, dspec.num_requests, H, K, dspec.page_size, d.num_pages,
+                                 d.page_table.shape[1], B.KV_FP8_UE8M0, B.IDX_GLOBAL, 0, 0,
+                                 dspec.softmax_scale))
+    ws = torch.empty(max(info.workspace_bytes, 16), dtype=torch.uint8, device=DEV)
+
+    def step():
+        B.indexer_logits(q_codes, weights, key_cache, row_len, ipt, ispec.next_n, iinp.width, logits=logits)
+        B.indexer_topk(logits, row_len, K, out=idx)
+        B.translate_indices(idx, d.row_req, d.page_table, dspec.page_size, d.num_pages, out=slots)
+        B.run(info, d.q, d.kv_cache, slots, None, None, d.sinks, out, lse, None, None, ws)
+
+    announce(f"graph of a step R={R} S={info.num_splits}")
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (idx, slots, out, lse)]
+    assert (ref[0] >= 0).any()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for i in range(3):
+        logits.fill_(float("nan"))
+        idx.fill_(-5)
+        slots.fill_(-5)
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        ws.fill_(0x5A)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want, what in zip((idx, slots, out, lse), ref, ("top-k", "slots", "out", "lse")):
+            assert torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got,
+                               want.view(torch.int16) if want.dtype == torch.bfloat16 else want), \
+                f"{what}: replay {i}"
