@@ -304,6 +304,18 @@ def test_balanced_rows_match_oracle(heads, splits):
     assert (out.float() - out2.float()).abs().max().item() <= 2e-2
 
 
+@pytest.mark.parametrize("fmt,heads,splits", [("bf16", 64, 2), ("fp8t", 64, 2), ("fp8t", 128, 3),
+                                               ("bf16", 32, 1)])
+def test_balanced_rows_other_formats(fmt, heads, splits):
+    # the balanced kernels of the BF16 and per-tensor FP8 caches, one- and two-split rows
+    inp = _small(fmt=fmt, heads=heads, topk=256, nreq=150, rows=(1,), ctx=(200, 600), valid="uniform",
+                 seed=81 + heads + splits, kv_scale=1.0 / 32 if fmt == "fp8t" else 1.0)
+    o, l = oracle_decode(inp)
+    announce(f"balanced rows {fmt} H={heads} S={splits}")
+    out, lse = gpu_decode(inp, num_splits=splits, flags=B.F_BALANCE_ROWS)
+    compare(out, lse, o, l, what=f"balanced {fmt} H={heads} S={splits}")
+
+
 def test_balanced_schedule_lists():
     """The scheduling launch's own lists, read back from the workspace: each row's count is
     the number of entries the oracle's translation keeps; each row's split count follows the
