@@ -22,6 +22,7 @@
 //   6. epilogue: final output with the sink folded in, or the sink-free split partial.
 #include <type_traits>
 
+#include "sparse_mla.h"
 #include "smla_device.h"
 #include "smla_kernels.h"
 
@@ -172,8 +173,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     s_row = min(max(a.row_splits[row], 1), a.S);
     split = min((int)((unsigned)job >> 24), s_row - 1);
     const int n = min(max(a.row_count[row], 0), a.K);
-    lo = (int)((long long)split * n / s_row);
-    if (split < s_row - 1) hi = (int)((long long)(split + 1) * n / s_row);
+    // 32-bit products suffice: split < 256 and n <= K <= 256 * kCMax (2^19)
+    lo = (int)((unsigned)split * (unsigned)n / (unsigned)s_row);
+    if (split < s_row - 1) hi = (int)((unsigned)(split + 1) * (unsigned)n / (unsigned)s_row);
     p0 = 0;
     p1 = a.K;
     if (tid == 0) sEpi = EpiArgs{a.out, a.lse, a.sinks, a.out_scale, s_row == 1};
@@ -1065,6 +1067,9 @@ __global__ __launch_bounds__(256) void gather_debug_kernel(const uint8_t* __rest
 // ---- balanced rows: entry counts per row, per-row split counts and a longest-first job order
 constexpr int kOrderBins = 1024;   // classes of the order: 32 entries (one tile) each, the last open
 constexpr int kMinJobTiles = 4;    // the shortest target job (128 entries, the planner's least chunk)
+// a balanced share (s + 1) * n / S_r is computed in 32 bits: s < S and n <= K <= S * kCMax
+static_assert((unsigned long long)SMLA_MAX_SPLITS * SMLA_MAX_SPLITS * kCMax < (1ull << 32),
+              "balanced shares overflow 32 bits");
 
 // One wave per row: the number of entries the decode keeps, by the same test as its
 // translation (an id >= 0 that names a slot of the pool, through the page table in LOGICAL
@@ -1163,7 +1168,8 @@ __global__ __launch_bounds__(1024) void schedule_rows_kernel(const int32_t* __re
     return S > 1 ? min(S, max((n + kCMax - 1) / kCMax, max(1, (tiles(n) + target - 1) / target))) : 1;
   };
   auto job_len = [](int n, int sr, int s) {
-    return (int)((long long)(s + 1) * n / sr - (long long)s * n / sr);
+    // 32-bit products suffice: s < 256 and n <= K <= 256 * kCMax (2^19)
+    return (int)((unsigned)(s + 1) * (unsigned)n / (unsigned)sr - (unsigned)s * (unsigned)n / (unsigned)sr);
   };
   for (int r = tid; r < R; r += 1024) {
     const int n = max(counts[r], 0);
