@@ -124,11 +124,14 @@ __global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ po,
 // per (row, head group, quarter of dv), whose bf16 results pass through LDS so that every
 // store writes whole 256-byte pieces of head rows (a wave's own 32 dv of 32 heads are
 // 64-byte pieces, half a cache line each); otherwise one single-wave workgroup per block,
-// which spreads a merge of few rows over more CUs.
+// which spreads a merge of few rows over more CUs, or (KR = 2: more than eight splits over
+// very few rows) per half block, whose lanes hold 8 outputs each so that sixteen splits load
+// in one round trip.
 constexpr int kStagePitch = 272;   // bytes per head row of the stage: 128 dv + 16 bytes of pad
 constexpr int kStageMinGroups = 128;   // (row, head group) pairs from which the stage is used
+constexpr int kHalfMaxGroups = 16;     // (row, head group) pairs up to which half blocks are used
 
-template <int NB, int NM, bool STAGE>
+template <int NB, int NM, bool STAGE, int KR>
 __global__ __launch_bounds__(STAGE ? 256 : 64) void merge_native_kernel(
     const float* __restrict__ po, const float* __restrict__ pml, int R, int S, int H,
     const float* __restrict__ sinks, float out_scale, uint16_t* __restrict__ out,
@@ -136,12 +139,14 @@ __global__ __launch_bounds__(STAGE ? 256 : 64) void merge_native_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t sStage[STAGE ? 32 * kStagePitch : 16];
   const int nwh = (H + 31) >> 5;
   const long long id = blockIdx.x;
-  constexpr int kPer = STAGE ? 4 : 16;               // workgroups per (row, head group)
+  static_assert(KR == 4 || (KR == 2 && !STAGE), "half blocks only without the stage");
+  constexpr int kPer = STAGE ? 4 : 16 * (4 / KR);     // workgroups per (row, head group)
   const int part = (int)(id % kPer);
   const int g = (int)((id / kPer) % nwh);
   const int r = (int)(id / (kPer * nwh));
   const int wave = STAGE ? (int)(threadIdx.x >> 6) : 0;
-  const int b = STAGE ? 4 * part + wave : part;
+  const int b = STAGE ? 4 * part + wave : (KR == 4 ? part : part >> 1);
+  const int k0 = KR == 4 ? 0 : 2 * (part & 1);       // the wave's first run of the block
   const int lane = threadIdx.x & 63;
   // chunks of this row: all S, or (balanced rows) the row's own count; a row of one chunk
   // was written by the decode itself (uniform over the workgroup: one row)
@@ -156,13 +161,13 @@ __global__ __launch_bounds__(STAGE ? 256 : 64) void merge_native_kernel(
   const float sink = (sinks != nullptr) ? sinks[hc] : -INFINITY;
   const float sig2 = sink * kLog2e;
   const f32x2* ml = reinterpret_cast<const f32x2*>(pml) + (size_t)r * S * H + hc;
-  const float* src0 = po + ((size_t)r * S * nwh + g) * (16 * 4 * 64 * 4) + b * (4 * 64 * 4) + 4 * lane;
+  const float* src0 = po + ((size_t)r * S * nwh + g) * (16 * 4 * 64 * 4) + (4 * b + k0) * (64 * 4) + 4 * lane;
   const size_t cstride = (size_t)nwh * (16 * 4 * 64 * 4);
   // one memory round trip for the pairs of the first NM splits and the runs of the first NB
   // (all issued before any use; the runs do not depend on the weights)
   static_assert(NM >= NB, "the first batch's weights come from the pairs loaded with it");
   f32x2 v[NM];
-  f32x4 x[NB][4];
+  f32x4 x[NB][KR];
 #pragma unroll
   for (int j = 0; j < NM; ++j)
     if (j < Sr) v[j] = ml[(size_t)j * H];
@@ -171,7 +176,7 @@ __global__ __launch_bounds__(STAGE ? 256 : 64) void merge_native_kernel(
     if (j < Sr && (NB > 4 || __ballot(v[j][1] > 0.f) != 0)) {
       const float* src = src0 + j * cstride;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) x[j][k] = *reinterpret_cast<const f32x4*>(src + k * (64 * 4));
+      for (int k = 0; k < KR; ++k) x[j][k] = *reinterpret_cast<const f32x4*>(src + k * (64 * 4));
     }
   // pass 1: the head's largest reference over the non-empty chunks (and the sink)
   float M = sig2;
@@ -194,9 +199,9 @@ __global__ __launch_bounds__(STAGE ? 256 : 64) void merge_native_kernel(
         any = true;
       }
   }
-  float acc[16];
+  float acc[4 * KR];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  for (int i = 0; i < 4 * KR; ++i) acc[i] = 0.f;
   float z = 0.f;
   if (any) {
     // pass 2: weights and the weighted sum; the first batch is already in registers
@@ -209,7 +214,7 @@ __global__ __launch_bounds__(STAGE ? 256 : 64) void merge_native_kernel(
             w2[j] = ml[(size_t)(c0 + j) * H];
             const float* src = src0 + (c0 + j) * cstride;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) x[j][k] = *reinterpret_cast<const f32x4*>(src + k * (64 * 4));
+            for (int k = 0; k < KR; ++k) x[j][k] = *reinterpret_cast<const f32x4*>(src + k * (64 * 4));
           }
         }
       } else {
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(STAGE ? 256 : 64) void merge_native_kernel(
           const float w = __builtin_amdgcn_exp2f(w2[j][0] - M);
           z += w * w2[j][1];
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
+          for (int k = 0; k < KR; ++k)
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[4 * k + i] += w * x[j][k][i];
         }
@@ -235,13 +240,13 @@ __global__ __launch_bounds__(STAGE ? 256 : 64) void merge_native_kernel(
   const float lse_v = z > 0.f ? (M + __log2f(z)) * kLn2 : sink;
   if constexpr (!STAGE) {
     if (h_ok) {
-      uint16_t* dst = out + ((size_t)r * H + h) * kV + 32 * b + 4 * (lane >> 5);
+      uint16_t* dst = out + ((size_t)r * H + h) * kV + 32 * b + 8 * k0 + 4 * (lane >> 5);
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+      for (int k = 0; k < KR; ++k)
         *reinterpret_cast<u32x2*>(dst + 8 * k) =
             u32x2{pack_bf16x2(acc[4 * k] * inv, acc[4 * k + 1] * inv),
                   pack_bf16x2(acc[4 * k + 2] * inv, acc[4 * k + 3] * inv)};
-      if (lse != nullptr && b == 0 && lane < 32) lse[(size_t)r * H + h] = lse_v;
+      if (lse != nullptr && b == 0 && k0 == 0 && lane < 32) lse[(size_t)r * H + h] = lse_v;
     }
     return;
   }
@@ -275,16 +280,23 @@ hipError_t launch_merge_native(const float* part_o, const float* part_ml, int R,
   // four-wave workgroups
   const long long groups = (long long)R * ((H + 31) / 32);
   const bool stage = groups >= kStageMinGroups;
-  const dim3 grid((unsigned)(groups * (stage ? 4 : 16)));
   const dim3 block(stage ? 256 : 64);
-#define SMLA_MERGE_NATIVE(NB, NM)                                                                 \
-  do {                                                                                            \
-    if (stage)                                                                                    \
-      hipLaunchKernelGGL((merge_native_kernel<NB, NM, true>), grid, block, 0, st, part_o, part_ml, \
-                         R, S, H, sinks, out_scale, out, lse, row_splits);                        \
-    else                                                                                          \
-      hipLaunchKernelGGL((merge_native_kernel<NB, NM, false>), grid, block, 0, st, part_o,         \
-                         part_ml, R, S, H, sinks, out_scale, out, lse, row_splits);               \
+  if (!stage && S > 8 && groups <= kHalfMaxGroups) {
+    // half blocks for very few rows: sixteen splits' runs in one round trip, and twice the
+    // waves (b2_h128_bf16_split16: 27.6 -> 27.1 us; 64 groups at 16 splits measured 2 % slower)
+    hipLaunchKernelGGL((merge_native_kernel<16, 16, false, 2>), dim3((unsigned)(groups * 32)), block, 0,
+                       st, part_o, part_ml, R, S, H, sinks, out_scale, out, lse, row_splits);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)(groups * (stage ? 4 : 16)));
+#define SMLA_MERGE_NATIVE(NB, NM)                                                                    \
+  do {                                                                                               \
+    if (stage)                                                                                       \
+      hipLaunchKernelGGL((merge_native_kernel<NB, NM, true, 4>), grid, block, 0, st, part_o, part_ml, \
+                         R, S, H, sinks, out_scale, out, lse, row_splits);                           \
+    else                                                                                             \
+      hipLaunchKernelGGL((merge_native_kernel<NB, NM, false, 4>), grid, block, 0, st, part_o,         \
+                         part_ml, R, S, H, sinks, out_scale, out, lse, row_splits);                  \
   } while (0)
   if (S <= 2)
     SMLA_MERGE_NATIVE(2, 2);

@@ -201,6 +201,19 @@ def test_forced_splits_match_unsplit(splits):
     compare(out, lse, o, l, what=f"S={splits}")
 
 
+@pytest.mark.parametrize("heads,splits", [(48, 24), (16, 9), (128, 17)])
+def test_forced_splits_over_few_rows(heads, splits):
+    # few rows and more than eight splits: the merge of half blocks (padded head groups, a
+    # partial second batch of sixteen splits, empty leading chunks)
+    inp = _small(heads=heads, topk=1024, nreq=2, rows=(1,), ctx=(1100, 3000), seed=19 + heads)
+    idx = inp.indices.clone()
+    idx[1, :200] = -1
+    o, l = oracle_decode(inp, indices=idx)
+    announce(f"few rows H={heads} S={splits}")
+    out, lse = gpu_decode(inp, indices=idx, num_splits=splits)
+    compare(out, lse, o, l, what=f"few rows H={heads} S={splits}")
+
+
 @pytest.mark.parametrize("splits", [None, 3])
 def test_topk_above_one_workgroup_capacity(splits):
     """K = 5000 exceeds the 2048 positions one workgroup takes: the planner must split (at
