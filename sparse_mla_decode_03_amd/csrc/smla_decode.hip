@@ -1,9 +1,10 @@
 // Fused top-k sparse MLA decode kernel for gfx950.
 //
 // One workgroup handles one (query row, split) pair with all H query heads, as
-// ceil(H/32) waves of 32 heads each.  Steps, in the order of the Triton decode path
-// described on prhub sglang#24692 ("SM120 support for DeepSeek-V4", implementation
-// breakdown 2-3):
+// ceil(H/32) waves of 32 heads each (for ragged batches, the next pair of a longest-first
+// job list that the two scheduling kernels at the end of this file build on the device).
+// Steps, in the order of the Triton decode path described on prhub sglang#24692 ("SM120
+// support for DeepSeek-V4", implementation breakdown 2-3):
 //   1. index translation + compaction: the row's top-k positions of this split are
 //      turned into cache slots through the page table (the block-table translation of
 //      prhub vllm#43477, key code excerpts: forward_mqa); -1 and out-of-range entries
