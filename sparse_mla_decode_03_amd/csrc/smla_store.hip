@@ -26,23 +26,6 @@ __device__ __forceinline__ uint32_t ue8m0_for_amax(float amax) {
   return (uint32_t)min(max(e, 0), 254);
 }
 
-// e4m3fn code of a finite v with |v| <= 448, rounded to nearest, ties to even.  Normal
-// range (|v| >= 2^-6): the fp32 mantissa is rounded to 3 bits at bit 20 (a carry moves into
-// the exponent) and the exponent rebiased from 127 to 7.  Below 2^-6 the code is the
-// subnormal step count m = v / 2^-9 (0..8; 8 is the smallest normal, code 0x08).
-__device__ __forceinline__ uint32_t e4m3fn_rne(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a >= 0x3C800000u) {
-    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-    code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
-  } else {
-    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  }
-  return ((u >> 24) & 0x80u) | code;
-}
-
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -89,12 +72,18 @@ __global__ __launch_bounds__(256) void store_kernel(const uint16_t* __restrict__
       am = fmaxf(am, __shfl_xor(am, 2));
       am = fmaxf(am, __shfl_xor(am, 4));
       const uint32_t e = ue8m0_for_amax(am);
-      const int sh = 127 - (int)e;            // x * 2^sh is exact
-      uint32_t c[8];
+      // x * 2^sh is exact and at most 448 in magnitude; the hardware conversion rounds it to
+      // the nearest e4m3fn value, ties to even (subnormal codes included), in the default
+      // round-to-nearest mode
+      const int sh = 127 - (int)e;
+      float y[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) c[j] = e4m3fn_rne(__builtin_amdgcn_ldexpf(x[j], sh));
-      *reinterpret_cast<u32x2*>(kv + sa.latent + 8 * lane) =
-          u32x2{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
+      for (int j = 0; j < 8; ++j) y[j] = __builtin_amdgcn_ldexpf(x[j], sh);
+      int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
+      int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
+      *reinterpret_cast<u32x2*>(kv + sa.latent + 8 * lane) = u32x2{(uint32_t)w0, (uint32_t)w1};
       if ((lane & 7) == 0) kv[sa.scales + (lane >> 3)] = (uint8_t)e;
     } else {
       *reinterpret_cast<u32x4*>(kv + sa.latent + 16 * lane) = w[i];

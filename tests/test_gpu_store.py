@@ -37,6 +37,13 @@ def _latent_with_edge_groups(n: int, seed: int) -> torch.Tensor:
         x[1, 128:192] = torch.cat([torch.tensor([448.0]), mids])
     if n > 2:
         x[2, :] = torch.linspace(-448.0, 448.0, 512)
+    if n > 3:
+        # every midpoint between consecutive positive codes (subnormal ones included), then
+        # their negatives, four groups of scale 1 (each led by 448)
+        pos = torch.from_numpy(orc.e4m3fn_to_f64(np.arange(0x7F, dtype=np.uint8))).float()
+        mids = (pos[:-1] + pos[1:]) / 2                # 126 ties
+        for k, part in enumerate((mids[:63], mids[63:], -mids[:63], -mids[63:])):
+            x[3, 64 * k:64 * k + 64] = torch.cat([torch.tensor([448.0]), part])
     return x.to(torch.bfloat16)
 
 
