@@ -470,7 +470,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by rows with no exchange; see the design notes)", file=sys.stderr)
+              "(the path would shard by rows, with no exchange between GPUs)", file=sys.stderr)
         return 2
 
     import torch

@@ -19,7 +19,7 @@ Sources (prhub.com.cn summaries of serving-engine pull requests):
                 init_layer_buffers (bmm1 scale = softmax scale * q_scale * kv_scale with
                 unit FP8 scales, so the logit scale is the softmax scale).
 The pages never write the formula out.  What is computed here is the plain reading
-of those passages; the readings are listed with the design notes of the repository.
+of those passages, stated at each function that takes one.
 
 Definitions implemented (natural exp/log; float64 throughout):
   k_j = dequantized cache entry (576), v_j = k_j[:512]
